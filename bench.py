@@ -1,0 +1,182 @@
+#!/usr/bin/env python3
+"""Throughput of one GPU's tensor-parallel GPT layer shard, forward + backward.
+
+A step is one mt_layer_fwd + mt_layer_bwd of the shard over one micro-batch of seeded
+synthetic inputs already resident in HBM. Default workload: the GPT-175B layer shape,
+shard 0 of tp=8 (h=12288, 12 of 96 heads of 128, seq 2048, micro-batch 1, bf16).
+
+Reported (one JSON line): model TFLOP/s = 3 x (forward GEMM + causal attention FLOPs)
+per step / step time, its fraction of the MI355X dense bf16 MFMA peak, the roofline
+of the dominant kernel (timed live with HIP events on the library's stream around
+that kernel's launches inside the timed steps), and the fp64 oracle timed on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+METRIC = "model TFLOP/s per GPU, GPT layer-shard fwd+bwd; % of bf16 MFMA peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gpt175b_tp8")
+    ap.add_argument("--dominant", default="fc1_fwd",
+                    help="label of the kernel launch whose roofline is reported")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--breakdown", action="store_true", help="also print a per-launch time breakdown (stderr)")
+    return ap.parse_args()
+
+
+def cpu_baseline(case, shape):
+    """The fp64 oracle, as it stands, on one full step of the same workload."""
+    import numpy as np
+    import oracle
+    import seeded_inputs as si
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    out, c = oracle.layer_fwd(case.x, case.layers[:1], shape.micro_batch, shape.seq, shape.head_dim)
+    dx, g = oracle.layer_bwd(case.dout, c, case.layers[:1])
+    dt = time.perf_counter() - t0
+    del out, c, dx, g
+    flops = si.model_flops(shape)
+    return {"value": round(flops / dt / 1e12, 4), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"one full fwd+bwd step of {case.shape.h}-wide shard (M={shape.tokens}) in NumPy fp64, "
+                      f"{dt:.1f} s", "seconds": round(dt, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the tensor-parallel "
+              "all-reduce is not part of it. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import seeded_inputs as si
+    import tensor_layer_gemms_amd as mt
+
+    if not os.path.exists(mt.LIB_PATH):
+        from tensor_layer_gemms_amd.build import build
+        build()
+    mt.lib()
+    w = si.WORKLOADS[args.workload]
+    shape = w.shape
+    print(f"[bench] generating seeded inputs for {args.workload}", file=sys.stderr, flush=True)
+    case = si.workload_case(args.workload)
+    dev = lambda a: torch.from_numpy(a).cuda().to(torch.bfloat16 if shape.dtype == "bf16" else torch.float32)  # noqa
+    sh = mt.make_shape(shape.h, shape.heads, shape.seq, shape.micro_batch, shape.tp, shape.shard, shape.dtype)
+    L = w.layers
+    weights = [{k: dev(v) for k, v in p.items()} for p in case.layers]
+    grads = [{k: torch.empty(v.shape, dtype=torch.float32, device="cuda") for k, v in p.items()} for p in case.layers]
+    acts = [dev(case.x)] + [torch.empty_like(dev(case.x)) for _ in range(L)]
+    dout = dev(case.dout)
+    dxs = [torch.empty_like(dout) for _ in range(L)]
+    saved = [torch.empty(mt.layer_saved_bytes(sh), dtype=torch.uint8, device="cuda") for _ in range(L)]
+    ws = torch.empty(mt.layer_workspace_bytes(sh), dtype=torch.uint8, device="cuda")
+    for l in range(L):
+        mt.check_layer_tensors(sh, weights[l], grads[l], x=acts[l], out=acts[l + 1], dx=dxs[l])
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for l in range(L):
+            mt.layer_fwd(sh, weights[l], acts[l], acts[l + 1], saved[l], ws, stream)
+        g = dout
+        for l in reversed(range(L)):
+            mt.layer_bwd(sh, weights[l], acts[l], saved[l], g, dxs[l], grads[l], ws, stream)
+            g = dxs[l]
+
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # per-launch breakdown (untimed pass, every launch bracketed by events)
+    breakdown = None
+    if args.breakdown:
+        mt.timing_reset()
+        mt.timing_enable(True, None)
+        step()
+        torch.cuda.synchronize()
+        mt.timing_enable(False)
+        breakdown = mt.timing_records()
+        mt.timing_reset()
+
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    mt.timing_reset()
+    mt.timing_enable(True, args.dominant)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mt.timing_enable(False)
+    recs = [r for r in mt.timing_records() if r[0] == args.dominant]
+    mt.timing_reset()
+    ms_per_step = start.elapsed_time(end) / args.steps
+    flops_step = L * si.model_flops(shape, causal=True)
+    dense_step = L * si.model_flops(shape, causal=False)
+    value = flops_step / (ms_per_step * 1e-3) / 1e12
+
+    roofline = None
+    if recs:
+        avg_ms = sum(r[1] for r in recs) / len(recs)
+        kflops = recs[0][2]
+        achieved = kflops / (avg_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": args.dominant,
+                    "avg_ms": round(avg_ms, 4), "launches": len(recs), "gflop_per_launch": round(kflops / 1e9, 2)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the fp64 oracle on the host (one step)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(case, shape)
+
+    if breakdown:
+        tot = sum(r[1] for r in breakdown)
+        print(f"[bench] breakdown of one step ({tot:.3f} ms in launches):", file=sys.stderr)
+        for lab, ms, fl, by in breakdown:
+            rate = f"{fl / ms / 1e9:8.1f} TFLOP/s" if fl else f"{by / ms / 1e6:8.1f} GB/s   "
+            print(f"  {lab:18s} {ms:8.4f} ms {100 * ms / tot:5.1f}%  {rate}", file=sys.stderr)
+
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if shape.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": args.workload, "h": shape.h, "heads": shape.heads, "heads_per_shard":
+                   shape.heads_per_shard, "head_dim": shape.head_dim, "seq": shape.seq,
+                   "micro_batch": shape.micro_batch, "tp": shape.tp, "shard": shape.shard, "layers": L,
+                   "gflop_per_step_causal": round(flops_step / 1e9, 1),
+                   "gflop_per_step_dense": round(dense_step / 1e9, 1)},
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "dense_count_tflops": round(dense_step / (ms_per_step * 1e-3) / 1e12, 2),
+        "wall_s_timed": round(wall, 3),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

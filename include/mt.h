@@ -1,0 +1,140 @@
+/*
+ * mt.h -- C ABI of one tensor-parallel (TP) shard of a GPT transformer layer,
+ * forward and backward, on one AMD Instinct MI355X (gfx950).
+ *
+ * What the shard computes (pre-LN GPT layer; one rank of a t-way tensor-parallel group):
+ *   U = LN1(X)
+ *   QKV_i = U W_qkv_i^T + b_qkv_i          column-parallel: this rank's heads
+ *   ctx_i = causal softmax attention over the rank's heads (scale 1/sqrt(d))
+ *   O_i = ctx_i W_o_i^T                   row-parallel: a PARTIAL sum
+ *   X2 = X + AR(O_i) + b_o;  V2 = LN2(X2)
+ *   A_i = V2 W1_i^T + b1_i;  Z_i = GeLU(A_i)   (fused bias + GeLU epilogue)
+ *   Y_i = Z_i W2_i^T                       row-parallel: a PARTIAL sum
+ *   Out = X2 + AR(Y_i) + b_fc2
+ * The block structure Y = f(X A) B with A split by columns and B split by rows, each
+ * rank computing f(X A_i) B_i whose sum over ranks an all-reduce forms, and the split of
+ * attention heads over ranks, follow the "Megatron-LM" concept report
+ * (compassingai.com), section 4.1; communication in the backward pass as well
+ * (so the input-gradients of the column-parallel GEMMs are partials too) follows its
+ * section 4.2. AR is the all-reduce point: on one GPU it is the identity, so for
+ * tp > 1 the shard returns exactly what one rank computes before communicating; the
+ * mt_mlp_* calls return the bare partials, whose sum over the t shards is the
+ * unsharded block.
+ *
+ * Conventions for every call:
+ *   - Device pointers are caller-owned, contiguous row-major, 16-byte aligned. The
+ *     library allocates nothing and keeps no state between calls (apart from the
+ *     optional timing records below).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). All work
+ *     is enqueued asynchronously on it; faults inside kernels surface at the caller's
+ *     next synchronisation.
+ *   - Activations and weights have the shape's dtype (MT_BF16: bfloat16 storage with
+ *     fp32 accumulation and fp32 LayerNorm/softmax/GeLU math; MT_FP32: fp32 throughout).
+ *     Parameter gradients are always fp32 and are overwritten (not accumulated).
+ *   - Every argument is validated before anything is launched; on error nothing is
+ *     launched and the status says why (mt_status_string).
+ *   - Shape limits: h % heads == 0, heads % tp == 0, 0 <= shard < tp, head dim
+ *     d = h / heads a multiple of 8, seq a multiple of 8 and <= 4096, h <= 32768
+ *     (bf16) or 16384 (fp32).
+ */
+#ifndef MT_H_
+#define MT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MT_OK = 0,
+  MT_ERR_INVALID_ARG = 1, /* null pointer, misalignment, inconsistent shape */
+  MT_ERR_UNSUPPORTED = 2, /* valid shape outside the supported limits above */
+  MT_ERR_HIP = 3,         /* a HIP launch or runtime call failed */
+  MT_ERR_WORKSPACE = 4    /* saved / workspace buffer smaller than the *_bytes query */
+} mt_status;
+
+typedef enum { MT_BF16 = 0, MT_FP32 = 1 } mt_dtype;
+
+/* One TP shard of one layer. h and heads are the GLOBAL (unsharded) sizes; the shard
+ * owns heads/tp heads and 4h/tp FFN columns. */
+typedef struct {
+  int32_t h, heads, seq, micro_batch, tp, shard;
+  int32_t dtype; /* mt_dtype */
+} mt_shape;
+
+/* Shard-local weights in nn.Linear layout W[out, in], dtype of the shape.
+ * M = micro_batch * seq tokens, ht = h/tp, ft = 4h/tp. */
+typedef struct {
+  const void *ln1_g, *ln1_b; /* [h] */
+  const void *w_qkv;         /* [3*ht, h]: rows = [Q heads | K heads | V heads] of the shard */
+  const void *b_qkv;         /* [3*ht] */
+  const void *w_o;           /* [h, ht] */
+  const void *b_o;           /* [h] replicated; added after the all-reduce point */
+  const void *ln2_g, *ln2_b; /* [h] */
+  const void *w_fc1;         /* [ft, h] */
+  const void *b_fc1;         /* [ft] */
+  const void *w_fc2;         /* [h, ft] */
+  const void *b_fc2;         /* [h] replicated */
+} mt_layer_weights;
+
+/* fp32 parameter gradients, same shapes as mt_layer_weights. The replicated ones
+ * (LayerNorm, b_o, b_fc2) are this rank's copy. */
+typedef struct {
+  float *ln1_g, *ln1_b, *w_qkv, *b_qkv, *w_o, *b_o, *ln2_g, *ln2_b, *w_fc1, *b_fc1, *w_fc2, *b_fc2;
+} mt_layer_grads;
+
+/* Bytes of the activation store written by mt_layer_fwd and read by mt_layer_bwd, and
+ * of the scratch workspace either call needs (no initialisation required). Return 0
+ * for an invalid shape. */
+size_t mt_layer_saved_bytes(const mt_shape *shape);
+size_t mt_layer_workspace_bytes(const mt_shape *shape);
+
+/* Forward of the shard: x [M, h] -> out [M, h]. `saved` must stay untouched until the
+ * matching mt_layer_bwd has run. */
+int mt_layer_fwd(const mt_shape *shape, const mt_layer_weights *w, const void *x, void *out, void *saved,
+                 size_t saved_bytes, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Backward of the shard given dout [M, h]: writes dx [M, h] (activation dtype) and every
+ * parameter gradient in `grads` (fp32). x and w must be those of the forward. */
+int mt_layer_bwd(const mt_shape *shape, const mt_layer_weights *w, const void *x, const void *saved,
+                 size_t saved_bytes, const void *dout, void *dx, const mt_layer_grads *grads, void *workspace,
+                 size_t workspace_bytes, void *stream);
+
+/* MLP block alone, the concept report's f(X A_i) B_i (section 4.1):
+ *   y_partial = GeLU(x W1^T + b1) W2^T  with x [M, h], W1 [ft, h], b1 [ft], W2 [h, ft].
+ * No LayerNorm, no output bias, no residual: the sum of y_partial over the tp shards is
+ * the unsharded block. */
+size_t mt_mlp_saved_bytes(const mt_shape *shape);
+size_t mt_mlp_workspace_bytes(const mt_shape *shape);
+int mt_mlp_fwd(const mt_shape *shape, const void *x, const void *w_fc1, const void *b_fc1, const void *w_fc2,
+               void *y_partial, void *saved, size_t saved_bytes, void *workspace, size_t workspace_bytes,
+               void *stream);
+/* Backward given dy [M, h]: dx_partial [M, h] (activation dtype; its sum over shards is
+ * the block's input gradient, section 4.2), dw_fc1 [ft, h], db_fc1 [ft], dw_fc2 [h, ft]
+ * in fp32. */
+int mt_mlp_bwd(const mt_shape *shape, const void *x, const void *w_fc1, const void *w_fc2, const void *saved,
+               size_t saved_bytes, const void *dy, void *dx_partial, float *dw_fc1, float *db_fc1, float *dw_fc2,
+               void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static text of a status code. */
+const char *mt_status_string(int status);
+
+/* Per-launch timing (the throughput-breakdown aid). While enabled, each launch whose
+ * label contains `label_filter` (NULL or "" = every launch) is bracketed by two HIP
+ * events on the call's stream and recorded with its label and algorithmic FLOPs and
+ * bytes. Enabling creates events on the host; records persist until mt_timing_reset.
+ * mt_timing_get waits for record i's end event and returns its duration in ms.
+ * Returns MT_OK or an error status. Not meant to be toggled while calls are in flight
+ * on other threads. */
+int mt_timing_enable(int enable, const char *label_filter);
+int mt_timing_reset(void);
+int mt_timing_count(void);
+int mt_timing_get(int i, char *label, size_t label_len, float *ms, double *flops, double *bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MT_H_ */

@@ -1,0 +1,98 @@
+// Device-side helpers shared by the HIP kernels of the layer shard (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
+__device__ __forceinline__ float to_f32(float v) { return v; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+// fp32 -> bf16 round-to-nearest-even (gfx950 lowers this to v_cvt_pk_bf16_f32).
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+
+// 16-byte vectors of T: 8 bf16 or 4 fp32.
+template <typename T> struct Vec16 { static constexpr int N = 16 / sizeof(T); };
+
+template <typename T>
+__device__ __forceinline__ void load16(const T* p, float* out) {
+  u32x4 raw = *reinterpret_cast<const u32x4*>(p);
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(raw[i] << 16);
+      out[2 * i + 1] = __uint_as_float(raw[i] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(raw[i]);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store16(T* p, const float* v) {
+  u32x4 raw;
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bf16 lo = (bf16)v[2 * i], hi = (bf16)v[2 * i + 1];
+      raw[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) raw[i] = __float_as_uint(v[i]);
+  }
+  *reinterpret_cast<u32x4*>(p) = raw;
+}
+
+// Wavefront (64 lanes) reductions.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Block-wide sum of NV values (every thread gets the totals). `red` holds
+// NV * (blockDim/64) floats of LDS.
+template <int NV, int NWAVES>
+__device__ __forceinline__ void block_sum(float* v, float* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) v[i] = wave_sum(v[i]);
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) red[i * NWAVES + wave] = v[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWAVES; ++w) s += red[i * NWAVES + w];
+    v[i] = s;
+  }
+  __syncthreads();
+}
+
+// Exact GeLU a * Phi(a) = a/2 (1 + erf(a / sqrt 2)) and its derivative
+// Phi(a) + a phi(a); erff is the HIP device library's.
+__device__ __forceinline__ float gelu_f(float a) {
+  return 0.5f * a * (1.0f + erff(a * 0.70710678118654752f));
+}
+__device__ __forceinline__ float gelu_grad_f(float a) {
+  return 0.5f * (1.0f + erff(a * 0.70710678118654752f)) + a * 0.39894228040143268f * __expf(-0.5f * a * a);
+}

@@ -1,0 +1,62 @@
+// GEMM family of the layer shard: C[m, n] = epilogue(sum_k A(m, k) B(n, k)).
+//
+// Every linear layer, its input-gradient (dgrad) and weight-gradient (wgrad), and the
+// four attention products are instances of this one contraction; they differ in which
+// index of each operand is contiguous in memory and in the fused epilogue:
+//   forward  Y = X W^T          A = X  [M, K] (K-contiguous), B = W [N, K] (K-contiguous)
+//   dgrad    dX = dY W          A = dY [M, K] (K-contiguous), B(n, k) = W[k, n] (N-contiguous)
+//   wgrad    dW = dY^T X        A(n, m) = dY[m, n], B(k, m) = X[m, k]: both token-strided
+// The split of the weights (columns of the first GEMM of a block, rows of the second)
+// follows the "Megatron-LM" concept report (compassingai.com), section 4.1; only the
+// operand layouts, not the arithmetic, depend on which side of the split a GEMM is.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mt {
+
+enum EpiKind : int {
+  EPI_STORE = 0,      // C = alpha * acc, stored in the activation type
+  EPI_STORE_F32 = 1,  // C = alpha * acc, stored as fp32 (weight gradients, scores)
+  EPI_BIAS = 2,       // C = acc + bias[n]
+  EPI_BIAS_GELU = 3,  // C = a = acc + bias[n] (pre-activation, kept for backward); C2 = GeLU(a)
+  EPI_DGELU = 4,      // C = acc * GeLU'(aux[m, n])            (aux = saved pre-activation)
+  EPI_DSOFTMAX = 5,   // C = aux[m, n] * (acc - vec[m])        (aux = P, vec = rowsum(P * dP))
+};
+
+enum Causal : int {
+  CAUSAL_NONE = 0,
+  CAUSAL_SKIP_UPPER = 1,  // output tiles entirely above the diagonal (n0 > last m) are skipped
+  CAUSAL_K_LE_M = 2,      // contraction limited to k < m0 + BM   (A = P or dS, row-major)
+  CAUSAL_K_GE_M = 3,      // contraction starts at k = m0          (A = P^T or dS^T)
+};
+
+// Rows of the probability matrices (P, dS) are written for columns
+// [0, min(s, roundup(q + 1, kCausalChunk))), with zeros right of the diagonal, so every
+// causal consumer whose tile sizes divide kCausalChunk reads only written entries.
+constexpr int kCausalChunk = 256;
+
+struct GemmArgs {
+  const void* A;
+  const void* B;
+  void* C;
+  void* C2;         // EPI_BIAS_GELU second output, same layout as C
+  const void* aux;  // EPI_DGELU / EPI_DSOFTMAX input, same layout as C
+  const void* vec;  // bias [N] (activation type) or fp32 row vector [M] per batch
+  int64_t lda, ldb, ldc;
+  // batch z = blockIdx.y; offsets (z / zdiv) * so + (z % zdiv) * si, in elements
+  int64_t a_so, a_si, b_so, b_si, c_so, c_si;
+  int64_t vec_bs;   // row-vector batch stride (EPI_DSOFTMAX)
+  int M, N, K, zdiv, causal;
+  float alpha;
+};
+
+// Host launchers (gemm_*.hip). a_kcontig / b_kcontig: whether A(m, k) / B(n, k) is
+// contiguous along k. Return the launch status.
+hipError_t launch_gemm_bf16(const GemmArgs& g, bool a_kcontig, bool b_kcontig, int kind, int batch,
+                            hipStream_t stream);
+hipError_t launch_gemm_f32(const GemmArgs& g, bool a_kcontig, bool b_kcontig, int kind, int batch,
+                           hipStream_t stream);
+
+}  // namespace mt

@@ -1,0 +1,274 @@
+// Device code of the GEMM family (see gemm.hpp for the contraction and layouts).
+#pragma once
+
+#include "device_common.hpp"
+#include "gemm.hpp"
+
+namespace mt {
+
+// ---------------------------------------------------------------------------- epilogue
+template <typename T, int KIND>
+__device__ __forceinline__ void epi_store(const GemmArgs& g, int64_t coff, int64_t voff, int m, int n, float v) {
+  const int64_t idx = coff + (int64_t)m * g.ldc + n;
+  if constexpr (KIND == EPI_STORE) {
+    static_cast<T*>(g.C)[idx] = from_f32<T>(g.alpha * v);
+  } else if constexpr (KIND == EPI_STORE_F32) {
+    static_cast<float*>(g.C)[idx] = g.alpha * v;
+  } else if constexpr (KIND == EPI_BIAS) {
+    static_cast<T*>(g.C)[idx] = from_f32<T>(v + to_f32(static_cast<const T*>(g.vec)[n]));
+  } else if constexpr (KIND == EPI_BIAS_GELU) {
+    const float a = v + to_f32(static_cast<const T*>(g.vec)[n]);
+    static_cast<T*>(g.C)[idx] = from_f32<T>(a);
+    static_cast<T*>(g.C2)[idx] = from_f32<T>(gelu_f(a));
+  } else if constexpr (KIND == EPI_DGELU) {
+    const float a = to_f32(static_cast<const T*>(g.aux)[idx]);
+    static_cast<T*>(g.C)[idx] = from_f32<T>(v * gelu_grad_f(a));
+  } else if constexpr (KIND == EPI_DSOFTMAX) {
+    const float p = to_f32(static_cast<const T*>(g.aux)[idx]);
+    const float d = static_cast<const float*>(g.vec)[voff + m];
+    static_cast<T*>(g.C)[idx] = from_f32<T>(p * (g.alpha * v - d));
+  }
+}
+
+__device__ __forceinline__ void causal_k_range(const GemmArgs& g, int m0, int bm, int& kbeg, int& kend) {
+  kbeg = 0;
+  kend = g.K;
+  if (g.causal == CAUSAL_K_LE_M) kend = min(g.K, m0 + bm);
+  if (g.causal == CAUSAL_K_GE_M) kbeg = m0;
+}
+
+// Logical tile for workgroup `bid`. Workgroups are handed to the 8 XCDs round-robin
+// (id mod 8); each XCD is given a contiguous range of logical tiles, and inside it
+// GROUP_M tile-rows are walked together so neighbouring tiles share A and B panels in
+// that XCD's L2.
+template <int GROUP_M>
+__device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+  constexpr int NXCD = 8;
+  const int total = tiles_m * tiles_n;
+  int logical = bid;
+  if (total >= NXCD) {
+    const int per = (total + NXCD - 1) / NXCD, rem = total % NXCD;
+    const int xcd = bid % NXCD, local = bid / NXCD;
+    logical = (rem == 0 || xcd < rem) ? xcd * per + local : rem * per + (xcd - rem) * (per - 1) + local;
+  }
+  const int group = GROUP_M * tiles_n;
+  const int first_m = (logical / group) * GROUP_M;
+  const int gm = min(tiles_m - first_m, GROUP_M);
+  const int r = logical % group;
+  tm = first_m + r % gm;
+  tn = r / gm;
+}
+
+// ---------------------------------------------------------------------------- bf16 MFMA
+// LDS tile: ROWS x 64 bf16, row = 128 bytes = 8 chunks of 16 bytes; chunk c of row r
+// lives at chunk position c ^ (r & 7), so the 32 lanes of an MFMA operand read (same
+// chunk, 32 consecutive rows) hit distinct banks.
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 64 + ((chunk ^ (row & 7)) << 3); }
+
+template <int ROWS, int NT, bool KCONTIG>
+struct TileLoader {
+  // K-contiguous: one 16-byte chunk per item. Token-strided: one 8x8 block per item
+  // (8 loads of 8 consecutive rows at 8 consecutive k, transposed in registers).
+  static constexpr int ITEMS = KCONTIG ? ROWS * 8 : ROWS;
+  static constexpr int PER = (ITEMS + NT - 1) / NT;
+  static constexpr int NREG = KCONTIG ? PER : PER * 8;
+  u32x4 r[NREG];
+
+  __device__ __forceinline__ void load(const bf16* base, int64_t ld, int row0, int rows_valid, int k0, int kend,
+                                       int tid) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int it = tid + i * NT;
+      if (ITEMS % NT != 0 && it >= ITEMS) break;
+      if constexpr (KCONTIG) {
+        const int row = it >> 3, kc = it & 7;
+        const int gr = row0 + row, gk = k0 + kc * 8;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (gr < rows_valid && gk < kend) v = *reinterpret_cast<const u32x4*>(base + (int64_t)gr * ld + gk);
+        r[i] = v;
+      } else {
+        const int kb = it & 7, rb = it >> 3;
+        const int gr = row0 + rb * 8;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+          const int gk = k0 + kb * 8 + kk;
+          u32x4 v = {0u, 0u, 0u, 0u};
+          if (gr < rows_valid && gk < kend) v = *reinterpret_cast<const u32x4*>(base + (int64_t)gk * ld + gr);
+          r[i * 8 + kk] = v;
+        }
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(bf16* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int it = tid + i * NT;
+      if (ITEMS % NT != 0 && it >= ITEMS) break;
+      if constexpr (KCONTIG) {
+        const int row = it >> 3, kc = it & 7;
+        *reinterpret_cast<u32x4*>(lds + swz(row, kc)) = r[i];
+      } else {
+        const int kb = it & 7, rb = it >> 3;
+        // r[i*8+kk] holds rows rb*8..rb*8+7 at k = kb*8+kk (two rows per dword);
+        // output row rr gathers its 8 k values (two k per dword).
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+          const uint32_t sel = (rr & 1) ? 0x07060302u : 0x05040100u;
+          u32x4 w;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            w[j] = __builtin_amdgcn_perm(r[i * 8 + 2 * j + 1][rr >> 1], r[i * 8 + 2 * j][rr >> 1], sel);
+          *reinterpret_cast<u32x4*>(lds + swz(rb * 8 + rr, kb)) = w;
+        }
+      }
+    }
+  }
+};
+
+template <bool A_K, bool B_K, int BM, int BN, int WM, int WN, int KIND>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
+  constexpr int NT = 64 * WM * WN, BK = 64;
+  constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
+  static_assert(TM >= 1 && TN >= 1, "wave tile must hold 32x32 MFMA blocks");
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * (BM + BN) * BK];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm0 = (wave / WN) * (BM / WM), wn0 = (wave % WN) * (BN / WN);
+  const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+  int tm, tn;
+  map_tile<4>(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  if (g.causal == CAUSAL_SKIP_UPPER && n0 > m0 + BM - 1) return;
+  int kbeg, kend;
+  causal_k_range(g, m0, BM, kbeg, kend);
+  const int z = blockIdx.y, zo = z / g.zdiv, zi = z % g.zdiv;
+  const bf16* A = static_cast<const bf16*>(g.A) + zo * g.a_so + zi * g.a_si;
+  const bf16* B = static_cast<const bf16*>(g.B) + zo * g.b_so + zi * g.b_si;
+
+  TileLoader<BM, NT, A_K> la;
+  TileLoader<BN, NT, B_K> lb;
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+  if (nk > 0) {
+    la.load(A, g.lda, m0, g.M, kbeg, kend, tid);
+    lb.load(B, g.ldb, n0, g.N, kbeg, kend, tid);
+    la.store(smem, tid);
+    lb.store(smem + BM * BK, tid);
+    __syncthreads();
+    for (int t = 0; t < nk; ++t) {
+      const int cur = t & 1;
+      if (t + 1 < nk) {
+        la.load(A, g.lda, m0, g.M, kbeg + (t + 1) * BK, kend, tid);
+        lb.load(B, g.ldb, n0, g.N, kbeg + (t + 1) * BK, kend, tid);
+      }
+      const bf16* sA = smem + cur * (BM + BN) * BK;
+      const bf16* sB = sA + BM * BK;
+#pragma unroll
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        // 32x32x16 operands: lane l supplies row (l & 31) and 8 consecutive k
+        // starting at 8 * (l >> 5) of the 16-wide k step.
+        const int ch = ks * 2 + (lane >> 5);
+        bf16x8 af[TM], bfr[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(sA + swz(wm0 + i * 32 + (lane & 31), ch));
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(sB + swz(wn0 + j * 32 + (lane & 31), ch));
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      }
+      if (t + 1 < nk) {
+        bf16* nxt = smem + (cur ^ 1) * (BM + BN) * BK;
+        la.store(nxt, tid);
+        lb.store(nxt + BM * BK, tid);
+      }
+      __syncthreads();
+    }
+  }
+
+  // 32x32 accumulator layout: lane l holds column (l & 31) and, in register r, row
+  // 8 * (r >> 2) + 4 * (l >> 5) + (r & 3).
+  const int64_t coff = zo * g.c_so + zi * g.c_si;
+  const int64_t voff = (int64_t)z * g.vec_bs;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int n = n0 + wn0 + j * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        if (m < g.M && n < g.N) epi_store<bf16, KIND>(g, coff, voff, m, n, acc[i][j][r]);
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------- fp32 SIMT
+// fp32 path: 64x64 tiles, 16-deep k steps through LDS, 4x4 outputs per thread, fp32
+// fused multiply-add. Same operand layouts, causal modes and epilogues as the MFMA path.
+template <bool A_K, bool B_K, int KIND>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
+  constexpr int BM = 64, BN = 64, BK = 16;
+  __shared__ float sA[BK][BM + 4];
+  __shared__ float sB[BK][BN + 4];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int tiles_n = (g.N + BN - 1) / BN;
+  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+  const int m0 = tm * BM, n0 = tn * BN;
+  if (g.causal == CAUSAL_SKIP_UPPER && n0 > m0 + BM - 1) return;
+  int kbeg, kend;
+  causal_k_range(g, m0, BM, kbeg, kend);
+  const int z = blockIdx.y, zo = z / g.zdiv, zi = z % g.zdiv;
+  const float* A = static_cast<const float*>(g.A) + zo * g.a_so + zi * g.a_si;
+  const float* B = static_cast<const float*>(g.B) + zo * g.b_so + zi * g.b_si;
+  float acc[4][4] = {};
+  for (int k0 = kbeg; k0 < kend; k0 += BK) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid + i * 256;
+      int r, k;
+      if (A_K) { r = e >> 4; k = e & 15; } else { k = e >> 6; r = e & 63; }
+      int gr = m0 + r, gk = k0 + k;
+      sA[k][r] = (gr < g.M && gk < kend) ? A[A_K ? (int64_t)gr * g.lda + gk : (int64_t)gk * g.lda + gr] : 0.f;
+      if (B_K) { r = e >> 4; k = e & 15; } else { k = e >> 6; r = e & 63; }
+      gr = n0 + r;
+      gk = k0 + k;
+      sB[k][r] = (gr < g.N && gk < kend) ? B[B_K ? (int64_t)gr * g.ldb + gk : (int64_t)gk * g.ldb + gr] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < BK; ++k) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = sA[k][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = sB[k][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  const int64_t coff = zo * g.c_so + zi * g.c_si;
+  const int64_t voff = (int64_t)z * g.vec_bs;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = m0 + ty * 4 + i, n = n0 + tx * 4 + j;
+      if (m < g.M && n < g.N) epi_store<float, KIND>(g, coff, voff, m, n, acc[i][j]);
+    }
+}
+
+}  // namespace mt

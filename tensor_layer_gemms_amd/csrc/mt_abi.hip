@@ -1,0 +1,684 @@
+// Host side of the layer shard: argument validation, carving of the saved-activation
+// and workspace buffers, and the launch sequences of forward and backward on the
+// caller's stream. Exposes the C ABI declared in include/mt.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "gemm.hpp"
+#include "mt.h"
+#include "rowwise.hpp"
+
+namespace mt {
+namespace {
+
+constexpr float kLnEps = 1e-5f;  // LayerNorm epsilon (silent on the pages; common default)
+
+// ------------------------------------------------------------------------- shapes
+struct Dims {
+  int64_t M, h, heads, at, d, seq, B, tp, hs, qkv, ft;
+  bool bf16;
+  int64_t es;  // bytes per activation element
+};
+
+int validate_shape(const mt_shape* s, Dims* out) {
+  if (!s) return MT_ERR_INVALID_ARG;
+  if (s->h <= 0 || s->heads <= 0 || s->seq <= 0 || s->micro_batch <= 0 || s->tp <= 0) return MT_ERR_INVALID_ARG;
+  if (s->shard < 0 || s->shard >= s->tp) return MT_ERR_INVALID_ARG;
+  if (s->dtype != MT_BF16 && s->dtype != MT_FP32) return MT_ERR_INVALID_ARG;
+  if (s->h % s->heads != 0 || s->heads % s->tp != 0) return MT_ERR_INVALID_ARG;
+  const int64_t d = s->h / s->heads;
+  if (d % 8 != 0 || s->seq % 8 != 0) return MT_ERR_UNSUPPORTED;
+  if (s->seq > kSoftmaxMaxSeq) return MT_ERR_UNSUPPORTED;
+  const int64_t hmax = (s->dtype == MT_BF16 ? 8 : 4) * (int64_t)kLnThreads * kLnChunksPerThread;
+  if (s->h > hmax) return MT_ERR_UNSUPPORTED;
+  const int64_t M = (int64_t)s->micro_batch * s->seq;
+  if (M > (1 << 24)) return MT_ERR_UNSUPPORTED;
+  Dims x;
+  x.M = M;
+  x.h = s->h;
+  x.heads = s->heads;
+  x.tp = s->tp;
+  x.at = s->heads / s->tp;
+  x.d = d;
+  x.seq = s->seq;
+  x.B = s->micro_batch;
+  x.hs = x.at * d;
+  x.qkv = 3 * x.hs;
+  x.ft = 4 * x.h / x.tp;
+  x.bf16 = s->dtype == MT_BF16;
+  x.es = x.bf16 ? 2 : 4;
+  *out = x;
+  return MT_OK;
+}
+
+bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Sub-buffers are carved at 256-byte boundaries; the same code sizes (base == null)
+// and carves, so the *_bytes queries always match what the calls use.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <class P = void>
+  P* take(size_t bytes) {
+    off = (off + 255) & ~size_t(255);
+    P* p = base ? reinterpret_cast<P*>(base + off) : nullptr;
+    off += bytes;
+    return p;
+  }
+};
+
+struct LayerSaved {
+  float *mean1, *rstd1, *mean2, *rstd2;
+  void *u, *qkv, *p, *ctx, *x2, *v2, *a, *z;
+};
+
+size_t carve_layer_saved(const Dims& d, void* base, LayerSaved* s) {
+  Carver c(base);
+  s->mean1 = c.take<float>(d.M * 4);
+  s->rstd1 = c.take<float>(d.M * 4);
+  s->mean2 = c.take<float>(d.M * 4);
+  s->rstd2 = c.take<float>(d.M * 4);
+  s->u = c.take(d.M * d.h * d.es);
+  s->qkv = c.take(d.M * d.qkv * d.es);
+  s->p = c.take(d.B * d.at * d.seq * d.seq * d.es);
+  s->ctx = c.take(d.M * d.hs * d.es);
+  s->x2 = c.take(d.M * d.h * d.es);
+  s->v2 = c.take(d.M * d.h * d.es);
+  s->a = c.take(d.M * d.ft * d.es);
+  s->z = c.take(d.M * d.ft * d.es);
+  return c.off;
+}
+
+struct LayerFwdWs {
+  float* S;
+  void* o;  // out-projection partial, then FC2 partial
+};
+
+size_t carve_layer_fwd_ws(const Dims& d, void* base, LayerFwdWs* w) {
+  Carver c(base);
+  w->S = c.take<float>(d.B * d.at * d.seq * d.seq * 4);
+  w->o = c.take(d.M * d.h * d.es);
+  return c.off;
+}
+
+struct LayerBwdWs {
+  void *da, *dv2, *dx2, *dctx, *ds, *dqkv;
+  float *D, *part;
+};
+
+size_t colsum_floats(const Dims& d) {
+  size_t n = colsum_partial_floats((int)d.M, (int)d.h, 1);
+  n = std::max(n, colsum_partial_floats((int)d.M, (int)d.ft, 0));
+  n = std::max(n, colsum_partial_floats((int)d.M, (int)d.qkv, 0));
+  return n;
+}
+
+size_t carve_layer_bwd_ws(const Dims& d, void* base, LayerBwdWs* w) {
+  Carver c(base);
+  w->da = c.take(d.M * d.ft * d.es);
+  w->dv2 = c.take(d.M * d.h * d.es);  // dV2 partial, later dU partial
+  w->dx2 = c.take(d.M * d.h * d.es);
+  w->dctx = c.take(d.M * d.hs * d.es);
+  w->ds = c.take(d.B * d.at * d.seq * d.seq * d.es);
+  w->dqkv = c.take(d.M * d.qkv * d.es);
+  w->D = c.take<float>(d.B * d.at * d.seq * 4);
+  w->part = c.take<float>(colsum_floats(d) * 4);
+  return c.off;
+}
+
+struct MlpSaved {
+  void *a, *z;
+};
+size_t carve_mlp_saved(const Dims& d, void* base, MlpSaved* s) {
+  Carver c(base);
+  s->a = c.take(d.M * d.ft * d.es);
+  s->z = c.take(d.M * d.ft * d.es);
+  return c.off;
+}
+struct MlpWs {
+  void* da;
+  float* part;
+};
+size_t carve_mlp_ws(const Dims& d, void* base, MlpWs* w) {
+  Carver c(base);
+  w->da = c.take(d.M * d.ft * d.es);
+  w->part = c.take<float>(colsum_partial_floats((int)d.M, (int)d.ft, 0) * 4);
+  return c.off;
+}
+
+// ------------------------------------------------------------------------- timing
+struct TimingRec {
+  std::string label;
+  hipEvent_t a, b;
+  double flops, bytes;
+};
+
+std::mutex g_tmu;
+bool g_timing = false;
+std::string g_filter;
+std::vector<TimingRec> g_recs;
+std::vector<hipEvent_t> g_free;
+
+hipEvent_t timing_event() {
+  if (!g_free.empty()) {
+    hipEvent_t e = g_free.back();
+    g_free.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Enqueues one launch (f returns hipError_t), optionally bracketed by timing events.
+class Seq {
+ public:
+  explicit Seq(hipStream_t s) : s_(s) {}
+  template <class F>
+  bool run(const char* label, double flops, double bytes, F&& f) {
+    if (err_ != hipSuccess) return false;
+    hipEvent_t a = nullptr, b = nullptr;
+    bool timed = false;
+    if (g_timing) {
+      std::lock_guard<std::mutex> lk(g_tmu);
+      if (g_timing && (g_filter.empty() || std::strstr(label, g_filter.c_str()) != nullptr)) {
+        a = timing_event();
+        b = timing_event();
+        timed = a && b;
+      }
+    }
+    if (timed && hipEventRecord(a, s_) != hipSuccess) timed = false;
+    err_ = f();
+    if (timed && hipEventRecord(b, s_) == hipSuccess) {
+      std::lock_guard<std::mutex> lk(g_tmu);
+      g_recs.push_back({label, a, b, flops, bytes});
+    }
+    return err_ == hipSuccess;
+  }
+  int status() const { return err_ == hipSuccess ? MT_OK : MT_ERR_HIP; }
+  hipStream_t stream() const { return s_; }
+
+ private:
+  hipStream_t s_;
+  hipError_t err_ = hipSuccess;
+};
+
+// ------------------------------------------------------------------------- GEMM helpers
+GemmArgs plain(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, int64_t M, int64_t N,
+               int64_t K) {
+  GemmArgs g;
+  std::memset(&g, 0, sizeof(g));
+  g.A = A;
+  g.B = B;
+  g.C = C;
+  g.lda = lda;
+  g.ldb = ldb;
+  g.ldc = ldc;
+  g.M = (int)M;
+  g.N = (int)N;
+  g.K = (int)K;
+  g.zdiv = 1;
+  g.alpha = 1.0f;
+  return g;
+}
+
+hipError_t gemm(const Dims& d, const GemmArgs& g, bool a_k, bool b_k, int kind, int batch, hipStream_t s) {
+  return d.bf16 ? launch_gemm_bf16(g, a_k, b_k, kind, batch, s) : launch_gemm_f32(g, a_k, b_k, kind, batch, s);
+}
+
+double gflop(double m, double n, double k) { return 2.0 * m * n * k; }
+
+// Per-head attention products over (b, k) pairs: batch z = b * at + k.
+struct Attn {
+  const Dims& d;
+  double causal_pairs() const { return (double)d.seq * (d.seq + 1) / 2.0; }
+  double flops() const { return 2.0 * d.d * causal_pairs() * d.B * d.at; }
+  // head slice of an [M, ld] activation whose head k starts at column col0 + k*d
+  void head_operand(int64_t ld, int64_t& so, int64_t& si) const {
+    so = d.seq * ld;
+    si = d.d;
+  }
+};
+
+// ------------------------------------------------------------------------- forward
+int layer_fwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, void* out, const LayerSaved& sv,
+                   const LayerFwdWs& ws, hipStream_t stream) {
+  Seq q(stream);
+  const bool bf = d.bf16;
+  const double es = (double)d.es;
+  const double Mh = (double)d.M * d.h;
+  const float scale = 1.0f / std::sqrt((float)d.d);
+  const int batch = (int)(d.B * d.at);
+  Attn at{d};
+
+  // F1 LayerNorm 1
+  q.run("ln1_fwd", 0, 2 * Mh * es, [&] {
+    return launch_ln_fwd(bf, false, x, nullptr, nullptr, w.ln1_g, w.ln1_b, nullptr, sv.u, sv.mean1, sv.rstd1,
+                         (int)d.M, (int)d.h, kLnEps, stream);
+  });
+  // F2 column-parallel QKV projection + bias
+  q.run("qkv_fwd", gflop(d.M, d.qkv, d.h), 0, [&] {
+    GemmArgs g = plain(sv.u, d.h, w.w_qkv, d.h, sv.qkv, d.qkv, d.M, d.qkv, d.h);
+    g.vec = w.b_qkv;
+    return gemm(d, g, true, true, EPI_BIAS, 1, stream);
+  });
+  // F3 scores S = Q K^T / sqrt(d), causal tiles only, fp32
+  q.run("attn_scores", at.flops(), 0, [&] {
+    GemmArgs g = plain(sv.qkv, d.qkv, static_cast<const char*>(sv.qkv) + d.hs * d.es, d.qkv, ws.S, d.seq, d.seq,
+                       d.seq, d.d);
+    at.head_operand(d.qkv, g.a_so, g.a_si);
+    at.head_operand(d.qkv, g.b_so, g.b_si);
+    g.c_so = d.at * d.seq * d.seq;
+    g.c_si = d.seq * d.seq;
+    g.zdiv = (int)d.at;
+    g.causal = CAUSAL_SKIP_UPPER;
+    g.alpha = scale;
+    return gemm(d, g, true, true, EPI_STORE_F32, batch, stream);
+  });
+  // F4 causal softmax -> P
+  q.run("softmax_fwd", 0, (double)batch * at.causal_pairs() * (4 + es), [&] {
+    return launch_softmax_causal(bf, ws.S, sv.p, batch, (int)d.seq, stream);
+  });
+  // F5 ctx = P V (k <= q), heads concatenated in columns
+  q.run("attn_ctx", at.flops(), 0, [&] {
+    GemmArgs g = plain(sv.p, d.seq, static_cast<const char*>(sv.qkv) + 2 * d.hs * d.es, d.qkv, sv.ctx, d.hs, d.seq,
+                       d.d, d.seq);
+    g.a_so = d.at * d.seq * d.seq;
+    g.a_si = d.seq * d.seq;
+    at.head_operand(d.qkv, g.b_so, g.b_si);
+    at.head_operand(d.hs, g.c_so, g.c_si);
+    g.zdiv = (int)d.at;
+    g.causal = CAUSAL_K_LE_M;
+    return gemm(d, g, true, false, EPI_STORE, batch, stream);
+  });
+  // F6 row-parallel out-projection: partial sum O_i (the all-reduce input)
+  q.run("out_proj_fwd", gflop(d.M, d.h, d.hs), 0, [&] {
+    GemmArgs g = plain(sv.ctx, d.hs, w.w_o, d.hs, ws.o, d.h, d.M, d.h, d.hs);
+    return gemm(d, g, true, true, EPI_STORE, 1, stream);
+  });
+  // F7 X2 = X + AR(O_i) + b_o (AR = identity on one GPU), V2 = LN2(X2)
+  q.run("add_ln2_fwd", 0, 4 * Mh * es, [&] {
+    return launch_ln_fwd(bf, true, x, ws.o, w.b_o, w.ln2_g, w.ln2_b, sv.x2, sv.v2, sv.mean2, sv.rstd2, (int)d.M,
+                         (int)d.h, kLnEps, stream);
+  });
+  // F8 column-parallel FC1 with fused bias + GeLU (keeps A and Z)
+  q.run("fc1_fwd", gflop(d.M, d.ft, d.h), 0, [&] {
+    GemmArgs g = plain(sv.v2, d.h, w.w_fc1, d.h, sv.a, d.ft, d.M, d.ft, d.h);
+    g.vec = w.b_fc1;
+    g.C2 = sv.z;
+    return gemm(d, g, true, true, EPI_BIAS_GELU, 1, stream);
+  });
+  // F9 row-parallel FC2: partial sum Y_i
+  q.run("fc2_fwd", gflop(d.M, d.h, d.ft), 0, [&] {
+    GemmArgs g = plain(sv.z, d.ft, w.w_fc2, d.ft, ws.o, d.h, d.M, d.h, d.ft);
+    return gemm(d, g, true, true, EPI_STORE, 1, stream);
+  });
+  // F10 Out = X2 + AR(Y_i) + b_fc2
+  q.run("bias_residual_fwd", 0, 3 * Mh * es, [&] {
+    return launch_add_bias_residual(bf, sv.x2, ws.o, w.b_fc2, out, (int)d.M, (int)d.h, stream);
+  });
+  return q.status();
+}
+
+// ------------------------------------------------------------------------- backward
+int layer_bwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, const LayerSaved& sv, const void* dout,
+                   void* dx, const mt_layer_grads& gr, const LayerBwdWs& ws, hipStream_t stream) {
+  Seq q(stream);
+  const bool bf = d.bf16;
+  const double es = (double)d.es;
+  const double Mh = (double)d.M * d.h;
+  const float scale = 1.0f / std::sqrt((float)d.d);
+  const int batch = (int)(d.B * d.at);
+  const int M = (int)d.M;
+  Attn at{d};
+
+  // B1 FC2: db_fc2, dW2 = dOut^T Z, dA = (dOut W2) * GeLU'(A)
+  q.run("db_fc2", 0, Mh * es, [&] {
+    return launch_colsum(bf, 0, dout, nullptr, nullptr, nullptr, gr.b_fc2, nullptr, ws.part, M, (int)d.h, stream);
+  });
+  q.run("fc2_wgrad", gflop(d.h, d.ft, d.M), 0, [&] {
+    GemmArgs g = plain(dout, d.h, sv.z, d.ft, gr.w_fc2, d.ft, d.h, d.ft, d.M);
+    return gemm(d, g, false, false, EPI_STORE_F32, 1, stream);
+  });
+  q.run("fc2_dgrad", gflop(d.M, d.ft, d.h), 0, [&] {
+    GemmArgs g = plain(dout, d.h, w.w_fc2, d.ft, ws.da, d.ft, d.M, d.ft, d.h);
+    g.aux = sv.a;
+    return gemm(d, g, true, false, EPI_DGELU, 1, stream);
+  });
+  // B2 FC1: db_fc1, dW1 = dA^T V2, dV2 = dA W1 (partial)
+  q.run("db_fc1", 0, d.M * d.ft * es, [&] {
+    return launch_colsum(bf, 0, ws.da, nullptr, nullptr, nullptr, gr.b_fc1, nullptr, ws.part, M, (int)d.ft, stream);
+  });
+  q.run("fc1_wgrad", gflop(d.ft, d.h, d.M), 0, [&] {
+    GemmArgs g = plain(ws.da, d.ft, sv.v2, d.h, gr.w_fc1, d.h, d.ft, d.h, d.M);
+    return gemm(d, g, false, false, EPI_STORE_F32, 1, stream);
+  });
+  q.run("fc1_dgrad", gflop(d.M, d.h, d.ft), 0, [&] {
+    GemmArgs g = plain(ws.da, d.ft, w.w_fc1, d.h, ws.dv2, d.h, d.M, d.h, d.ft);
+    return gemm(d, g, true, false, EPI_STORE, 1, stream);
+  });
+  // B3 dX2 = dOut + LN2-backward(AR(dV2)); dgamma2, dbeta2; db_o = colsum(dX2)
+  q.run("ln2_bwd", 0, 4 * Mh * es, [&] {
+    return launch_ln_bwd(bf, ws.dv2, sv.x2, w.ln2_g, sv.mean2, sv.rstd2, dout, ws.dx2, M, (int)d.h, stream);
+  });
+  q.run("ln2_param_grads", 0, 2 * Mh * es, [&] {
+    return launch_colsum(bf, 1, ws.dv2, sv.x2, sv.mean2, sv.rstd2, gr.ln2_g, gr.ln2_b, ws.part, M, (int)d.h, stream);
+  });
+  q.run("db_o", 0, Mh * es, [&] {
+    return launch_colsum(bf, 0, ws.dx2, nullptr, nullptr, nullptr, gr.b_o, nullptr, ws.part, M, (int)d.h, stream);
+  });
+  // B4 out-projection: dW_o = dX2^T ctx, dctx = dX2 W_o
+  q.run("out_proj_wgrad", gflop(d.h, d.hs, d.M), 0, [&] {
+    GemmArgs g = plain(ws.dx2, d.h, sv.ctx, d.hs, gr.w_o, d.hs, d.h, d.hs, d.M);
+    return gemm(d, g, false, false, EPI_STORE_F32, 1, stream);
+  });
+  q.run("out_proj_dgrad", gflop(d.M, d.hs, d.h), 0, [&] {
+    GemmArgs g = plain(ws.dx2, d.h, w.w_o, d.hs, ws.dctx, d.hs, d.M, d.hs, d.h);
+    return gemm(d, g, true, false, EPI_STORE, 1, stream);
+  });
+  // B5/B6 attention: D = rowsum(dctx * ctx) = rowsum(P * dP); dS = P * (dctx V^T - D)
+  q.run("attn_rowdot", 0, 2.0 * d.M * d.hs * es, [&] {
+    return launch_attn_rowdot(bf, ws.dctx, sv.ctx, ws.D, (int)d.B, (int)d.seq, (int)d.at, (int)d.d, stream);
+  });
+  const char* qkv = static_cast<const char*>(sv.qkv);
+  char* dqkv = static_cast<char*>(ws.dqkv);
+  q.run("attn_dscores", at.flops(), 0, [&] {
+    GemmArgs g = plain(ws.dctx, d.hs, qkv + 2 * d.hs * d.es, d.qkv, ws.ds, d.seq, d.seq, d.seq, d.d);
+    at.head_operand(d.hs, g.a_so, g.a_si);
+    at.head_operand(d.qkv, g.b_so, g.b_si);
+    g.c_so = d.at * d.seq * d.seq;
+    g.c_si = d.seq * d.seq;
+    g.aux = sv.p;
+    g.vec = ws.D;
+    g.vec_bs = d.seq;
+    g.zdiv = (int)d.at;
+    g.causal = CAUSAL_SKIP_UPPER;
+    return gemm(d, g, true, true, EPI_DSOFTMAX, batch, stream);
+  });
+  q.run("attn_dv", at.flops(), 0, [&] {  // dV = P^T dctx (q >= j)
+    GemmArgs g = plain(sv.p, d.seq, ws.dctx, d.hs, dqkv + 2 * d.hs * d.es, d.qkv, d.seq, d.d, d.seq);
+    g.a_so = d.at * d.seq * d.seq;
+    g.a_si = d.seq * d.seq;
+    at.head_operand(d.hs, g.b_so, g.b_si);
+    at.head_operand(d.qkv, g.c_so, g.c_si);
+    g.zdiv = (int)d.at;
+    g.causal = CAUSAL_K_GE_M;
+    return gemm(d, g, false, false, EPI_STORE, batch, stream);
+  });
+  q.run("attn_dq", at.flops(), 0, [&] {  // dQ = dS K / sqrt(d) (j <= q)
+    GemmArgs g = plain(ws.ds, d.seq, qkv + d.hs * d.es, d.qkv, dqkv, d.qkv, d.seq, d.d, d.seq);
+    g.a_so = d.at * d.seq * d.seq;
+    g.a_si = d.seq * d.seq;
+    at.head_operand(d.qkv, g.b_so, g.b_si);
+    at.head_operand(d.qkv, g.c_so, g.c_si);
+    g.zdiv = (int)d.at;
+    g.causal = CAUSAL_K_LE_M;
+    g.alpha = scale;
+    return gemm(d, g, true, false, EPI_STORE, batch, stream);
+  });
+  q.run("attn_dk", at.flops(), 0, [&] {  // dK = dS^T Q / sqrt(d) (q >= j)
+    GemmArgs g = plain(ws.ds, d.seq, qkv, d.qkv, dqkv + d.hs * d.es, d.qkv, d.seq, d.d, d.seq);
+    g.a_so = d.at * d.seq * d.seq;
+    g.a_si = d.seq * d.seq;
+    at.head_operand(d.qkv, g.b_so, g.b_si);
+    at.head_operand(d.qkv, g.c_so, g.c_si);
+    g.zdiv = (int)d.at;
+    g.causal = CAUSAL_K_GE_M;
+    g.alpha = scale;
+    return gemm(d, g, false, false, EPI_STORE, batch, stream);
+  });
+  // B7 QKV: db_qkv, dW_qkv = dQKV^T U, dU = dQKV W_qkv (partial)
+  q.run("db_qkv", 0, d.M * d.qkv * es, [&] {
+    return launch_colsum(bf, 0, ws.dqkv, nullptr, nullptr, nullptr, gr.b_qkv, nullptr, ws.part, M, (int)d.qkv,
+                         stream);
+  });
+  q.run("qkv_wgrad", gflop(d.qkv, d.h, d.M), 0, [&] {
+    GemmArgs g = plain(ws.dqkv, d.qkv, sv.u, d.h, gr.w_qkv, d.h, d.qkv, d.h, d.M);
+    return gemm(d, g, false, false, EPI_STORE_F32, 1, stream);
+  });
+  q.run("qkv_dgrad", gflop(d.M, d.h, d.qkv), 0, [&] {
+    GemmArgs g = plain(ws.dqkv, d.qkv, w.w_qkv, d.h, ws.dv2, d.h, d.M, d.h, d.qkv);
+    return gemm(d, g, true, false, EPI_STORE, 1, stream);
+  });
+  // B8 dX = dX2 + LN1-backward(AR(dU)); dgamma1, dbeta1
+  q.run("ln1_bwd", 0, 4 * Mh * es, [&] {
+    return launch_ln_bwd(bf, ws.dv2, x, w.ln1_g, sv.mean1, sv.rstd1, ws.dx2, dx, M, (int)d.h, stream);
+  });
+  q.run("ln1_param_grads", 0, 2 * Mh * es, [&] {
+    return launch_colsum(bf, 1, ws.dv2, x, sv.mean1, sv.rstd1, gr.ln1_g, gr.ln1_b, ws.part, M, (int)d.h, stream);
+  });
+  return q.status();
+}
+
+// ------------------------------------------------------------------------- MLP block
+int mlp_fwd_impl(const Dims& d, const void* x, const void* w1, const void* b1, const void* w2, void* y,
+                 const MlpSaved& sv, hipStream_t stream) {
+  Seq q(stream);
+  q.run("fc1_fwd", gflop(d.M, d.ft, d.h), 0, [&] {
+    GemmArgs g = plain(x, d.h, w1, d.h, sv.a, d.ft, d.M, d.ft, d.h);
+    g.vec = b1;
+    g.C2 = sv.z;
+    return gemm(d, g, true, true, EPI_BIAS_GELU, 1, stream);
+  });
+  q.run("fc2_fwd", gflop(d.M, d.h, d.ft), 0, [&] {
+    GemmArgs g = plain(sv.z, d.ft, w2, d.ft, y, d.h, d.M, d.h, d.ft);
+    return gemm(d, g, true, true, EPI_STORE, 1, stream);
+  });
+  return q.status();
+}
+
+int mlp_bwd_impl(const Dims& d, const void* x, const void* w1, const void* w2, const MlpSaved& sv, const void* dy,
+                 void* dx, float* dw1, float* db1, float* dw2, const MlpWs& ws, hipStream_t stream) {
+  Seq q(stream);
+  q.run("fc2_wgrad", gflop(d.h, d.ft, d.M), 0, [&] {
+    GemmArgs g = plain(dy, d.h, sv.z, d.ft, dw2, d.ft, d.h, d.ft, d.M);
+    return gemm(d, g, false, false, EPI_STORE_F32, 1, stream);
+  });
+  q.run("fc2_dgrad", gflop(d.M, d.ft, d.h), 0, [&] {
+    GemmArgs g = plain(dy, d.h, w2, d.ft, ws.da, d.ft, d.M, d.ft, d.h);
+    g.aux = sv.a;
+    return gemm(d, g, true, false, EPI_DGELU, 1, stream);
+  });
+  q.run("db_fc1", 0, (double)d.M * d.ft * d.es, [&] {
+    return launch_colsum(d.bf16, 0, ws.da, nullptr, nullptr, nullptr, db1, nullptr, ws.part, (int)d.M, (int)d.ft,
+                         stream);
+  });
+  q.run("fc1_wgrad", gflop(d.ft, d.h, d.M), 0, [&] {
+    GemmArgs g = plain(ws.da, d.ft, x, d.h, dw1, d.h, d.ft, d.h, d.M);
+    return gemm(d, g, false, false, EPI_STORE_F32, 1, stream);
+  });
+  q.run("fc1_dgrad", gflop(d.M, d.h, d.ft), 0, [&] {
+    GemmArgs g = plain(ws.da, d.ft, w1, d.h, dx, d.h, d.M, d.h, d.ft);
+    return gemm(d, g, true, false, EPI_STORE, 1, stream);
+  });
+  return q.status();
+}
+
+bool weights_ok(const mt_layer_weights* w) {
+  if (!w) return false;
+  const void* p[] = {w->ln1_g, w->ln1_b, w->w_qkv, w->b_qkv, w->w_o,   w->b_o,
+                     w->ln2_g, w->ln2_b, w->w_fc1, w->b_fc1, w->w_fc2, w->b_fc2};
+  for (const void* q : p)
+    if (!aligned16(q)) return false;
+  return true;
+}
+
+bool grads_ok(const mt_layer_grads* g) {
+  if (!g) return false;
+  const void* p[] = {g->ln1_g, g->ln1_b, g->w_qkv, g->b_qkv, g->w_o,   g->b_o,
+                     g->ln2_g, g->ln2_b, g->w_fc1, g->b_fc1, g->w_fc2, g->b_fc2};
+  for (const void* q : p)
+    if (!aligned16(q)) return false;
+  return true;
+}
+
+}  // namespace
+}  // namespace mt
+
+using namespace mt;
+
+extern "C" {
+
+size_t mt_layer_saved_bytes(const mt_shape* shape) {
+  Dims d;
+  if (validate_shape(shape, &d) != MT_OK) return 0;
+  LayerSaved s;
+  return carve_layer_saved(d, nullptr, &s);
+}
+
+size_t mt_layer_workspace_bytes(const mt_shape* shape) {
+  Dims d;
+  if (validate_shape(shape, &d) != MT_OK) return 0;
+  LayerFwdWs f;
+  LayerBwdWs b;
+  return std::max(carve_layer_fwd_ws(d, nullptr, &f), carve_layer_bwd_ws(d, nullptr, &b));
+}
+
+int mt_layer_fwd(const mt_shape* shape, const mt_layer_weights* w, const void* x, void* out, void* saved,
+                 size_t saved_bytes, void* workspace, size_t workspace_bytes, void* stream) {
+  Dims d;
+  int st = validate_shape(shape, &d);
+  if (st != MT_OK) return st;
+  if (!weights_ok(w) || !aligned16(x) || !aligned16(out) || !aligned16(saved) || !aligned16(workspace))
+    return MT_ERR_INVALID_ARG;
+  LayerSaved sv;
+  LayerFwdWs ws;
+  if (saved_bytes < carve_layer_saved(d, nullptr, &sv) || workspace_bytes < mt_layer_workspace_bytes(shape))
+    return MT_ERR_WORKSPACE;
+  carve_layer_saved(d, saved, &sv);
+  carve_layer_fwd_ws(d, workspace, &ws);
+  return layer_fwd_impl(d, *w, x, out, sv, ws, static_cast<hipStream_t>(stream));
+}
+
+int mt_layer_bwd(const mt_shape* shape, const mt_layer_weights* w, const void* x, const void* saved,
+                 size_t saved_bytes, const void* dout, void* dx, const mt_layer_grads* grads, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  Dims d;
+  int st = validate_shape(shape, &d);
+  if (st != MT_OK) return st;
+  if (!weights_ok(w) || !grads_ok(grads) || !aligned16(x) || !aligned16(saved) || !aligned16(dout) ||
+      !aligned16(dx) || !aligned16(workspace))
+    return MT_ERR_INVALID_ARG;
+  LayerSaved sv;
+  LayerBwdWs ws;
+  if (saved_bytes < carve_layer_saved(d, nullptr, &sv) || workspace_bytes < mt_layer_workspace_bytes(shape))
+    return MT_ERR_WORKSPACE;
+  carve_layer_saved(d, const_cast<void*>(saved), &sv);
+  carve_layer_bwd_ws(d, workspace, &ws);
+  return layer_bwd_impl(d, *w, x, sv, dout, dx, *grads, ws, static_cast<hipStream_t>(stream));
+}
+
+size_t mt_mlp_saved_bytes(const mt_shape* shape) {
+  Dims d;
+  if (validate_shape(shape, &d) != MT_OK) return 0;
+  MlpSaved s;
+  return carve_mlp_saved(d, nullptr, &s);
+}
+
+size_t mt_mlp_workspace_bytes(const mt_shape* shape) {
+  Dims d;
+  if (validate_shape(shape, &d) != MT_OK) return 0;
+  MlpWs w;
+  return carve_mlp_ws(d, nullptr, &w);
+}
+
+int mt_mlp_fwd(const mt_shape* shape, const void* x, const void* w_fc1, const void* b_fc1, const void* w_fc2,
+               void* y_partial, void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes,
+               void* stream) {
+  Dims d;
+  int st = validate_shape(shape, &d);
+  if (st != MT_OK) return st;
+  (void)workspace;
+  if (!aligned16(x) || !aligned16(w_fc1) || !aligned16(b_fc1) || !aligned16(w_fc2) || !aligned16(y_partial) ||
+      !aligned16(saved))
+    return MT_ERR_INVALID_ARG;
+  if (workspace && !aligned16(workspace)) return MT_ERR_INVALID_ARG;
+  MlpSaved sv;
+  if (saved_bytes < carve_mlp_saved(d, nullptr, &sv)) return MT_ERR_WORKSPACE;
+  (void)workspace_bytes;  // the forward needs no scratch
+  carve_mlp_saved(d, saved, &sv);
+  return mlp_fwd_impl(d, x, w_fc1, b_fc1, w_fc2, y_partial, sv, static_cast<hipStream_t>(stream));
+}
+
+int mt_mlp_bwd(const mt_shape* shape, const void* x, const void* w_fc1, const void* w_fc2, const void* saved,
+               size_t saved_bytes, const void* dy, void* dx_partial, float* dw_fc1, float* db_fc1, float* dw_fc2,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  Dims d;
+  int st = validate_shape(shape, &d);
+  if (st != MT_OK) return st;
+  if (!aligned16(x) || !aligned16(w_fc1) || !aligned16(w_fc2) || !aligned16(saved) || !aligned16(dy) ||
+      !aligned16(dx_partial) || !aligned16(dw_fc1) || !aligned16(db_fc1) || !aligned16(dw_fc2) ||
+      !aligned16(workspace))
+    return MT_ERR_INVALID_ARG;
+  MlpSaved sv;
+  MlpWs ws;
+  if (saved_bytes < carve_mlp_saved(d, nullptr, &sv) || workspace_bytes < carve_mlp_ws(d, nullptr, &ws))
+    return MT_ERR_WORKSPACE;
+  carve_mlp_saved(d, const_cast<void*>(saved), &sv);
+  carve_mlp_ws(d, workspace, &ws);
+  return mlp_bwd_impl(d, x, w_fc1, w_fc2, sv, dy, dx_partial, dw_fc1, db_fc1, dw_fc2, ws,
+                      static_cast<hipStream_t>(stream));
+}
+
+const char* mt_status_string(int status) {
+  switch (status) {
+    case MT_OK: return "ok";
+    case MT_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, or inconsistent shape)";
+    case MT_ERR_UNSUPPORTED: return "unsupported shape (head dim or seq not a multiple of 8, seq > 4096, h too large)";
+    case MT_ERR_HIP: return "HIP launch or runtime error";
+    case MT_ERR_WORKSPACE: return "saved or workspace buffer smaller than the *_bytes query";
+    default: return "unknown status";
+  }
+}
+
+int mt_timing_enable(int enable, const char* label_filter) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  g_timing = enable != 0;
+  g_filter = label_filter ? label_filter : "";
+  return MT_OK;
+}
+
+int mt_timing_reset(void) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  for (auto& r : g_recs) {
+    g_free.push_back(r.a);
+    g_free.push_back(r.b);
+  }
+  g_recs.clear();
+  return MT_OK;
+}
+
+int mt_timing_count(void) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  return (int)g_recs.size();
+}
+
+int mt_timing_get(int i, char* label, size_t label_len, float* ms, double* flops, double* bytes) {
+  TimingRec r;
+  {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    if (i < 0 || i >= (int)g_recs.size()) return MT_ERR_INVALID_ARG;
+    r = g_recs[i];
+  }
+  if (label && label_len > 0) {
+    std::strncpy(label, r.label.c_str(), label_len - 1);
+    label[label_len - 1] = '\0';
+  }
+  if (hipEventSynchronize(r.b) != hipSuccess) return MT_ERR_HIP;
+  float t = 0.f;
+  if (hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) return MT_ERR_HIP;
+  if (ms) *ms = t;
+  if (flops) *flops = r.flops;
+  if (bytes) *bytes = r.bytes;
+  return MT_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,48 @@
+// Host launchers of the HBM-bound kernels: LayerNorm forward/backward (with the fused
+// bias + residual add), causal softmax, column sums (bias and LayerNorm parameter
+// gradients), the final bias + residual add and the attention row dot.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mt {
+
+// Largest row LayerNorm keeps in registers: 512 threads x 8 chunks of 16 bytes.
+constexpr int kLnThreads = 512;
+constexpr int kLnChunksPerThread = 8;
+// Longest causal softmax row kept in registers (64 lanes x 4 x 16 values).
+constexpr int kSoftmaxMaxSeq = 4096;
+
+// y = LN(x) (ADD == false) or, with ADD, x2 = x + o + bias written to x2 first and
+// y = LN(x2). Saves the row mean and 1/sqrt(var + eps) (fp32). T = bf16 (is_bf16) or fp32.
+hipError_t launch_ln_fwd(bool is_bf16, bool add, const void* x, const void* o, const void* bias,
+                         const void* gamma, const void* beta, void* x2, void* y, float* mean, float* rstd,
+                         int rows, int h, float eps, hipStream_t s);
+
+// dx = resid + LN-backward(dy; x, gamma, mean, rstd).
+hipError_t launch_ln_bwd(bool is_bf16, const void* dy, const void* x, const void* gamma, const float* mean,
+                         const float* rstd, const void* resid, void* dx, int rows, int h, hipStream_t s);
+
+// Column sums over `rows` rows, deterministic two-stage reduction through `partial`.
+// mode 0: out0[c] = sum_r a[r, c].
+// mode 1: out0[c] = sum_r a[r, c] * (x[r, c] - mean[r]) * rstd[r], out1[c] = sum_r a[r, c].
+size_t colsum_partial_floats(int rows, int cols, int mode);
+hipError_t launch_colsum(bool is_bf16, int mode, const void* a, const void* x, const float* mean,
+                         const float* rstd, float* out0, float* out1, float* partial, int rows, int cols,
+                         hipStream_t s);
+
+// out = x2 + y + bias (bias broadcast over rows).
+hipError_t launch_add_bias_residual(bool is_bf16, const void* x2, const void* y, const void* bias, void* out,
+                                    int rows, int h, hipStream_t s);
+
+// P = softmax over keys j <= q of S (fp32) for each of `nmat` [seq, seq] matrices;
+// row q is written for j < min(seq, roundup(q + 1, 256)), zeros right of the diagonal.
+hipError_t launch_softmax_causal(bool is_bf16, const float* S, void* P, int nmat, int seq, hipStream_t s);
+
+// D[(b * heads + k) * seq + q] = sum_c dctx[b*seq+q, k*d+c] * ctx[b*seq+q, k*d+c]
+// (= rowsum(P * dP) of head k, since ctx = P V and dP = dctx V^T).
+hipError_t launch_attn_rowdot(bool is_bf16, const void* dctx, const void* ctx, float* D, int batch, int seq,
+                              int heads, int d, hipStream_t s);
+
+}  // namespace mt

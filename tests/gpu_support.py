@@ -1,0 +1,138 @@
+"""Helpers for the GPU parity tests: seeded inputs to device tensors, one call of the
+HIP path through the C ABI, and the per-tensor comparison against the fp64 oracle.
+
+Tolerance (the stated bar): for every output tensor T,
+    max |T_gpu - T_oracle| <= tol * RMS(T_oracle),
+tol = 2e-2 for the bf16 path and 1e-4 for the fp32 path.
+"""
+from __future__ import annotations
+
+import sys
+from typing import Dict, List, Tuple
+
+import numpy as np
+
+import oracle
+import seeded_inputs as si
+
+TOL = {"bf16": 2e-2, "fp32": 1e-4}
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def mt_mod():
+    import tensor_layer_gemms_amd as mt
+    return mt
+
+
+def to_dev(a: np.ndarray, dtype: str):
+    torch = torch_mod()
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda")
+    return t.to(torch.bfloat16) if dtype == "bf16" else t
+
+
+def to_np(t) -> np.ndarray:
+    return t.detach().to(torch_mod().float32).cpu().numpy().astype(np.float64)
+
+
+def mt_shape(shape: si.LayerShape):
+    return mt_mod().make_shape(shape.h, shape.heads, shape.seq, shape.micro_batch, shape.tp, shape.shard, shape.dtype)
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_layer_gpu(shape: si.LayerShape, x: np.ndarray, dout: np.ndarray, params: Dict[str, np.ndarray],
+                  repeat: int = 1):
+    """One mt_layer_fwd + mt_layer_bwd; returns (out, dx, grads) as float64 arrays."""
+    torch, mt = torch_mod(), mt_mod()
+    sh = mt_shape(shape)
+    saved = torch.empty(mt.layer_saved_bytes(sh), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(mt.layer_workspace_bytes(sh), dtype=torch.uint8, device="cuda")
+    w = {k: to_dev(v, shape.dtype) for k, v in params.items()}
+    xd, dd = to_dev(x, shape.dtype), to_dev(dout, shape.dtype)
+    out, dx = torch.empty_like(xd), torch.empty_like(xd)
+    grads = {k: torch.empty(v.shape, dtype=torch.float32, device="cuda") for k, v in params.items()}
+    mt.check_layer_tensors(sh, w, grads, x=xd, out=out, dout=dd, dx=dx)
+    results = []
+    for _ in range(repeat):
+        mt.layer_fwd(sh, w, xd, out, saved, ws)
+        mt.layer_bwd(sh, w, xd, saved, dd, dx, grads, ws)
+        torch.cuda.synchronize()
+        results.append((to_np(out), to_np(dx), {k: to_np(g) for k, g in grads.items()}))
+    return results[0] if repeat == 1 else results
+
+
+def run_stage_gpu(shape: si.LayerShape, x: np.ndarray, dout: np.ndarray, layers: List[Dict[str, np.ndarray]]):
+    """Consecutive layers as one stage: forward l0..lL-1, then backward lL-1..l0."""
+    torch, mt = torch_mod(), mt_mod()
+    sh = mt_shape(shape)
+    L = len(layers)
+    saved = [torch.empty(mt.layer_saved_bytes(sh), dtype=torch.uint8, device="cuda") for _ in range(L)]
+    ws = torch.empty(mt.layer_workspace_bytes(sh), dtype=torch.uint8, device="cuda")
+    ws_ = [{k: to_dev(v, shape.dtype) for k, v in p.items()} for p in layers]
+    acts = [to_dev(x, shape.dtype)] + [torch.empty_like(to_dev(x, shape.dtype)) for _ in range(L)]
+    grads = [{k: torch.empty(v.shape, dtype=torch.float32, device="cuda") for k, v in p.items()} for p in layers]
+    for l in range(L):
+        mt.check_layer_tensors(sh, ws_[l], grads[l], x=acts[l], out=acts[l + 1])
+        mt.layer_fwd(sh, ws_[l], acts[l], acts[l + 1], saved[l], ws)
+    g = to_dev(dout, shape.dtype)
+    for l in reversed(range(L)):
+        dx = torch.empty_like(g)
+        mt.layer_bwd(sh, ws_[l], acts[l], saved[l], g, dx, grads[l], ws)
+        g = dx
+    torch.cuda.synchronize()
+    return to_np(acts[L]), to_np(g), [{k: to_np(v) for k, v in gr.items()} for gr in grads]
+
+
+def run_mlp_gpu(shape: si.LayerShape, x: np.ndarray, dy: np.ndarray, p: Dict[str, np.ndarray]):
+    """mt_mlp_fwd + mt_mlp_bwd of one shard; returns (y_partial, dx_partial, grads)."""
+    torch, mt = torch_mod(), mt_mod()
+    sh = mt_shape(shape)
+    dt = shape.dtype
+    xd, dyd = to_dev(x, dt), to_dev(dy, dt)
+    w1, b1, w2 = to_dev(p["w_fc1"], dt), to_dev(p["b_fc1"], dt), to_dev(p["w_fc2"], dt)
+    saved = torch.empty(mt.mlp_saved_bytes(sh), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(mt.mlp_workspace_bytes(sh), dtype=torch.uint8, device="cuda")
+    y, dx = torch.empty_like(xd), torch.empty_like(xd)
+    dw1 = torch.empty(p["w_fc1"].shape, dtype=torch.float32, device="cuda")
+    db1 = torch.empty(p["b_fc1"].shape, dtype=torch.float32, device="cuda")
+    dw2 = torch.empty(p["w_fc2"].shape, dtype=torch.float32, device="cuda")
+    ft = 4 * shape.h // shape.tp
+    assert w1.numel() == ft * shape.h and w2.numel() == ft * shape.h and b1.numel() == ft
+    assert xd.numel() == shape.tokens * shape.h and dyd.numel() == xd.numel()
+    mt.mlp_fwd(sh, xd, w1, b1, w2, y, saved, ws)
+    mt.mlp_bwd(sh, xd, w1, w2, saved, dyd, dx, dw1, db1, dw2, ws)
+    torch.cuda.synchronize()
+    return to_np(y), to_np(dx), dict(w_fc1=to_np(dw1), b_fc1=to_np(db1), w_fc2=to_np(dw2))
+
+
+def compare(name: str, gpu: np.ndarray, ref: np.ndarray, tol: float) -> Tuple[bool, float, float]:
+    err = float(np.max(np.abs(gpu - ref))) if ref.size else 0.0
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    ok = bool(np.all(np.isfinite(gpu))) and err <= tol * rms
+    log(f"  {name:10s} max|err| {err:.3e}  rms {rms:.3e}  ratio {err / max(rms, 1e-30):.2e}  {'ok' if ok else 'FAIL'}")
+    return ok, err, rms
+
+
+def check_all(gpu_out, gpu_dx, gpu_grads, ref_out, ref_dx, ref_grads, tol: float, keys=None) -> List[str]:
+    bad = []
+    if not compare("out", gpu_out, ref_out, tol)[0]:
+        bad.append("out")
+    if not compare("dx", gpu_dx, ref_dx, tol)[0]:
+        bad.append("dx")
+    for k in (keys or sorted(ref_grads)):
+        if not compare(k, gpu_grads[k], ref_grads[k], tol)[0]:
+            bad.append(k)
+    return bad
+
+
+def oracle_layer(shape: si.LayerShape, x, dout, params):
+    out, c = oracle.layer_fwd(x, [params], shape.micro_batch, shape.seq, shape.head_dim)
+    dx, g = oracle.layer_bwd(dout, c, [params])
+    return out, dx, g[0]

@@ -1,0 +1,136 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol include/mt.h
+declares, sizes its buffers consistently and rejects bad arguments with the documented
+status before launching anything (every call below fails validation on the host)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import tensor_layer_gemms_amd as mt
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mt.LIB_PATH):
+        from tensor_layer_gemms_amd.build import build
+        build(verbose=False)
+    return mt.lib()
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "mt.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mt_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared()
+    assert "mt_layer_fwd" in declared and "mt_mlp_bwd" in declared
+    out = subprocess.run(["nm", "-D", "--defined-only", mt.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (mt_\w+)", out))
+    missing = [s for s in declared if s not in exported]
+    assert not missing, missing
+    assert set(declared) == set(mt.EXPORTED), "binding signatures must cover the header"
+
+
+def _shape(**kw):
+    base = dict(h=1024, heads=16, seq=1024, micro_batch=4, tp=1, shard=0, dtype="bf16")
+    base.update(kw)
+    return mt.make_shape(**base)
+
+
+def test_buffer_queries_consistent(lib):
+    s = _shape()
+    M, h, f, a, seq = 4096, 1024, 4096, 16, 1024
+    saved = mt.layer_saved_bytes(s)
+    # at least U, QKV, P, ctx, X2, V2, A, Z in bf16 plus four fp32 row statistics
+    need = 2 * (M * h * 3 + M * 3 * h + 4 * a * seq * seq + M * h + 2 * M * f) + 16 * M
+    assert need <= saved <= need + 64 * 256
+    assert mt.layer_workspace_bytes(s) >= 4 * 4 * a * seq * seq  # fp32 scores
+    assert mt.mlp_saved_bytes(s) == 2 * 2 * M * f
+    s8 = _shape(h=12288, heads=96, seq=2048, micro_batch=1, tp=8)
+    s8b = _shape(h=12288, heads=96, seq=2048, micro_batch=1, tp=8, shard=7)
+    assert mt.layer_saved_bytes(s8) == mt.layer_saved_bytes(s8b) > 0
+    assert mt.layer_saved_bytes(_shape(dtype="fp32")) > saved
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(heads=12), mt.MT_ERR_INVALID_ARG),            # h % heads
+    (dict(tp=3), mt.MT_ERR_INVALID_ARG),                # heads % tp
+    (dict(tp=2, shard=2), mt.MT_ERR_INVALID_ARG),       # shard out of range
+    (dict(shard=-1), mt.MT_ERR_INVALID_ARG),
+    (dict(seq=1020), mt.MT_ERR_UNSUPPORTED),            # seq % 8
+    (dict(seq=8192), mt.MT_ERR_UNSUPPORTED),            # beyond the softmax row limit
+    (dict(h=1028, heads=257), mt.MT_ERR_UNSUPPORTED),   # head dim 4
+    (dict(h=65536, heads=512), mt.MT_ERR_UNSUPPORTED),  # LayerNorm row limit
+    (dict(micro_batch=0), mt.MT_ERR_INVALID_ARG),
+])
+def test_bad_shapes_rejected(lib, kw, status):
+    s = _shape(**kw)
+    assert mt.layer_saved_bytes(s) == 0 and mt.layer_workspace_bytes(s) == 0
+    w = mt.LayerWeights(*([0x1000] * 12))
+    rc = lib.mt_layer_fwd(ctypes.byref(s), ctypes.byref(w), 0x1000, 0x1000, 0x1000, 1 << 40, 0x1000, 1 << 40, None)
+    assert rc == status
+
+
+def test_null_and_misaligned_pointers_rejected(lib):
+    s = _shape()
+    good = [0x10000] * 12
+    for i in range(12):
+        bad = list(good)
+        bad[i] = 0
+        w = mt.LayerWeights(*bad)
+        assert lib.mt_layer_fwd(ctypes.byref(s), ctypes.byref(w), 0x1000, 0x1000, 0x1000, 1 << 40, 0x1000, 1 << 40,
+                                None) == mt.MT_ERR_INVALID_ARG
+    w = mt.LayerWeights(*good)
+    assert lib.mt_layer_fwd(ctypes.byref(s), ctypes.byref(w), 0x1008, 0x1000, 0x1000, 1 << 40, 0x1000, 1 << 40,
+                            None) == mt.MT_ERR_INVALID_ARG
+    assert lib.mt_layer_fwd(None, ctypes.byref(w), 0x1000, 0x1000, 0x1000, 1 << 40, 0x1000, 1 << 40,
+                            None) == mt.MT_ERR_INVALID_ARG
+    assert lib.mt_mlp_fwd(ctypes.byref(s), 0, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 1 << 40, None, 0,
+                          None) == mt.MT_ERR_INVALID_ARG
+    g = mt.LayerGrads(*([0x1000] * 11 + [0]))
+    assert lib.mt_layer_bwd(ctypes.byref(s), ctypes.byref(w), 0x1000, 0x1000, 1 << 40, 0x1000, 0x1000, ctypes.byref(g),
+                            0x1000, 1 << 40, None) == mt.MT_ERR_INVALID_ARG
+
+
+def test_small_buffers_rejected(lib):
+    s = _shape()
+    w = mt.LayerWeights(*([0x1000] * 12))
+    g = mt.LayerGrads(*([0x1000] * 12))
+    saved, ws = mt.layer_saved_bytes(s), mt.layer_workspace_bytes(s)
+    assert lib.mt_layer_fwd(ctypes.byref(s), ctypes.byref(w), 0x1000, 0x1000, 0x1000, saved - 1, 0x1000, ws,
+                            None) == mt.MT_ERR_WORKSPACE
+    assert lib.mt_layer_fwd(ctypes.byref(s), ctypes.byref(w), 0x1000, 0x1000, 0x1000, saved, 0x1000, ws - 1,
+                            None) == mt.MT_ERR_WORKSPACE
+    assert lib.mt_layer_bwd(ctypes.byref(s), ctypes.byref(w), 0x1000, 0x1000, saved - 256, 0x1000, 0x1000,
+                            ctypes.byref(g), 0x1000, ws, None) == mt.MT_ERR_WORKSPACE
+    ms = mt.mlp_saved_bytes(s)
+    assert lib.mt_mlp_fwd(ctypes.byref(s), 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, ms - 1, None, 0,
+                          None) == mt.MT_ERR_WORKSPACE
+    mw = mt.mlp_workspace_bytes(s)
+    assert lib.mt_mlp_bwd(ctypes.byref(s), 0x1000, 0x1000, 0x1000, 0x1000, ms, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000,
+                          0x1000, mw - 1, None) == mt.MT_ERR_WORKSPACE
+
+
+def test_status_strings_and_timing_api(lib):
+    for st in range(5):
+        assert len(mt.status_string(st)) >= 2
+    assert "unknown" in mt.status_string(99)
+    mt.timing_enable(True, "fc1")
+    mt.timing_enable(False)
+    mt.timing_reset()
+    assert mt.timing_records() == []
+    assert lib.mt_timing_get(0, None, 0, None, None, None) == mt.MT_ERR_INVALID_ARG
+
+
+def test_binding_rejects_mismatched_tensors():
+    torch = pytest.importorskip("torch")
+    s = _shape(h=64, heads=4, seq=32, micro_batch=2, dtype="fp32")
+    w = {k: torch.zeros(v) for k, v in mt.weight_shapes(s).items()}
+    with pytest.raises(ValueError):
+        mt.check_layer_tensors(s, w)  # host tensors are not device buffers

@@ -1,0 +1,132 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle, on seeded inputs.
+
+Every output of the layer is compared: Out, dX and all twelve parameter gradients,
+with max|gpu - oracle| <= tol * RMS(oracle), tol 2e-2 (bf16) / 1e-4 (fp32).
+Shapes go from the tiny fp32 layer through multi-tile shapes with ragged tails and
+odd head dims to the workloads' full sizes.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import seeded_inputs as si
+from gpu_support import (TOL, check_all, log, oracle_layer, run_layer_gpu, run_mlp_gpu, run_stage_gpu)
+
+pytestmark = pytest.mark.gpu
+
+
+def _layer_case(shape, seed=0, random_affine=False, global_weights=True):
+    return si.make_case(shape, seed=seed, global_weights=global_weights, random_affine=random_affine)
+
+
+def _check_layer(shape, case, params=None):
+    params = params if params is not None else case.layers[0]
+    log(f"layer {shape}")
+    g_out, g_dx, g_gr = run_layer_gpu(shape, case.x, case.dout, params)
+    r_out, r_dx, r_gr = oracle_layer(shape, case.x, case.dout, params)
+    bad = check_all(g_out, g_dx, g_gr, r_out, r_dx, r_gr, TOL[shape.dtype])
+    assert not bad, f"tensors over tolerance: {bad}"
+
+
+TINY = si.WORKLOADS["tiny_fp32"].shape
+
+
+@pytest.mark.parametrize("random_affine", [False, True])
+def test_tiny_fp32_layer(random_affine):
+    _check_layer(TINY, _layer_case(TINY, random_affine=random_affine))
+
+
+@pytest.mark.parametrize("shard", [0, 1])
+def test_tiny_fp32_tp2_shard(shard):
+    """One rank of a tp=2 split: the shard's weights, all-reduce as the identity."""
+    shape = TINY.replace(tp=2, shard=shard)
+    case = _layer_case(shape, random_affine=True)
+    _check_layer(shape, case)
+
+
+def test_tiny_bf16_layer():
+    shape = TINY.replace(dtype="bf16")
+    _check_layer(shape, _layer_case(shape, random_affine=True))
+
+
+@pytest.mark.parametrize("dtype,tp", [("fp32", 2), ("bf16", 2), ("bf16", 4)])
+def test_mlp_shards_sum_to_unsharded_block(dtype, tp):
+    """The pages' invariant on the GPU: run every shard of the MLP block sequentially on
+    one device and sum the partials; compare with the unsharded oracle block."""
+    shape = si.LayerShape(h=256, heads=4, seq=72, micro_batch=3, tp=tp, dtype=dtype)
+    case = si.mlp_case(shape.replace(tp=1), seed=5, random_bias=True)
+    g = case.global_layers[0]
+    y_sum = dx_sum = 0.0
+    grads = []
+    for i in range(tp):
+        p = si.shard_slice(g, shape, i)
+        y, dx, gr = run_mlp_gpu(shape.replace(shard=i), case.x, case.dout, p)
+        y_sum, dx_sum = y_sum + y, dx_sum + dx
+        grads.append(gr)
+    y_ref, c = oracle.mlp_fwd(case.x, [g])
+    dx_ref, g_ref = oracle.mlp_bwd(case.dout, c, [g])
+    tol = TOL[dtype]
+    from gpu_support import compare
+    assert compare("sum y", y_sum, y_ref, tol)[0]
+    assert compare("sum dx", dx_sum, dx_ref, tol)[0]
+    fs = 4 * shape.h // tp
+    for i, gr in enumerate(grads):
+        assert compare(f"dW1[{i}]", gr["w_fc1"], g_ref[0]["w_fc1"][i * fs:(i + 1) * fs], tol)[0]
+        assert compare(f"db1[{i}]", gr["b_fc1"], g_ref[0]["b_fc1"][i * fs:(i + 1) * fs], tol)[0]
+        assert compare(f"dW2[{i}]", gr["w_fc2"], g_ref[0]["w_fc2"][:, i * fs:(i + 1) * fs], tol)[0]
+
+
+@pytest.mark.parametrize("h,heads,seq,mb,tp,shard", [
+    (320, 5, 136, 3, 1, 0),    # several tiles, ragged token and feature tails
+    (640, 4, 264, 1, 2, 1),    # head dim 160, shard 1 of 2, ragged seq
+    (512, 8, 520, 2, 2, 0),    # seq spanning three causal chunks
+])
+def test_layer_bf16_multi_tile(h, heads, seq, mb, tp, shard):
+    shape = si.LayerShape(h=h, heads=heads, seq=seq, micro_batch=mb, tp=tp, shard=shard)
+    case = _layer_case(shape, seed=h + seq, random_affine=True)
+    _check_layer(shape, case)
+
+
+def test_layer_fp32_multi_tile():
+    shape = si.LayerShape(h=192, heads=3, seq=200, micro_batch=2, tp=1, dtype="fp32")
+    _check_layer(shape, _layer_case(shape, seed=3, random_affine=True))
+
+
+def test_gpt_h1024_full():
+    w = si.WORKLOADS["gpt_h1024"]
+    case = si.workload_case("gpt_h1024")
+    _check_layer(w.shape, case)
+
+
+@pytest.mark.timeout(900)
+def test_gpt175b_tp8_shard_full():
+    """The 175B-shaped shard at full size, every output against the full oracle."""
+    w = si.WORKLOADS["gpt175b_tp8"]
+    case = si.workload_case("gpt175b_tp8")
+    _check_layer(w.shape, case)
+
+
+def test_bitwise_deterministic():
+    """Two runs give identical bits: no float atomics, fixed reduction orders."""
+    shape = si.LayerShape(h=512, heads=8, seq=256, micro_batch=2, tp=2)
+    case = _layer_case(shape, seed=9, random_affine=True)
+    (o1, d1, g1), (o2, d2, g2) = run_layer_gpu(shape, case.x, case.dout, case.layers[0], repeat=2)
+    assert np.array_equal(o1, o2) and np.array_equal(d1, d2)
+    for k in g1:
+        assert np.array_equal(g1[k], g2[k]), k
+
+
+def test_stage_two_layers_small():
+    """Consecutive layers as one pipeline stage (forward l0, l1; backward l1, l0)."""
+    shape = si.LayerShape(h=256, heads=4, seq=128, micro_batch=2, tp=2)
+    case = si.make_case(shape, seed=12, layers=2, random_affine=True)
+    out, dx, grads = run_stage_gpu(shape, case.x, case.dout, case.layers)
+    layers = [[p] for p in case.layers]
+    r_out, caches = oracle.stage_fwd(case.x, layers, shape.micro_batch, shape.seq, shape.head_dim)
+    r_dx, r_grads = oracle.stage_bwd(case.dout, caches, layers)
+    bad = check_all(out, dx, grads[0], r_out, r_dx, r_grads[0][0], TOL["bf16"])
+    for k in r_grads[1][0]:
+        from gpu_support import compare
+        if not compare(f"l1.{k}", grads[1][k], r_grads[1][0][k], TOL["bf16"])[0]:
+            bad.append("l1." + k)
+    assert not bad, bad
