@@ -34,8 +34,10 @@
  *   - Every argument is validated before anything is launched; on error nothing is
  *     launched and the status says why (mt_status_string).
  *   - Shape limits: h % heads == 0, heads % tp == 0, 0 <= shard < tp, head dim
- *     d = h / heads a multiple of 8, seq a multiple of 8 and <= 4096, h <= 32768
- *     (bf16) or 16384 (fp32).
+ *     d = h / heads a multiple of 8, seq a multiple of 8 and <= 4096, h <= 32768.
+ *   - Precision of the bf16 path: the residual stream X2 = X + O + b_o and its
+ *     gradient dX2 are kept in fp32 inside the call; everything stored between kernels
+ *     as a GEMM operand (U, QKV, P, ctx, V2, A, Z, dA, dctx, dS, dQKV, partials) is bf16.
  */
 #ifndef MT_H_
 #define MT_H_

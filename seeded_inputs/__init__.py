@@ -202,11 +202,23 @@ def shard_slice(global_params: Dict[str, np.ndarray], shape: LayerShape, shard: 
     )
 
 
+# NumPy's SeedSequence zero-pads its entropy words, so keys that differ only by trailing
+# zeros (0 and [0, 0, 0, 0]) give the SAME stream. Every keyed stream therefore ends in
+# this fixed nonzero word.
+_KEY_TAIL = 0x6D74
+PURPOSE_X, PURPOSE_DOUT, PURPOSE_WEIGHT = 1, 2, 3
+
+
+def keyed_rng(seed: int, purpose: int, layer: int = 0, shard: int = 0, tensor: int = 0) -> np.random.Generator:
+    """Independent stream per (seed, purpose, layer, shard, tensor)."""
+    return np.random.default_rng([seed, purpose, layer, shard, tensor, _KEY_TAIL])
+
+
 def draw_shard_layer(shape: LayerShape, seed: int, layer: int, shard: int,
                      random_affine: bool = False) -> Dict[str, np.ndarray]:
-    """Shard-local weights drawn directly, one counter-keyed stream per tensor."""
+    """Shard-local weights drawn directly, one keyed stream per tensor."""
     h, t = shape.h, shape.tp
-    key = lambda tid: np.random.default_rng([seed, layer, shard, tid])  # noqa: E731
+    key = lambda tid: keyed_rng(seed, PURPOSE_WEIGHT, layer, shard, tid)  # noqa: E731
     p = dict(
         w_qkv=_normal(key(0), (3 * h // t, h), WEIGHT_STD),
         w_o=_normal(key(1), (h, h // t), WEIGHT_STD),
@@ -236,8 +248,8 @@ def make_case(shape: LayerShape, seed: int = 0, layers: int = 1, global_weights:
 
     Order for global-weight workloads: default_rng(seed) draws X, then per layer
     W_qkv, W_o, W1, W2 (global), then dOut; biases/affine from default_rng([seed, 7])
-    when random_affine. Shard-local workloads draw X then dOut from default_rng(seed)
-    and each weight tensor from default_rng([seed, layer, shard, tensor_id]).
+    when random_affine. Shard-local workloads draw X, dOut and each weight tensor from
+    its own keyed stream (keyed_rng).
     bf16 workloads round every tensor to bfloat16-representable float32 values, so the
     GPU (bf16) and the oracle (fp64) see the same numbers.
     """
@@ -251,8 +263,8 @@ def make_case(shape: LayerShape, seed: int = 0, layers: int = 1, global_weights:
         dout = _normal(rng, (M, h))
         shard_layers = [shard_slice(g, shape, shape.shard) for g in global_layers]
     else:
-        x = _normal(rng, (M, h))
-        dout = _normal(rng, (M, h))
+        x = _normal(keyed_rng(seed, PURPOSE_X), (M, h))
+        dout = _normal(keyed_rng(seed, PURPOSE_DOUT), (M, h))
         shard_layers = [draw_shard_layer(shape, seed, l, shape.shard, random_affine) for l in range(layers)]
     if shape.dtype == "bf16":
         x, dout = bf16_round(x), bf16_round(dout)

@@ -54,6 +54,27 @@ __device__ __forceinline__ void store16(T* p, const float* v) {
   *reinterpret_cast<u32x4*>(p) = raw;
 }
 
+// 8 consecutive elements of T <-> 8 floats (one 16-byte access for bf16, two for fp32).
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float* out) {
+  if constexpr (sizeof(T) == 2) {
+    load16(p, out);
+  } else {
+    load16(p, out);
+    load16(p + 4, out + 4);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store8(T* p, const float* v) {
+  if constexpr (sizeof(T) == 2) {
+    store16(p, v);
+  } else {
+    store16(p, v);
+    store16(p + 4, v + 4);
+  }
+}
+
 // Wavefront (64 lanes) reductions.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

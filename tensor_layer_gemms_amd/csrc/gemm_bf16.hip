@@ -12,6 +12,8 @@ struct TileCfg {
   int bm, bn;
   float eff;  // relative per-tile MFMA efficiency (bigger tiles reuse LDS operands more)
 };
+// 256x256: 8 waves (2 x 4), wave tile 128x64; 256x128: 4 waves (2 x 2), 128x64;
+// 128x128: 4 waves, 64x64.
 constexpr TileCfg kTiles[] = {{256, 256, 1.0f}, {256, 128, 0.9f}, {128, 128, 0.75f}};
 
 int pick_tile(const GemmArgs& g, int batch) {
@@ -30,19 +32,20 @@ int pick_tile(const GemmArgs& g, int batch) {
   return best;
 }
 
-template <bool AK, bool BK, int BM, int BN, int KIND>
+template <bool AK, bool BK, int BM, int BN, int WM, int WN, int KIND>
 hipError_t run(const GemmArgs& g, int batch, hipStream_t s) {
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_bf16_kernel<AK, BK, BM, BN, 2, 2, KIND>), dim3(tiles, batch), dim3(256), 0, s, g);
+  hipLaunchKernelGGL((gemm_bf16_kernel<AK, BK, BM, BN, WM, WN, KIND>), dim3(tiles, batch), dim3(64 * WM * WN), 0, s,
+                     g);
   return hipGetLastError();
 }
 
 template <bool AK, bool BK, int KIND>
 hipError_t run_tile(const GemmArgs& g, int batch, hipStream_t s) {
   switch (pick_tile(g, batch)) {
-    case 0: return run<AK, BK, 256, 256, KIND>(g, batch, s);
-    case 1: return run<AK, BK, 256, 128, KIND>(g, batch, s);
-    default: return run<AK, BK, 128, 128, KIND>(g, batch, s);
+    case 0: return run<AK, BK, 256, 256, 2, 4, KIND>(g, batch, s);
+    case 1: return run<AK, BK, 256, 128, 2, 2, KIND>(g, batch, s);
+    default: return run<AK, BK, 128, 128, 2, 2, KIND>(g, batch, s);
   }
 }
 

@@ -7,6 +7,7 @@
 namespace mt {
 
 // ---------------------------------------------------------------------------- epilogue
+// Per-element epilogue (fp32 SIMT path).
 template <typename T, int KIND>
 __device__ __forceinline__ void epi_store(const GemmArgs& g, int64_t coff, int64_t voff, int m, int n, float v) {
   const int64_t idx = coff + (int64_t)m * g.ldc + n;
@@ -28,6 +29,66 @@ __device__ __forceinline__ void epi_store(const GemmArgs& g, int64_t coff, int64
     const float d = static_cast<const float*>(g.vec)[voff + m];
     static_cast<T*>(g.C)[idx] = from_f32<T>(p * (g.alpha * v - d));
   }
+}
+
+// 4 consecutive bf16 <-> 4 floats (8-byte accesses).
+__device__ __forceinline__ void load4_bf16(const bf16* p, float* v) {
+  const u32x2 r = *reinterpret_cast<const u32x2*>(p);
+  v[0] = __uint_as_float(r[0] << 16);
+  v[1] = __uint_as_float(r[0] & 0xffff0000u);
+  v[2] = __uint_as_float(r[1] << 16);
+  v[3] = __uint_as_float(r[1] & 0xffff0000u);
+}
+__device__ __forceinline__ void store4_bf16(bf16* p, const float* v) {
+  u32x2 r;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const bf16 lo = (bf16)v[2 * e], hi = (bf16)v[2 * e + 1];
+    r[e] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+  }
+  *reinterpret_cast<u32x2*>(p) = r;
+}
+
+// Epilogue of the MFMA path for 4 consecutive columns n..n+3 of row m (bf16 operands;
+// the activation type is bf16). Inputs are loaded before anything is stored.
+template <int KIND>
+__device__ __forceinline__ void epi_store4(const GemmArgs& g, int64_t coff, int64_t voff, int m, int n,
+                                           const float* acc) {
+  const int64_t idx = coff + (int64_t)m * g.ldc + n;
+  float v[4];
+  if constexpr (KIND == EPI_STORE_F32) {
+    f32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = g.alpha * acc[e];
+    *reinterpret_cast<f32x4*>(static_cast<float*>(g.C) + idx) = w;
+    return;
+  } else if constexpr (KIND == EPI_STORE) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = g.alpha * acc[e];
+  } else if constexpr (KIND == EPI_BIAS || KIND == EPI_BIAS_GELU) {
+    float b[4];
+    load4_bf16(static_cast<const bf16*>(g.vec) + n, b);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = acc[e] + b[e];
+    if constexpr (KIND == EPI_BIAS_GELU) {
+      float z[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) z[e] = gelu_f(v[e]);
+      store4_bf16(static_cast<bf16*>(g.C2) + idx, z);
+    }
+  } else if constexpr (KIND == EPI_DGELU) {
+    float a[4];
+    load4_bf16(static_cast<const bf16*>(g.aux) + idx, a);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = acc[e] * gelu_grad_f(a[e]);
+  } else if constexpr (KIND == EPI_DSOFTMAX) {
+    float p[4];
+    load4_bf16(static_cast<const bf16*>(g.aux) + idx, p);
+    const float d = static_cast<const float*>(g.vec)[voff + m];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = p[e] * (g.alpha * acc[e] - d);
+  }
+  store4_bf16(static_cast<bf16*>(g.C) + idx, v);
 }
 
 __device__ __forceinline__ void causal_k_range(const GemmArgs& g, int m0, int bm, int& kbeg, int& kend) {
@@ -80,21 +141,23 @@ struct TileLoader {
     for (int i = 0; i < PER; ++i) {
       const int it = tid + i * NT;
       if (ITEMS % NT != 0 && it >= ITEMS) break;
+      // Out-of-range items load from the (always valid) tile origin and are zeroed
+      // with a select, so the loads need no branches.
       if constexpr (KCONTIG) {
         const int row = it >> 3, kc = it & 7;
         const int gr = row0 + row, gk = k0 + kc * 8;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (gr < rows_valid && gk < kend) v = *reinterpret_cast<const u32x4*>(base + (int64_t)gr * ld + gk);
-        r[i] = v;
+        const bool ok = gr < rows_valid && gk < kend;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(base + (ok ? (int64_t)gr * ld + gk : 0));
+        r[i] = ok ? v : u32x4{0u, 0u, 0u, 0u};
       } else {
         const int kb = it & 7, rb = it >> 3;
         const int gr = row0 + rb * 8;
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
           const int gk = k0 + kb * 8 + kk;
-          u32x4 v = {0u, 0u, 0u, 0u};
-          if (gr < rows_valid && gk < kend) v = *reinterpret_cast<const u32x4*>(base + (int64_t)gk * ld + gr);
-          r[i * 8 + kk] = v;
+          const bool ok = gr < rows_valid && gk < kend;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(base + (ok ? (int64_t)gk * ld + gr : 0));
+          r[i * 8 + kk] = ok ? v : u32x4{0u, 0u, 0u, 0u};
         }
       }
     }
@@ -185,7 +248,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
         for (int i = 0; i < TM; ++i)
 #pragma unroll
           for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
       }
       if (t + 1 < nk) {
         bf16* nxt = smem + (cur ^ 1) * (BM + BN) * BK;
@@ -196,21 +259,25 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
     }
   }
 
-  // 32x32 accumulator layout: lane l holds column (l & 31) and, in register r, row
-  // 8 * (r >> 2) + 4 * (l >> 5) + (r & 3).
+  // The MFMA computes the transposed block (B rows as its first operand), so in the
+  // 32x32 accumulator layout lane l holds row (l & 31) and, in registers 4g..4g+3, the
+  // four consecutive columns 8g + 4 (l >> 5) + 0..3. N is a multiple of 8, so a group
+  // is either wholly inside or wholly outside the matrix.
   const int64_t coff = zo * g.c_so + zi * g.c_si;
   const int64_t voff = (int64_t)z * g.vec_bs;
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < TM; ++i) {
+    const int m = m0 + wm0 + i * 32 + (lane & 31);
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int n = n0 + wn0 + j * 32 + (lane & 31);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        if (m < g.M && n < g.N) epi_store<bf16, KIND>(g, coff, voff, m, n, acc[i][j][r]);
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn0 + j * 32 + q * 8 + (lane >> 5) * 4;
+        float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        if (m < g.M && n < g.N) epi_store4<KIND>(g, coff, voff, m, n, v);
       }
     }
+  }
 }
 
 // ---------------------------------------------------------------------------- fp32 SIMT

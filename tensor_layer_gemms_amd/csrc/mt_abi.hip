@@ -36,8 +36,7 @@ int validate_shape(const mt_shape* s, Dims* out) {
   const int64_t d = s->h / s->heads;
   if (d % 8 != 0 || s->seq % 8 != 0) return MT_ERR_UNSUPPORTED;
   if (s->seq > kSoftmaxMaxSeq) return MT_ERR_UNSUPPORTED;
-  const int64_t hmax = (s->dtype == MT_BF16 ? 8 : 4) * (int64_t)kLnThreads * kLnChunksPerThread;
-  if (s->h > hmax) return MT_ERR_UNSUPPORTED;
+  if (s->h > kLnMaxH) return MT_ERR_UNSUPPORTED;
   const int64_t M = (int64_t)s->micro_batch * s->seq;
   if (M > (1 << 24)) return MT_ERR_UNSUPPORTED;
   Dims x;
@@ -77,7 +76,8 @@ struct Carver {
 
 struct LayerSaved {
   float *mean1, *rstd1, *mean2, *rstd2;
-  void *u, *qkv, *p, *ctx, *x2, *v2, *a, *z;
+  float* x2;  // residual stream X + O + b_o, fp32
+  void *u, *qkv, *p, *ctx, *v2, *a, *z;
 };
 
 size_t carve_layer_saved(const Dims& d, void* base, LayerSaved* s) {
@@ -90,7 +90,7 @@ size_t carve_layer_saved(const Dims& d, void* base, LayerSaved* s) {
   s->qkv = c.take(d.M * d.qkv * d.es);
   s->p = c.take(d.B * d.at * d.seq * d.seq * d.es);
   s->ctx = c.take(d.M * d.hs * d.es);
-  s->x2 = c.take(d.M * d.h * d.es);
+  s->x2 = c.take<float>(d.M * d.h * 4);
   s->v2 = c.take(d.M * d.h * d.es);
   s->a = c.take(d.M * d.ft * d.es);
   s->z = c.take(d.M * d.ft * d.es);
@@ -111,7 +111,7 @@ size_t carve_layer_fwd_ws(const Dims& d, void* base, LayerFwdWs* w) {
 
 struct LayerBwdWs {
   void *da, *dv2, *dx2, *dctx, *ds, *dqkv;
-  float *D, *part;
+  float *dx2f, *D, *part;  // dx2f: fp32 copy of dX2 for the residual path
 };
 
 size_t colsum_floats(const Dims& d) {
@@ -126,6 +126,7 @@ size_t carve_layer_bwd_ws(const Dims& d, void* base, LayerBwdWs* w) {
   w->da = c.take(d.M * d.ft * d.es);
   w->dv2 = c.take(d.M * d.h * d.es);  // dV2 partial, later dU partial
   w->dx2 = c.take(d.M * d.h * d.es);
+  w->dx2f = c.take<float>(d.M * d.h * 4);
   w->dctx = c.take(d.M * d.hs * d.es);
   w->ds = c.take(d.B * d.at * d.seq * d.seq * d.es);
   w->dqkv = c.take(d.M * d.qkv * d.es);
@@ -261,8 +262,7 @@ int layer_fwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, void
 
   // F1 LayerNorm 1
   q.run("ln1_fwd", 0, 2 * Mh * es, [&] {
-    return launch_ln_fwd(bf, false, x, nullptr, nullptr, w.ln1_g, w.ln1_b, nullptr, sv.u, sv.mean1, sv.rstd1,
-                         (int)d.M, (int)d.h, kLnEps, stream);
+    return launch_ln_fwd(bf, x, w.ln1_g, w.ln1_b, sv.u, sv.mean1, sv.rstd1, (int)d.M, (int)d.h, kLnEps, stream);
   });
   // F2 column-parallel QKV projection + bias
   q.run("qkv_fwd", gflop(d.M, d.qkv, d.h), 0, [&] {
@@ -304,10 +304,10 @@ int layer_fwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, void
     GemmArgs g = plain(sv.ctx, d.hs, w.w_o, d.hs, ws.o, d.h, d.M, d.h, d.hs);
     return gemm(d, g, true, true, EPI_STORE, 1, stream);
   });
-  // F7 X2 = X + AR(O_i) + b_o (AR = identity on one GPU), V2 = LN2(X2)
-  q.run("add_ln2_fwd", 0, 4 * Mh * es, [&] {
-    return launch_ln_fwd(bf, true, x, ws.o, w.b_o, w.ln2_g, w.ln2_b, sv.x2, sv.v2, sv.mean2, sv.rstd2, (int)d.M,
-                         (int)d.h, kLnEps, stream);
+  // F7 X2 = X + AR(O_i) + b_o (AR = identity on one GPU; X2 kept in fp32), V2 = LN2(X2)
+  q.run("add_ln2_fwd", 0, Mh * (3 * es + 4), [&] {
+    return launch_add_ln_fwd(bf, x, ws.o, w.b_o, w.ln2_g, w.ln2_b, sv.x2, sv.v2, sv.mean2, sv.rstd2, (int)d.M,
+                             (int)d.h, kLnEps, stream);
   });
   // F8 column-parallel FC1 with fused bias + GeLU (keeps A and Z)
   q.run("fc1_fwd", gflop(d.M, d.ft, d.h), 0, [&] {
@@ -322,7 +322,7 @@ int layer_fwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, void
     return gemm(d, g, true, true, EPI_STORE, 1, stream);
   });
   // F10 Out = X2 + AR(Y_i) + b_fc2
-  q.run("bias_residual_fwd", 0, 3 * Mh * es, [&] {
+  q.run("bias_residual_fwd", 0, Mh * (2 * es + 4), [&] {
     return launch_add_bias_residual(bf, sv.x2, ws.o, w.b_fc2, out, (int)d.M, (int)d.h, stream);
   });
   return q.status();
@@ -342,7 +342,8 @@ int layer_bwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, cons
 
   // B1 FC2: db_fc2, dW2 = dOut^T Z, dA = (dOut W2) * GeLU'(A)
   q.run("db_fc2", 0, Mh * es, [&] {
-    return launch_colsum(bf, 0, dout, nullptr, nullptr, nullptr, gr.b_fc2, nullptr, ws.part, M, (int)d.h, stream);
+    return launch_colsum(bf, 0, dout, false, nullptr, false, nullptr, nullptr, gr.b_fc2, nullptr, ws.part, M,
+                         (int)d.h, stream);
   });
   q.run("fc2_wgrad", gflop(d.h, d.ft, d.M), 0, [&] {
     GemmArgs g = plain(dout, d.h, sv.z, d.ft, gr.w_fc2, d.ft, d.h, d.ft, d.M);
@@ -355,7 +356,8 @@ int layer_bwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, cons
   });
   // B2 FC1: db_fc1, dW1 = dA^T V2, dV2 = dA W1 (partial)
   q.run("db_fc1", 0, d.M * d.ft * es, [&] {
-    return launch_colsum(bf, 0, ws.da, nullptr, nullptr, nullptr, gr.b_fc1, nullptr, ws.part, M, (int)d.ft, stream);
+    return launch_colsum(bf, 0, ws.da, false, nullptr, false, nullptr, nullptr, gr.b_fc1, nullptr, ws.part, M,
+                         (int)d.ft, stream);
   });
   q.run("fc1_wgrad", gflop(d.ft, d.h, d.M), 0, [&] {
     GemmArgs g = plain(ws.da, d.ft, sv.v2, d.h, gr.w_fc1, d.h, d.ft, d.h, d.M);
@@ -365,15 +367,19 @@ int layer_bwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, cons
     GemmArgs g = plain(ws.da, d.ft, w.w_fc1, d.h, ws.dv2, d.h, d.M, d.h, d.ft);
     return gemm(d, g, true, false, EPI_STORE, 1, stream);
   });
-  // B3 dX2 = dOut + LN2-backward(AR(dV2)); dgamma2, dbeta2; db_o = colsum(dX2)
-  q.run("ln2_bwd", 0, 4 * Mh * es, [&] {
-    return launch_ln_bwd(bf, ws.dv2, sv.x2, w.ln2_g, sv.mean2, sv.rstd2, dout, ws.dx2, M, (int)d.h, stream);
+  // B3 dX2 = dOut + LN2-backward(AR(dV2)) (written as the GEMM operand and as an fp32
+  // copy for the residual path); dgamma2, dbeta2; db_o = colsum(dX2)
+  q.run("ln2_bwd", 0, Mh * (3 * es + 8), [&] {
+    return launch_ln_bwd(bf, ws.dv2, sv.x2, true, w.ln2_g, sv.mean2, sv.rstd2, dout, false, ws.dx2, ws.dx2f, M,
+                         (int)d.h, stream);
   });
-  q.run("ln2_param_grads", 0, 2 * Mh * es, [&] {
-    return launch_colsum(bf, 1, ws.dv2, sv.x2, sv.mean2, sv.rstd2, gr.ln2_g, gr.ln2_b, ws.part, M, (int)d.h, stream);
+  q.run("ln2_param_grads", 0, Mh * (es + 4), [&] {
+    return launch_colsum(bf, 1, ws.dv2, false, sv.x2, true, sv.mean2, sv.rstd2, gr.ln2_g, gr.ln2_b, ws.part, M,
+                         (int)d.h, stream);
   });
-  q.run("db_o", 0, Mh * es, [&] {
-    return launch_colsum(bf, 0, ws.dx2, nullptr, nullptr, nullptr, gr.b_o, nullptr, ws.part, M, (int)d.h, stream);
+  q.run("db_o", 0, Mh * 4, [&] {
+    return launch_colsum(bf, 0, ws.dx2f, true, nullptr, false, nullptr, nullptr, gr.b_o, nullptr, ws.part, M,
+                         (int)d.h, stream);
   });
   // B4 out-projection: dW_o = dX2^T ctx, dctx = dX2 W_o
   q.run("out_proj_wgrad", gflop(d.h, d.hs, d.M), 0, [&] {
@@ -437,8 +443,8 @@ int layer_bwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, cons
   });
   // B7 QKV: db_qkv, dW_qkv = dQKV^T U, dU = dQKV W_qkv (partial)
   q.run("db_qkv", 0, d.M * d.qkv * es, [&] {
-    return launch_colsum(bf, 0, ws.dqkv, nullptr, nullptr, nullptr, gr.b_qkv, nullptr, ws.part, M, (int)d.qkv,
-                         stream);
+    return launch_colsum(bf, 0, ws.dqkv, false, nullptr, false, nullptr, nullptr, gr.b_qkv, nullptr, ws.part, M,
+                         (int)d.qkv, stream);
   });
   q.run("qkv_wgrad", gflop(d.qkv, d.h, d.M), 0, [&] {
     GemmArgs g = plain(ws.dqkv, d.qkv, sv.u, d.h, gr.w_qkv, d.h, d.qkv, d.h, d.M);
@@ -449,11 +455,13 @@ int layer_bwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, cons
     return gemm(d, g, true, false, EPI_STORE, 1, stream);
   });
   // B8 dX = dX2 + LN1-backward(AR(dU)); dgamma1, dbeta1
-  q.run("ln1_bwd", 0, 4 * Mh * es, [&] {
-    return launch_ln_bwd(bf, ws.dv2, x, w.ln1_g, sv.mean1, sv.rstd1, ws.dx2, dx, M, (int)d.h, stream);
+  q.run("ln1_bwd", 0, Mh * (3 * es + 4), [&] {
+    return launch_ln_bwd(bf, ws.dv2, x, false, w.ln1_g, sv.mean1, sv.rstd1, ws.dx2f, true, dx, nullptr, M, (int)d.h,
+                         stream);
   });
   q.run("ln1_param_grads", 0, 2 * Mh * es, [&] {
-    return launch_colsum(bf, 1, ws.dv2, x, sv.mean1, sv.rstd1, gr.ln1_g, gr.ln1_b, ws.part, M, (int)d.h, stream);
+    return launch_colsum(bf, 1, ws.dv2, false, x, false, sv.mean1, sv.rstd1, gr.ln1_g, gr.ln1_b, ws.part, M,
+                         (int)d.h, stream);
   });
   return q.status();
 }
@@ -488,8 +496,8 @@ int mlp_bwd_impl(const Dims& d, const void* x, const void* w1, const void* w2, c
     return gemm(d, g, true, false, EPI_DGELU, 1, stream);
   });
   q.run("db_fc1", 0, (double)d.M * d.ft * d.es, [&] {
-    return launch_colsum(d.bf16, 0, ws.da, nullptr, nullptr, nullptr, db1, nullptr, ws.part, (int)d.M, (int)d.ft,
-                         stream);
+    return launch_colsum(d.bf16, 0, ws.da, false, nullptr, false, nullptr, nullptr, db1, nullptr, ws.part, (int)d.M,
+                         (int)d.ft, stream);
   });
   q.run("fc1_wgrad", gflop(d.ft, d.h, d.M), 0, [&] {
     GemmArgs g = plain(ws.da, d.ft, x, d.h, dw1, d.h, d.ft, d.h, d.M);

@@ -9,41 +9,40 @@ namespace mt {
 
 namespace {
 
-template <typename T>
-using V = Vec16<T>;
-
 // ------------------------------------------------------------------ LayerNorm forward
 // LayerNorm is one of the fused element-wise operations ("In-Depth Analysis of
 // Distributed Training Frameworks ... Megatron-LM", oreateai.com, section 2.2). One
-// block per row; the row stays in registers between the mean, variance and output passes.
+// block per row, 8-element chunks; the row stays in registers between the mean,
+// variance and output passes. With ADD the residual sum x + o + bias is formed in fp32,
+// written to the fp32 residual stream x2, and normalised without rounding.
 template <typename T, bool ADD, int CPT>
 __global__ __launch_bounds__(kLnThreads) void ln_fwd_kernel(const T* __restrict__ x, const T* __restrict__ o,
                                                             const T* __restrict__ bias, const T* __restrict__ gamma,
-                                                            const T* __restrict__ beta, T* __restrict__ x2,
+                                                            const T* __restrict__ beta, float* __restrict__ x2,
                                                             T* __restrict__ y, float* __restrict__ mean,
                                                             float* __restrict__ rstd, int h, float eps) {
-  constexpr int VE = V<T>::N, NW = kLnThreads / 64;
+  constexpr int NW = kLnThreads / 64;
   __shared__ float red[NW];
   const int64_t row = blockIdx.x;
-  const int nch = h / VE;
-  float v[CPT][VE];
+  const int nch = h / 8;
+  float v[CPT][8];
   float s = 0.f;
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     const int ch = threadIdx.x + c * kLnThreads;
     if (ch < nch) {
-      const int64_t off = row * h + (int64_t)ch * VE;
-      load16(x + off, v[c]);
+      const int64_t off = row * h + (int64_t)ch * 8;
+      load8(x + off, v[c]);
       if constexpr (ADD) {
-        float ov[VE], bv[VE];
-        load16(o + off, ov);
-        load16(bias + ch * VE, bv);
+        float ov[8], bv[8];
+        load8(o + off, ov);
+        load8(bias + ch * 8, bv);
 #pragma unroll
-        for (int e = 0; e < VE; ++e) v[c][e] = to_f32(from_f32<T>(v[c][e] + ov[e] + bv[e]));
-        store16(x2 + off, v[c]);  // the stored (rounded) residual is what LN and backward see
+        for (int e = 0; e < 8; ++e) v[c][e] += ov[e] + bv[e];
+        store8(x2 + off, v[c]);
       }
 #pragma unroll
-      for (int e = 0; e < VE; ++e) s += v[c][e];
+      for (int e = 0; e < 8; ++e) s += v[c][e];
     }
   }
   block_sum<1, NW>(&s, red);
@@ -54,7 +53,7 @@ __global__ __launch_bounds__(kLnThreads) void ln_fwd_kernel(const T* __restrict_
     const int ch = threadIdx.x + c * kLnThreads;
     if (ch < nch) {
 #pragma unroll
-      for (int e = 0; e < VE; ++e) {
+      for (int e = 0; e < 8; ++e) {
         const float dlt = v[c][e] - mu;
         q += dlt * dlt;
       }
@@ -70,42 +69,43 @@ __global__ __launch_bounds__(kLnThreads) void ln_fwd_kernel(const T* __restrict_
   for (int c = 0; c < CPT; ++c) {
     const int ch = threadIdx.x + c * kLnThreads;
     if (ch < nch) {
-      float gv[VE], bv[VE], out[VE];
-      load16(gamma + ch * VE, gv);
-      load16(beta + ch * VE, bv);
+      float gv[8], bv[8], out[8];
+      load8(gamma + ch * 8, gv);
+      load8(beta + ch * 8, bv);
 #pragma unroll
-      for (int e = 0; e < VE; ++e) out[e] = (v[c][e] - mu) * rs * gv[e] + bv[e];
-      store16(y + row * h + (int64_t)ch * VE, out);
+      for (int e = 0; e < 8; ++e) out[e] = (v[c][e] - mu) * rs * gv[e] + bv[e];
+      store8(y + row * h + (int64_t)ch * 8, out);
     }
   }
 }
 
 // ------------------------------------------------------------------ LayerNorm backward
 // dx = resid + rstd * (g - mean(g) - xhat * mean(g * xhat)), g = dy * gamma.
-template <typename T, int CPT>
-__global__ __launch_bounds__(kLnThreads) void ln_bwd_kernel(const T* __restrict__ dy, const T* __restrict__ x,
+template <typename T, typename TX, typename TR, int CPT>
+__global__ __launch_bounds__(kLnThreads) void ln_bwd_kernel(const T* __restrict__ dy, const TX* __restrict__ x,
                                                             const T* __restrict__ gamma,
                                                             const float* __restrict__ mean,
                                                             const float* __restrict__ rstd,
-                                                            const T* __restrict__ resid, T* __restrict__ dx, int h) {
-  constexpr int VE = V<T>::N, NW = kLnThreads / 64;
+                                                            const TR* __restrict__ resid, T* __restrict__ dx,
+                                                            float* __restrict__ dxf, int h) {
+  constexpr int NW = kLnThreads / 64;
   __shared__ float red[2 * NW];
   const int64_t row = blockIdx.x;
-  const int nch = h / VE;
+  const int nch = h / 8;
   const float mu = mean[row], rs = rstd[row];
-  float g[CPT][VE], xh[CPT][VE];
+  float g[CPT][8], xh[CPT][8];
   float s[2] = {0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     const int ch = threadIdx.x + c * kLnThreads;
     if (ch < nch) {
-      const int64_t off = row * h + (int64_t)ch * VE;
-      float gv[VE];
-      load16(dy + off, g[c]);
-      load16(x + off, xh[c]);
-      load16(gamma + ch * VE, gv);
+      const int64_t off = row * h + (int64_t)ch * 8;
+      float gv[8];
+      load8(dy + off, g[c]);
+      load8(x + off, xh[c]);
+      load8(gamma + ch * 8, gv);
 #pragma unroll
-      for (int e = 0; e < VE; ++e) {
+      for (int e = 0; e < 8; ++e) {
         g[c][e] *= gv[e];
         xh[c][e] = (xh[c][e] - mu) * rs;
         s[0] += g[c][e];
@@ -119,68 +119,68 @@ __global__ __launch_bounds__(kLnThreads) void ln_bwd_kernel(const T* __restrict_
   for (int c = 0; c < CPT; ++c) {
     const int ch = threadIdx.x + c * kLnThreads;
     if (ch < nch) {
-      const int64_t off = row * h + (int64_t)ch * VE;
-      float rv[VE], out[VE];
-      load16(resid + off, rv);
+      const int64_t off = row * h + (int64_t)ch * 8;
+      float rv[8], out[8];
+      load8(resid + off, rv);
 #pragma unroll
-      for (int e = 0; e < VE; ++e) out[e] = rv[e] + rs * (g[c][e] - mg - xh[c][e] * mgx);
-      store16(dx + off, out);
+      for (int e = 0; e < 8; ++e) out[e] = rv[e] + rs * (g[c][e] - mg - xh[c][e] * mgx);
+      store8(dx + off, out);
+      if (dxf) store8(dxf + off, out);
     }
   }
 }
 
 // ------------------------------------------------------------------ column sums
-// Stage 1: block (64 column chunks x 4 row lanes) sums a slab of rows per column.
-template <typename T, int MODE>
-__global__ __launch_bounds__(256) void colsum_partial_kernel(const T* __restrict__ a, const T* __restrict__ x,
+// Stage 1: block (64 column chunks of 8 x 4 row lanes) sums a slab of rows per column.
+template <typename TA, typename TX, int MODE>
+__global__ __launch_bounds__(256) void colsum_partial_kernel(const TA* __restrict__ a, const TX* __restrict__ x,
                                                              const float* __restrict__ mean,
                                                              const float* __restrict__ rstd,
                                                              float* __restrict__ part, int rows, int cols,
                                                              int rows_per_block, int nrb) {
-  constexpr int VE = V<T>::N;
   constexpr int NS = MODE == 1 ? 2 : 1;
-  __shared__ float red[NS][4][64][VE];
+  __shared__ float red[NS][4][64][8];
   const int lane = threadIdx.x & 63, rl = threadIdx.x >> 6;
   const int chunk = blockIdx.x * 64 + lane;
-  const int nch = cols / VE;
+  const int nch = cols / 8;
   const int r0 = blockIdx.y * rows_per_block, r1 = min(rows, r0 + rows_per_block);
-  float acc[NS][VE];
+  float acc[NS][8];
 #pragma unroll
   for (int k = 0; k < NS; ++k)
 #pragma unroll
-    for (int e = 0; e < VE; ++e) acc[k][e] = 0.f;
+    for (int e = 0; e < 8; ++e) acc[k][e] = 0.f;
   if (chunk < nch) {
     for (int r = r0 + rl; r < r1; r += 4) {
-      const int64_t off = (int64_t)r * cols + (int64_t)chunk * VE;
-      float av[VE];
-      load16(a + off, av);
+      const int64_t off = (int64_t)r * cols + (int64_t)chunk * 8;
+      float av[8];
+      load8(a + off, av);
       if constexpr (MODE == 1) {
-        float xv[VE];
-        load16(x + off, xv);
+        float xv[8];
+        load8(x + off, xv);
         const float mu = mean[r], rs = rstd[r];
 #pragma unroll
-        for (int e = 0; e < VE; ++e) {
+        for (int e = 0; e < 8; ++e) {
           acc[0][e] += av[e] * ((xv[e] - mu) * rs);
           acc[1][e] += av[e];
         }
       } else {
 #pragma unroll
-        for (int e = 0; e < VE; ++e) acc[0][e] += av[e];
+        for (int e = 0; e < 8; ++e) acc[0][e] += av[e];
       }
     }
   }
 #pragma unroll
   for (int k = 0; k < NS; ++k)
 #pragma unroll
-    for (int e = 0; e < VE; ++e) red[k][rl][lane][e] = acc[k][e];
+    for (int e = 0; e < 8; ++e) red[k][rl][lane][e] = acc[k][e];
   __syncthreads();
   if (rl == 0 && chunk < nch) {
 #pragma unroll
     for (int k = 0; k < NS; ++k)
 #pragma unroll
-      for (int e = 0; e < VE; ++e) {
+      for (int e = 0; e < 8; ++e) {
         const float t = red[k][0][lane][e] + red[k][1][lane][e] + red[k][2][lane][e] + red[k][3][lane][e];
-        part[((int64_t)k * nrb + blockIdx.y) * cols + (int64_t)chunk * VE + e] = t;
+        part[((int64_t)k * nrb + blockIdx.y) * cols + (int64_t)chunk * 8 + e] = t;
       }
   }
 }
@@ -202,19 +202,18 @@ __global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restri
 
 // ------------------------------------------------------------------ bias + residual
 template <typename T>
-__global__ __launch_bounds__(256) void add_bias_residual_kernel(const T* __restrict__ x2, const T* __restrict__ y,
+__global__ __launch_bounds__(256) void add_bias_residual_kernel(const float* __restrict__ x2, const T* __restrict__ y,
                                                                 const T* __restrict__ bias, T* __restrict__ out,
                                                                 int64_t nchunks, int hch) {
-  constexpr int VE = V<T>::N;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= nchunks) return;
-  float a[VE], b[VE], c[VE];
-  load16(x2 + i * VE, a);
-  load16(y + i * VE, b);
-  load16(bias + (i % hch) * VE, c);
+  float a[8], b[8], c[8];
+  load8(x2 + i * 8, a);
+  load8(y + i * 8, b);
+  load8(bias + (i % hch) * 8, c);
 #pragma unroll
-  for (int e = 0; e < VE; ++e) a[e] += b[e] + c[e];
-  store16(out + i * VE, a);
+  for (int e = 0; e < 8; ++e) a[e] += b[e] + c[e];
+  store8(out + i * 8, a);
 }
 
 // ------------------------------------------------------------------ causal softmax
@@ -284,32 +283,31 @@ template <typename T>
 __global__ __launch_bounds__(256) void attn_rowdot_kernel(const T* __restrict__ dctx, const T* __restrict__ ctx,
                                                           float* __restrict__ D, int64_t nrows, int seq, int heads,
                                                           int d) {
-  constexpr int VE = V<T>::N;
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= nrows * heads) return;
   const int64_t r = t / heads;
   const int k = (int)(t % heads);
   const int64_t base = r * (int64_t)heads * d + (int64_t)k * d;
   float s = 0.f;
-  for (int c = 0; c < d; c += VE) {
-    float a[VE], b[VE];
-    load16(dctx + base + c, a);
-    load16(ctx + base + c, b);
+  for (int c = 0; c < d; c += 8) {
+    float a[8], b[8];
+    load8(dctx + base + c, a);
+    load8(ctx + base + c, b);
 #pragma unroll
-    for (int e = 0; e < VE; ++e) s += a[e] * b[e];
+    for (int e = 0; e < 8; ++e) s += a[e] * b[e];
   }
   const int64_t b = r / seq, q = r % seq;
   D[(b * heads + k) * seq + q] = s;
 }
 
-int ln_cpt(int h, int ve) {
-  const int nch = h / ve;
+int ln_cpt(int h) {
+  const int nch = h / 8;
   const int need = (nch + kLnThreads - 1) / kLnThreads;
   return need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
 }
 
-void colsum_geometry(int rows, int cols, int ve, int& xblocks, int& rpb, int& nrb) {
-  const int nch = cols / ve;
+void colsum_geometry(int rows, int cols, int& xblocks, int& rpb, int& nrb) {
+  const int nch = cols / 8;
   xblocks = (nch + 63) / 64;
   int want = (2048 + xblocks - 1) / xblocks;
   const int cap = (rows + 15) / 16;
@@ -319,45 +317,65 @@ void colsum_geometry(int rows, int cols, int ve, int& xblocks, int& rpb, int& nr
   nrb = (rows + rpb - 1) / rpb;
 }
 
+template <typename T, bool ADD, int CPT>
+void ln_fwd_launch(const void* x, const void* o, const void* bias, const void* gamma, const void* beta, float* x2,
+                   void* y, float* mean, float* rstd, int rows, int h, float eps, hipStream_t s) {
+  hipLaunchKernelGGL((ln_fwd_kernel<T, ADD, CPT>), dim3(rows), dim3(kLnThreads), 0, s, (const T*)x, (const T*)o,
+                     (const T*)bias, (const T*)gamma, (const T*)beta, x2, (T*)y, mean, rstd, h, eps);
+}
+
 template <typename T, bool ADD>
-hipError_t ln_fwd_t(const void* x, const void* o, const void* bias, const void* gamma, const void* beta, void* x2,
+hipError_t ln_fwd_t(const void* x, const void* o, const void* bias, const void* gamma, const void* beta, float* x2,
                     void* y, float* mean, float* rstd, int rows, int h, float eps, hipStream_t s) {
-  const T *px = (const T*)x, *po = (const T*)o, *pb = (const T*)bias, *pg = (const T*)gamma, *pbe = (const T*)beta;
-  T *px2 = (T*)x2, *py = (T*)y;
-  switch (ln_cpt(h, V<T>::N)) {
-    case 1: hipLaunchKernelGGL((ln_fwd_kernel<T, ADD, 1>), dim3(rows), dim3(kLnThreads), 0, s, px, po, pb, pg, pbe, px2, py, mean, rstd, h, eps); break;
-    case 2: hipLaunchKernelGGL((ln_fwd_kernel<T, ADD, 2>), dim3(rows), dim3(kLnThreads), 0, s, px, po, pb, pg, pbe, px2, py, mean, rstd, h, eps); break;
-    case 4: hipLaunchKernelGGL((ln_fwd_kernel<T, ADD, 4>), dim3(rows), dim3(kLnThreads), 0, s, px, po, pb, pg, pbe, px2, py, mean, rstd, h, eps); break;
-    default: hipLaunchKernelGGL((ln_fwd_kernel<T, ADD, 8>), dim3(rows), dim3(kLnThreads), 0, s, px, po, pb, pg, pbe, px2, py, mean, rstd, h, eps); break;
+  switch (ln_cpt(h)) {
+    case 1: ln_fwd_launch<T, ADD, 1>(x, o, bias, gamma, beta, x2, y, mean, rstd, rows, h, eps, s); break;
+    case 2: ln_fwd_launch<T, ADD, 2>(x, o, bias, gamma, beta, x2, y, mean, rstd, rows, h, eps, s); break;
+    case 4: ln_fwd_launch<T, ADD, 4>(x, o, bias, gamma, beta, x2, y, mean, rstd, rows, h, eps, s); break;
+    default: ln_fwd_launch<T, ADD, 8>(x, o, bias, gamma, beta, x2, y, mean, rstd, rows, h, eps, s); break;
   }
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, typename TX, typename TR, int CPT>
+void ln_bwd_launch(const void* dy, const void* x, const void* gamma, const float* mean, const float* rstd,
+                   const void* resid, void* dx, float* dxf, int rows, int h, hipStream_t s) {
+  hipLaunchKernelGGL((ln_bwd_kernel<T, TX, TR, CPT>), dim3(rows), dim3(kLnThreads), 0, s, (const T*)dy,
+                     (const TX*)x, (const T*)gamma, mean, rstd, (const TR*)resid, (T*)dx, dxf, h);
+}
+
+template <typename T, typename TX, typename TR>
 hipError_t ln_bwd_t(const void* dy, const void* x, const void* gamma, const float* mean, const float* rstd,
-                    const void* resid, void* dx, int rows, int h, hipStream_t s) {
-  const T *pdy = (const T*)dy, *px = (const T*)x, *pg = (const T*)gamma, *pr = (const T*)resid;
-  T* pdx = (T*)dx;
-  switch (ln_cpt(h, V<T>::N)) {
-    case 1: hipLaunchKernelGGL((ln_bwd_kernel<T, 1>), dim3(rows), dim3(kLnThreads), 0, s, pdy, px, pg, mean, rstd, pr, pdx, h); break;
-    case 2: hipLaunchKernelGGL((ln_bwd_kernel<T, 2>), dim3(rows), dim3(kLnThreads), 0, s, pdy, px, pg, mean, rstd, pr, pdx, h); break;
-    case 4: hipLaunchKernelGGL((ln_bwd_kernel<T, 4>), dim3(rows), dim3(kLnThreads), 0, s, pdy, px, pg, mean, rstd, pr, pdx, h); break;
-    default: hipLaunchKernelGGL((ln_bwd_kernel<T, 8>), dim3(rows), dim3(kLnThreads), 0, s, pdy, px, pg, mean, rstd, pr, pdx, h); break;
+                    const void* resid, void* dx, float* dxf, int rows, int h, hipStream_t s) {
+  switch (ln_cpt(h)) {
+    case 1: ln_bwd_launch<T, TX, TR, 1>(dy, x, gamma, mean, rstd, resid, dx, dxf, rows, h, s); break;
+    case 2: ln_bwd_launch<T, TX, TR, 2>(dy, x, gamma, mean, rstd, resid, dx, dxf, rows, h, s); break;
+    case 4: ln_bwd_launch<T, TX, TR, 4>(dy, x, gamma, mean, rstd, resid, dx, dxf, rows, h, s); break;
+    default: ln_bwd_launch<T, TX, TR, 8>(dy, x, gamma, mean, rstd, resid, dx, dxf, rows, h, s); break;
   }
   return hipGetLastError();
 }
 
 template <typename T>
+hipError_t ln_bwd_dispatch(const void* dy, const void* x, bool x_f32, const void* gamma, const float* mean,
+                           const float* rstd, const void* resid, bool resid_f32, void* dx, float* dxf, int rows,
+                           int h, hipStream_t s) {
+  if (x_f32 && !resid_f32) return ln_bwd_t<T, float, T>(dy, x, gamma, mean, rstd, resid, dx, dxf, rows, h, s);
+  if (!x_f32 && resid_f32) return ln_bwd_t<T, T, float>(dy, x, gamma, mean, rstd, resid, dx, dxf, rows, h, s);
+  if (x_f32 && resid_f32) return ln_bwd_t<T, float, float>(dy, x, gamma, mean, rstd, resid, dx, dxf, rows, h, s);
+  return ln_bwd_t<T, T, T>(dy, x, gamma, mean, rstd, resid, dx, dxf, rows, h, s);
+}
+
+template <typename TA, typename TX>
 hipError_t colsum_t(int mode, const void* a, const void* x, const float* mean, const float* rstd, float* out0,
                     float* out1, float* partial, int rows, int cols, hipStream_t s) {
   int xb, rpb, nrb;
-  colsum_geometry(rows, cols, V<T>::N, xb, rpb, nrb);
+  colsum_geometry(rows, cols, xb, rpb, nrb);
   if (mode == 1)
-    hipLaunchKernelGGL((colsum_partial_kernel<T, 1>), dim3(xb, nrb), dim3(256), 0, s, (const T*)a, (const T*)x, mean,
-                       rstd, partial, rows, cols, rpb, nrb);
+    hipLaunchKernelGGL((colsum_partial_kernel<TA, TX, 1>), dim3(xb, nrb), dim3(256), 0, s, (const TA*)a,
+                       (const TX*)x, mean, rstd, partial, rows, cols, rpb, nrb);
   else
-    hipLaunchKernelGGL((colsum_partial_kernel<T, 0>), dim3(xb, nrb), dim3(256), 0, s, (const T*)a, (const T*)x, mean,
-                       rstd, partial, rows, cols, rpb, nrb);
+    hipLaunchKernelGGL((colsum_partial_kernel<TA, TX, 0>), dim3(xb, nrb), dim3(256), 0, s, (const TA*)a,
+                       (const TX*)x, mean, rstd, partial, rows, cols, rpb, nrb);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(colsum_final_kernel, dim3((cols + 255) / 256), dim3(256), 0, s, partial, out0, out1, nrb, cols,
@@ -380,52 +398,57 @@ hipError_t softmax_t(const float* S, void* P, int nmat, int seq, hipStream_t s) 
 
 }  // namespace
 
-hipError_t launch_ln_fwd(bool is_bf16, bool add, const void* x, const void* o, const void* bias, const void* gamma,
-                         const void* beta, void* x2, void* y, float* mean, float* rstd, int rows, int h, float eps,
-                         hipStream_t s) {
+hipError_t launch_ln_fwd(bool is_bf16, const void* x, const void* gamma, const void* beta, void* y, float* mean,
+                         float* rstd, int rows, int h, float eps, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (is_bf16)
-    return add ? ln_fwd_t<bf16, true>(x, o, bias, gamma, beta, x2, y, mean, rstd, rows, h, eps, s)
-               : ln_fwd_t<bf16, false>(x, o, bias, gamma, beta, x2, y, mean, rstd, rows, h, eps, s);
-  return add ? ln_fwd_t<float, true>(x, o, bias, gamma, beta, x2, y, mean, rstd, rows, h, eps, s)
-             : ln_fwd_t<float, false>(x, o, bias, gamma, beta, x2, y, mean, rstd, rows, h, eps, s);
+  return is_bf16 ? ln_fwd_t<bf16, false>(x, nullptr, nullptr, gamma, beta, nullptr, y, mean, rstd, rows, h, eps, s)
+                 : ln_fwd_t<float, false>(x, nullptr, nullptr, gamma, beta, nullptr, y, mean, rstd, rows, h, eps, s);
 }
 
-hipError_t launch_ln_bwd(bool is_bf16, const void* dy, const void* x, const void* gamma, const float* mean,
-                         const float* rstd, const void* resid, void* dx, int rows, int h, hipStream_t s) {
+hipError_t launch_add_ln_fwd(bool is_bf16, const void* x, const void* o, const void* bias, const void* gamma,
+                             const void* beta, float* x2, void* y, float* mean, float* rstd, int rows, int h,
+                             float eps, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  return is_bf16 ? ln_bwd_t<bf16>(dy, x, gamma, mean, rstd, resid, dx, rows, h, s)
-                 : ln_bwd_t<float>(dy, x, gamma, mean, rstd, resid, dx, rows, h, s);
+  return is_bf16 ? ln_fwd_t<bf16, true>(x, o, bias, gamma, beta, x2, y, mean, rstd, rows, h, eps, s)
+                 : ln_fwd_t<float, true>(x, o, bias, gamma, beta, x2, y, mean, rstd, rows, h, eps, s);
+}
+
+hipError_t launch_ln_bwd(bool is_bf16, const void* dy, const void* x, bool x_f32, const void* gamma,
+                         const float* mean, const float* rstd, const void* resid, bool resid_f32, void* dx,
+                         float* dx_f32, int rows, int h, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  return is_bf16 ? ln_bwd_dispatch<bf16>(dy, x, x_f32, gamma, mean, rstd, resid, resid_f32, dx, dx_f32, rows, h, s)
+                 : ln_bwd_dispatch<float>(dy, x, x_f32, gamma, mean, rstd, resid, resid_f32, dx, dx_f32, rows, h, s);
 }
 
 size_t colsum_partial_floats(int rows, int cols, int mode) {
   int xb, rpb, nrb;
-  colsum_geometry(rows, cols, 4, xb, rpb, nrb);  // fp32 chunks give the most slabs
-  int xb2, rpb2, nrb2;
-  colsum_geometry(rows, cols, 8, xb2, rpb2, nrb2);
-  const int n = nrb > nrb2 ? nrb : nrb2;
-  return (size_t)n * cols * (mode == 1 ? 2 : 1);
+  colsum_geometry(rows, cols, xb, rpb, nrb);
+  return (size_t)nrb * cols * (mode == 1 ? 2 : 1);
 }
 
-hipError_t launch_colsum(bool is_bf16, int mode, const void* a, const void* x, const float* mean, const float* rstd,
-                         float* out0, float* out1, float* partial, int rows, int cols, hipStream_t s) {
+hipError_t launch_colsum(bool is_bf16, int mode, const void* a, bool a_f32, const void* x, bool x_f32,
+                         const float* mean, const float* rstd, float* out0, float* out1, float* partial, int rows,
+                         int cols, hipStream_t s) {
   if (cols <= 0) return hipSuccess;
-  return is_bf16 ? colsum_t<bf16>(mode, a, x, mean, rstd, out0, out1, partial, rows, cols, s)
-                 : colsum_t<float>(mode, a, x, mean, rstd, out0, out1, partial, rows, cols, s);
+  if (!is_bf16 || (a_f32 && (mode == 0 || x_f32)))
+    return colsum_t<float, float>(mode, a, x, mean, rstd, out0, out1, partial, rows, cols, s);
+  if (a_f32) return colsum_t<float, bf16>(mode, a, x, mean, rstd, out0, out1, partial, rows, cols, s);
+  if (mode == 1 && x_f32) return colsum_t<bf16, float>(mode, a, x, mean, rstd, out0, out1, partial, rows, cols, s);
+  return colsum_t<bf16, bf16>(mode, a, x, mean, rstd, out0, out1, partial, rows, cols, s);
 }
 
-hipError_t launch_add_bias_residual(bool is_bf16, const void* x2, const void* y, const void* bias, void* out, int rows,
-                                    int h, hipStream_t s) {
-  const int ve = is_bf16 ? 8 : 4;
-  const int64_t n = (int64_t)rows * h / ve;
+hipError_t launch_add_bias_residual(bool is_bf16, const float* x2, const void* y, const void* bias, void* out,
+                                    int rows, int h, hipStream_t s) {
+  const int64_t n = (int64_t)rows * h / 8;
   if (n <= 0) return hipSuccess;
   const dim3 grid((unsigned)((n + 255) / 256));
   if (is_bf16)
-    hipLaunchKernelGGL(add_bias_residual_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)x2, (const bf16*)y,
-                       (const bf16*)bias, (bf16*)out, n, h / ve);
+    hipLaunchKernelGGL(add_bias_residual_kernel<bf16>, grid, dim3(256), 0, s, x2, (const bf16*)y, (const bf16*)bias,
+                       (bf16*)out, n, h / 8);
   else
-    hipLaunchKernelGGL(add_bias_residual_kernel<float>, grid, dim3(256), 0, s, (const float*)x2, (const float*)y,
-                       (const float*)bias, (float*)out, n, h / ve);
+    hipLaunchKernelGGL(add_bias_residual_kernel<float>, grid, dim3(256), 0, s, x2, (const float*)y,
+                       (const float*)bias, (float*)out, n, h / 8);
   return hipGetLastError();
 }
 

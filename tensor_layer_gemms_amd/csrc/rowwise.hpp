@@ -8,32 +8,42 @@
 
 namespace mt {
 
-// Largest row LayerNorm keeps in registers: 512 threads x 8 chunks of 16 bytes.
+// Largest row LayerNorm keeps in registers: 512 threads x 8 chunks of 8 elements.
 constexpr int kLnThreads = 512;
 constexpr int kLnChunksPerThread = 8;
+constexpr int kLnMaxH = kLnThreads * kLnChunksPerThread * 8;
 // Longest causal softmax row kept in registers (64 lanes x 4 x 16 values).
 constexpr int kSoftmaxMaxSeq = 4096;
 
-// y = LN(x) (ADD == false) or, with ADD, x2 = x + o + bias written to x2 first and
-// y = LN(x2). Saves the row mean and 1/sqrt(var + eps) (fp32). T = bf16 (is_bf16) or fp32.
-hipError_t launch_ln_fwd(bool is_bf16, bool add, const void* x, const void* o, const void* bias,
-                         const void* gamma, const void* beta, void* x2, void* y, float* mean, float* rstd,
-                         int rows, int h, float eps, hipStream_t s);
+// T below is the activation type: bf16 (is_bf16) or fp32. The residual stream X2 and
+// its gradient dX2 are kept in fp32 whatever T is.
 
-// dx = resid + LN-backward(dy; x, gamma, mean, rstd).
-hipError_t launch_ln_bwd(bool is_bf16, const void* dy, const void* x, const void* gamma, const float* mean,
-                         const float* rstd, const void* resid, void* dx, int rows, int h, hipStream_t s);
+// y = LN(x); saves the row mean and 1/sqrt(var + eps) (fp32).
+hipError_t launch_ln_fwd(bool is_bf16, const void* x, const void* gamma, const void* beta, void* y, float* mean,
+                         float* rstd, int rows, int h, float eps, hipStream_t s);
+
+// x2 = x + o + bias (fp32, unrounded), y = LN(x2).
+hipError_t launch_add_ln_fwd(bool is_bf16, const void* x, const void* o, const void* bias, const void* gamma,
+                             const void* beta, float* x2, void* y, float* mean, float* rstd, int rows, int h,
+                             float eps, hipStream_t s);
+
+// dx = resid + LN-backward(dy; x, gamma, mean, rstd). x / resid are fp32 when the
+// matching flag is set (else type T). dx is T; dx_f32 (optional) receives an fp32 copy.
+hipError_t launch_ln_bwd(bool is_bf16, const void* dy, const void* x, bool x_f32, const void* gamma,
+                         const float* mean, const float* rstd, const void* resid, bool resid_f32, void* dx,
+                         float* dx_f32, int rows, int h, hipStream_t s);
 
 // Column sums over `rows` rows, deterministic two-stage reduction through `partial`.
 // mode 0: out0[c] = sum_r a[r, c].
 // mode 1: out0[c] = sum_r a[r, c] * (x[r, c] - mean[r]) * rstd[r], out1[c] = sum_r a[r, c].
+// a / x are fp32 when a_f32 / x_f32, else type T.
 size_t colsum_partial_floats(int rows, int cols, int mode);
-hipError_t launch_colsum(bool is_bf16, int mode, const void* a, const void* x, const float* mean,
-                         const float* rstd, float* out0, float* out1, float* partial, int rows, int cols,
-                         hipStream_t s);
+hipError_t launch_colsum(bool is_bf16, int mode, const void* a, bool a_f32, const void* x, bool x_f32,
+                         const float* mean, const float* rstd, float* out0, float* out1, float* partial, int rows,
+                         int cols, hipStream_t s);
 
-// out = x2 + y + bias (bias broadcast over rows).
-hipError_t launch_add_bias_residual(bool is_bf16, const void* x2, const void* y, const void* bias, void* out,
+// out = x2 + y + bias (x2 fp32, bias broadcast over rows).
+hipError_t launch_add_bias_residual(bool is_bf16, const float* x2, const void* y, const void* bias, void* out,
                                     int rows, int h, hipStream_t s);
 
 // P = softmax over keys j <= q of S (fp32) for each of `nmat` [seq, seq] matrices;

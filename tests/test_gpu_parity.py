@@ -1,7 +1,7 @@
 """Parity of the HIP path (through the C ABI) with the fp64 oracle, on seeded inputs.
 
 Every output of the layer is compared: Out, dX and all twelve parameter gradients,
-with max|gpu - oracle| <= tol * RMS(oracle), tol 2e-2 (bf16) / 1e-4 (fp32).
+to the bar stated in gpu_support (fp32: max-abs <= 1e-4 RMS; bf16: normwise 2e-2).
 Shapes go from the tiny fp32 layer through multi-tile shapes with ragged tails and
 odd head dims to the workloads' full sizes.
 """
@@ -67,13 +67,14 @@ def test_mlp_shards_sum_to_unsharded_block(dtype, tp):
     dx_ref, g_ref = oracle.mlp_bwd(case.dout, c, [g])
     tol = TOL[dtype]
     from gpu_support import compare
-    assert compare("sum y", y_sum, y_ref, tol)[0]
-    assert compare("sum dx", dx_sum, dx_ref, tol)[0]
+    nw = dtype == "bf16"
+    assert compare("sum y", y_sum, y_ref, tol, nw)[0]
+    assert compare("sum dx", dx_sum, dx_ref, tol, nw)[0]
     fs = 4 * shape.h // tp
     for i, gr in enumerate(grads):
-        assert compare(f"dW1[{i}]", gr["w_fc1"], g_ref[0]["w_fc1"][i * fs:(i + 1) * fs], tol)[0]
-        assert compare(f"db1[{i}]", gr["b_fc1"], g_ref[0]["b_fc1"][i * fs:(i + 1) * fs], tol)[0]
-        assert compare(f"dW2[{i}]", gr["w_fc2"], g_ref[0]["w_fc2"][:, i * fs:(i + 1) * fs], tol)[0]
+        assert compare(f"dW1[{i}]", gr["w_fc1"], g_ref[0]["w_fc1"][i * fs:(i + 1) * fs], tol, nw)[0]
+        assert compare(f"db1[{i}]", gr["b_fc1"], g_ref[0]["b_fc1"][i * fs:(i + 1) * fs], tol, nw)[0]
+        assert compare(f"dW2[{i}]", gr["w_fc2"], g_ref[0]["w_fc2"][:, i * fs:(i + 1) * fs], tol, nw)[0]
 
 
 @pytest.mark.parametrize("h,heads,seq,mb,tp,shard", [
@@ -127,6 +128,6 @@ def test_stage_two_layers_small():
     bad = check_all(out, dx, grads[0], r_out, r_dx, r_grads[0][0], TOL["bf16"])
     for k in r_grads[1][0]:
         from gpu_support import compare
-        if not compare(f"l1.{k}", grads[1][k], r_grads[1][0][k], TOL["bf16"])[0]:
+        if not compare(f"l1.{k}", grads[1][k], r_grads[1][0][k], TOL["bf16"], True)[0]:
             bad.append("l1." + k)
     assert not bad, bad

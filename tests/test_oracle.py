@@ -345,3 +345,18 @@ def test_matches_torch_fp64_autograd(tp):
     assert _rel(dx, tx.grad.numpy()) < 1e-11
     for k in si.PARAM_NAMES:
         assert _rel(g[0][k], tp_[k].grad.numpy()) < 1e-11, k
+
+
+def test_keyed_streams_are_independent():
+    """Shard-local inputs come from distinct streams (NumPy pads seed words with zeros,
+    so [0] and [0, 0, 0, 0] would otherwise collide and correlate X with the weights)."""
+    shape = si.LayerShape(h=256, heads=4, seq=64, micro_batch=2, tp=2)
+    case = si.make_case(shape, seed=0)
+    w = case.layers[0]["w_qkv"] / si.WEIGHT_STD
+    n = min(case.x.shape[0], w.shape[0])
+    corr = np.sum(case.x[:n] * w[:n], axis=1) / shape.h
+    assert np.max(np.abs(corr)) < 0.35
+    assert not np.allclose(case.x[0, :8], case.dout[0, :8])
+    heads = [si.keyed_rng(0, p, l, r, t).standard_normal(4).tobytes()
+             for p in (1, 2, 3) for l in (0, 1) for r in (0, 1) for t in (0, 1, 2)]
+    assert len(set(heads)) == len(heads)
