@@ -121,10 +121,12 @@ __device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int&
 }
 
 // ---------------------------------------------------------------------------- bf16 MFMA
-// LDS tile: ROWS x 64 bf16, row = 128 bytes = 8 chunks of 16 bytes; chunk c of row r
-// lives at chunk position c ^ (r & 7), so the 32 lanes of an MFMA operand read (same
-// chunk, 32 consecutive rows) hit distinct banks.
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 64 + ((chunk ^ (row & 7)) << 3); }
+// LDS tile: ROWS x 64 bf16, row = 128 bytes = 8 chunks of 16 bytes. The 64 banks of 4
+// bytes span 256 bytes = two rows, and a 16-byte read is served 16 lanes at a time. An
+// MFMA operand read has 16 lanes on 16 consecutive rows at the same chunk, so chunk c of
+// row r lives at position c ^ ((r >> 1) & 7): the eight even rows then use eight distinct
+// chunks of the lower bank half and the eight odd rows those of the upper half.
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 1) & 7)) << 3); }
 
 template <int ROWS, int NT, bool KCONTIG>
 struct TileLoader {
@@ -133,34 +135,42 @@ struct TileLoader {
   static constexpr int ITEMS = KCONTIG ? ROWS * 8 : ROWS;
   static constexpr int PER = (ITEMS + NT - 1) / NT;
   static constexpr int NREG = KCONTIG ? PER : PER * 8;
+  static_assert(NREG <= 32, "validity mask holds 32 loads");
   u32x4 r[NREG];
+  uint32_t ok = 0;  // bit q: load q was in range (zeroed at store time otherwise)
 
+  // Issues the global loads of one k tile. Out-of-range items read the (always valid)
+  // tile origin; their bit in `ok` is clear and store() writes zeros instead. Nothing
+  // here consumes the loaded data, so the loads stay in flight until store().
   __device__ __forceinline__ void load(const bf16* base, int64_t ld, int row0, int rows_valid, int k0, int kend,
                                        int tid) {
+    ok = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int it = tid + i * NT;
       if (ITEMS % NT != 0 && it >= ITEMS) break;
-      // Out-of-range items load from the (always valid) tile origin and are zeroed
-      // with a select, so the loads need no branches.
       if constexpr (KCONTIG) {
         const int row = it >> 3, kc = it & 7;
         const int gr = row0 + row, gk = k0 + kc * 8;
-        const bool ok = gr < rows_valid && gk < kend;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(base + (ok ? (int64_t)gr * ld + gk : 0));
-        r[i] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+        const bool v = gr < rows_valid && gk < kend;
+        r[i] = *reinterpret_cast<const u32x4*>(base + (v ? (int64_t)gr * ld + gk : 0));
+        ok |= (uint32_t)v << i;
       } else {
         const int kb = it & 7, rb = it >> 3;
         const int gr = row0 + rb * 8;
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
           const int gk = k0 + kb * 8 + kk;
-          const bool ok = gr < rows_valid && gk < kend;
-          const u32x4 v = *reinterpret_cast<const u32x4*>(base + (ok ? (int64_t)gk * ld + gr : 0));
-          r[i * 8 + kk] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+          const bool v = gr < rows_valid && gk < kend;
+          r[i * 8 + kk] = *reinterpret_cast<const u32x4*>(base + (v ? (int64_t)gk * ld + gr : 0));
+          ok |= (uint32_t)v << (i * 8 + kk);
         }
       }
     }
+  }
+
+  __device__ __forceinline__ u32x4 val(int q) const {
+    return ((ok >> q) & 1u) ? r[q] : u32x4{0u, 0u, 0u, 0u};
   }
 
   __device__ __forceinline__ void store(bf16* lds, int tid) const {
@@ -170,19 +180,29 @@ struct TileLoader {
       if (ITEMS % NT != 0 && it >= ITEMS) break;
       if constexpr (KCONTIG) {
         const int row = it >> 3, kc = it & 7;
-        *reinterpret_cast<u32x4*>(lds + swz(row, kc)) = r[i];
+        *reinterpret_cast<u32x4*>(lds + swz(row, kc)) = val(i);
       } else {
         const int kb = it & 7, rb = it >> 3;
-        // r[i*8+kk] holds rows rb*8..rb*8+7 at k = kb*8+kk (two rows per dword);
-        // output row rr gathers its 8 k values (two k per dword).
+        u32x4 v[8];
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) v[kk] = val(i * 8 + kk);
+        // v[kk] holds rows rb*8..rb*8+7 at k = kb*8+kk (two rows per dword); output
+        // row rr gathers its 8 k values (two k per dword). Lanes 8..15 hold the next
+        // row block; they write the rows in the order rr ^ 1 so that each 16-lane store
+        // covers one even and one odd row (both bank halves).
+        const bool odd = rb & 1;
 #pragma unroll
         for (int rr = 0; rr < 8; ++rr) {
-          const uint32_t sel = (rr & 1) ? 0x07060302u : 0x05040100u;
-          u32x4 w;
+          u32x4 wa, wb;
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            w[j] = __builtin_amdgcn_perm(r[i * 8 + 2 * j + 1][rr >> 1], r[i * 8 + 2 * j][rr >> 1], sel);
-          *reinterpret_cast<u32x4*>(lds + swz(rb * 8 + rr, kb)) = w;
+          for (int j = 0; j < 4; ++j) {
+            wa[j] = __builtin_amdgcn_perm(v[2 * j + 1][rr >> 1], v[2 * j][rr >> 1],
+                                          (rr & 1) ? 0x07060302u : 0x05040100u);
+            wb[j] = __builtin_amdgcn_perm(v[2 * j + 1][(rr ^ 1) >> 1], v[2 * j][(rr ^ 1) >> 1],
+                                          ((rr ^ 1) & 1) ? 0x07060302u : 0x05040100u);
+          }
+          const int row = rb * 8 + (odd ? (rr ^ 1) : rr);
+          *reinterpret_cast<u32x4*>(lds + swz(row, kb)) = odd ? wb : wa;
         }
       }
     }
@@ -234,21 +254,29 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
       }
       const bf16* sA = smem + cur * (BM + BN) * BK;
       const bf16* sB = sA + BM * BK;
+      // 32x32x16 operands: lane l supplies row (l & 31) and 8 consecutive k starting at
+      // 8 * (l >> 5) of the 16-wide k step. Fragments of step ks+1 are read while the
+      // MFMAs of step ks run.
+      bf16x8 af[2][TM], bfr[2][TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[0][i] = *reinterpret_cast<const bf16x8*>(sA + swz(wm0 + i * 32 + (lane & 31), lane >> 5));
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bfr[0][j] = *reinterpret_cast<const bf16x8*>(sB + swz(wn0 + j * 32 + (lane & 31), lane >> 5));
 #pragma unroll
       for (int ks = 0; ks < BK / 16; ++ks) {
-        // 32x32x16 operands: lane l supplies row (l & 31) and 8 consecutive k
-        // starting at 8 * (l >> 5) of the 16-wide k step.
-        const int ch = ks * 2 + (lane >> 5);
-        bf16x8 af[TM], bfr[TN];
+        const int cb = ks & 1, nb = cb ^ 1;
+        if (ks + 1 < BK / 16) {
+          const int ch = (ks + 1) * 2 + (lane >> 5);
 #pragma unroll
-        for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(sA + swz(wm0 + i * 32 + (lane & 31), ch));
+          for (int i = 0; i < TM; ++i) af[nb][i] = *reinterpret_cast<const bf16x8*>(sA + swz(wm0 + i * 32 + (lane & 31), ch));
 #pragma unroll
-        for (int j = 0; j < TN; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(sB + swz(wn0 + j * 32 + (lane & 31), ch));
+          for (int j = 0; j < TN; ++j) bfr[nb][j] = *reinterpret_cast<const bf16x8*>(sB + swz(wn0 + j * 32 + (lane & 31), ch));
+        }
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
           for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cb][j], af[cb][i], acc[i][j], 0, 0, 0);
       }
       if (t + 1 < nk) {
         bf16* nxt = smem + (cur ^ 1) * (BM + BN) * BK;
