@@ -24,6 +24,37 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 METRIC = "model TFLOP/s per GPU, GPT layer-shard fwd+bwd; % of bf16 MFMA peak"
+# HBM traffic of the dominant kernel, measured with rocprofv3 counters and committed as a
+# summary; it is reported only while the GEMM sources hash to the value recorded there.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fc1_fwd_gpt175b_tp8_traffic.txt")
+GEMM_SOURCES = ["tensor_layer_gemms_amd/csrc/gemm_kernels.hpp", "tensor_layer_gemms_amd/csrc/gemm_bf16.hip",
+                "tensor_layer_gemms_amd/csrc/gemm.hpp", "tensor_layer_gemms_amd/csrc/device_common.hpp"]
+
+
+def gemm_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in GEMM_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kernel: str):
+    """Bytes per launch of `kernel` from the committed counter summary, or None when the
+    summary is missing, is for another kernel, or predates the current GEMM sources."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("label") != kernel or kv.get("gemm_source_hash") != gemm_source_hash():
+            return None
+        return float(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def parse():
@@ -36,7 +67,20 @@ def parse():
                     help="label of the kernel launch whose roofline is reported")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="also print a per-launch time breakdown (stderr)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes three times (counter calibration)")
     return ap.parse_args()
+
+
+def copy_probe(nbytes: int) -> None:
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes}), flush=True)
 
 
 def cpu_baseline(case, shape):
@@ -62,6 +106,9 @@ def cpu_baseline(case, shape):
 
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the tensor-parallel "
               "all-reduce is not part of it. Run with --gpus 1.", file=sys.stderr)
@@ -144,8 +191,9 @@ def main():
         avg_ms = sum(r[1] for r in recs) / len(recs)
         kflops = recs[0][2]
         achieved = kflops / (avg_ms * 1e-3) / 1e12
+        traffic = committed_traffic(args.dominant)
         roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": args.dominant,
+                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic, "kernel": args.dominant,
                     "avg_ms": round(avg_ms, 4), "launches": len(recs), "gflop_per_launch": round(kflops / 1e9, 2)}
 
     cpu = None

@@ -23,6 +23,7 @@ enum EpiKind : int {
   EPI_BIAS_GELU = 3,  // C = a = acc + bias[n] (pre-activation, kept for backward); C2 = GeLU(a)
   EPI_DGELU = 4,      // C = acc * GeLU'(aux[m, n])            (aux = saved pre-activation)
   EPI_DSOFTMAX = 5,   // C = aux[m, n] * (acc - vec[m])        (aux = P, vec = rowsum(P * dP))
+  EPI_BIAS_SPLIT = 6, // v = acc + bias[n]; C = bf16(v); for n < seg_n also C2 = bf16(v - bf16(v))
 };
 
 enum Causal : int {
@@ -37,11 +38,21 @@ enum Causal : int {
 // causal consumer whose tile sizes divide kCausalChunk reads only written entries.
 constexpr int kCausalChunk = 256;
 
+// K segments (bf16 path): the contraction may run over nseg segments of K each, segment s
+// reading A from seg_a[s] and B from seg_b[s] with the strides of A and B (segment 0 is
+// A and B). Tiles whose first column is >= seg_n run segment 0 only. This forms
+// hi/lo-compensated products, e.g. (U_hi + U_lo) W^T or Q_hi K_hi^T + Q_hi K_lo^T +
+// Q_lo K_hi^T, with bf16 MFMA operands.
+constexpr int kMaxSeg = 3;
+
 struct GemmArgs {
   const void* A;
   const void* B;
+  const void* seg_a[kMaxSeg];
+  const void* seg_b[kMaxSeg];
+  int nseg, seg_n;
   void* C;
-  void* C2;         // EPI_BIAS_GELU second output, same layout as C
+  void* C2;         // EPI_BIAS_GELU / EPI_BIAS_SPLIT second output, same layout as C
   const void* aux;  // EPI_DGELU / EPI_DSOFTMAX input, same layout as C
   const void* vec;  // bias [N] (activation type) or fp32 row vector [M] per batch
   int64_t lda, ldb, ldc;

@@ -9,24 +9,28 @@ namespace {
 constexpr int kNumCUs = 256;
 
 struct TileCfg {
-  int bm, bn;
-  float eff;  // relative per-tile MFMA efficiency (bigger tiles reuse LDS operands more)
+  int bm, bn, wm, wn;
+  float eff;  // relative per-tile throughput, measured on the layer's shapes
 };
-// 256x256: 8 waves (2 x 4), wave tile 128x64; 256x128: 4 waves (2 x 2), 128x64;
-// 128x128: 4 waves, 64x64.
-constexpr TileCfg kTiles[] = {{256, 256, 1.0f}, {256, 128, 0.9f}, {128, 128, 0.75f}};
+// Candidates per operand layout: forward (A, B k-contiguous), input gradient (B
+// n-contiguous), weight gradient (both token-strided).
+constexpr TileCfg kFwd[] = {{256, 256, 2, 4, 1.0f}, {128, 128, 2, 2, 0.85f}};
+constexpr TileCfg kDgrad[] = {{256, 128, 2, 4, 1.0f}, {256, 256, 2, 4, 0.95f}, {128, 128, 2, 2, 0.8f}};
+constexpr TileCfg kWgrad[] = {{256, 256, 2, 2, 1.0f}, {128, 256, 2, 2, 0.9f}, {128, 128, 2, 2, 0.8f}};
 
-int pick_tile(const GemmArgs& g, int batch) {
-  if (g.causal != CAUSAL_NONE) return 2;  // attention products: small square tiles
+// Pick the candidate with the least estimated time: whole waves of tiles over the CUs
+// times tile area over the candidate's throughput.
+template <int N>
+int pick(const TileCfg (&c)[N], const GemmArgs& g, int batch) {
   int best = 0;
   double best_cost = 1e300;
-  for (int c = 0; c < 3; ++c) {
-    const long tiles = (long)((g.M + kTiles[c].bm - 1) / kTiles[c].bm) * ((g.N + kTiles[c].bn - 1) / kTiles[c].bn) * batch;
+  for (int i = 0; i < N; ++i) {
+    const long tiles = (long)((g.M + c[i].bm - 1) / c[i].bm) * ((g.N + c[i].bn - 1) / c[i].bn) * batch;
     const long waves = (tiles + kNumCUs - 1) / kNumCUs;
-    const double cost = (double)waves * kTiles[c].bm * kTiles[c].bn / kTiles[c].eff;
+    const double cost = (double)waves * c[i].bm * c[i].bn / c[i].eff;
     if (cost < best_cost * 0.999) {
       best_cost = cost;
-      best = c;
+      best = i;
     }
   }
   return best;
@@ -42,10 +46,26 @@ hipError_t run(const GemmArgs& g, int batch, hipStream_t s) {
 
 template <bool AK, bool BK, int KIND>
 hipError_t run_tile(const GemmArgs& g, int batch, hipStream_t s) {
-  switch (pick_tile(g, batch)) {
-    case 0: return run<AK, BK, 256, 256, 2, 4, KIND>(g, batch, s);
-    case 1: return run<AK, BK, 256, 128, 2, 2, KIND>(g, batch, s);
-    default: return run<AK, BK, 128, 128, 2, 2, KIND>(g, batch, s);
+  // Attention products (causal) use 128x128 tiles: every causal tile size must divide
+  // the 256-column chunk the probability rows are written in.
+  if (g.causal != CAUSAL_NONE) return run<AK, BK, 128, 128, 2, 2, KIND>(g, batch, s);
+  if constexpr (AK && BK) {
+    switch (pick(kFwd, g, batch)) {
+      case 0: return run<AK, BK, 256, 256, 2, 4, KIND>(g, batch, s);
+      default: return run<AK, BK, 128, 128, 2, 2, KIND>(g, batch, s);
+    }
+  } else if constexpr (AK) {
+    switch (pick(kDgrad, g, batch)) {
+      case 0: return run<AK, BK, 256, 128, 2, 4, KIND>(g, batch, s);
+      case 1: return run<AK, BK, 256, 256, 2, 4, KIND>(g, batch, s);
+      default: return run<AK, BK, 128, 128, 2, 2, KIND>(g, batch, s);
+    }
+  } else {
+    switch (pick(kWgrad, g, batch)) {
+      case 0: return run<AK, BK, 256, 256, 2, 2, KIND>(g, batch, s);
+      case 1: return run<AK, BK, 128, 256, 2, 2, KIND>(g, batch, s);
+      default: return run<AK, BK, 128, 128, 2, 2, KIND>(g, batch, s);
+    }
   }
 }
 
@@ -53,11 +73,14 @@ hipError_t run_tile(const GemmArgs& g, int batch, hipStream_t s) {
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, bool a_k, bool b_k, int kind, int batch, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0 || batch <= 0) return hipSuccess;
+  if (g.nseg < 1 || g.nseg > kMaxSeg || (g.nseg > 1 && g.causal != CAUSAL_NONE && g.causal != CAUSAL_SKIP_UPPER))
+    return hipErrorInvalidValue;
   if (a_k && b_k) {  // forward products (X W^T, Q K^T, dctx V^T)
     switch (kind) {
       case EPI_STORE: return run_tile<true, true, EPI_STORE>(g, batch, s);
       case EPI_STORE_F32: return run_tile<true, true, EPI_STORE_F32>(g, batch, s);
       case EPI_BIAS: return run_tile<true, true, EPI_BIAS>(g, batch, s);
+      case EPI_BIAS_SPLIT: return run_tile<true, true, EPI_BIAS_SPLIT>(g, batch, s);
       case EPI_BIAS_GELU: return run_tile<true, true, EPI_BIAS_GELU>(g, batch, s);
       case EPI_DSOFTMAX: return run_tile<true, true, EPI_DSOFTMAX>(g, batch, s);
     }

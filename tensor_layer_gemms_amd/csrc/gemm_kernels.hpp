@@ -76,6 +76,17 @@ __device__ __forceinline__ void epi_store4(const GemmArgs& g, int64_t coff, int6
       for (int e = 0; e < 4; ++e) z[e] = gelu_f(v[e]);
       store4_bf16(static_cast<bf16*>(g.C2) + idx, z);
     }
+  } else if constexpr (KIND == EPI_BIAS_SPLIT) {
+    float b[4];
+    load4_bf16(static_cast<const bf16*>(g.vec) + n, b);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = acc[e] + b[e];
+    if (n < g.seg_n) {
+      float lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) lo[e] = v[e] - (float)(bf16)v[e];
+      store4_bf16(static_cast<bf16*>(g.C2) + idx, lo);
+    }
   } else if constexpr (KIND == EPI_DGELU) {
     float a[4];
     load4_bf16(static_cast<const bf16*>(g.aux) + idx, a);
@@ -135,6 +146,7 @@ struct TileLoader {
   static constexpr int ITEMS = KCONTIG ? ROWS * 8 : ROWS;
   static constexpr int PER = (ITEMS + NT - 1) / NT;
   static constexpr int NREG = KCONTIG ? PER : PER * 8;
+  static constexpr int NDSW = KCONTIG ? PER : PER * 8;  // LDS writes per tile
   static_assert(NREG <= 32, "validity mask holds 32 loads");
   u32x4 r[NREG];
   uint32_t ok = 0;  // bit q: load q was in range (zeroed at store time otherwise)
@@ -226,8 +238,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
   int kbeg, kend;
   causal_k_range(g, m0, BM, kbeg, kend);
   const int z = blockIdx.y, zo = z / g.zdiv, zi = z % g.zdiv;
-  const bf16* A = static_cast<const bf16*>(g.A) + zo * g.a_so + zi * g.a_si;
-  const bf16* B = static_cast<const bf16*>(g.B) + zo * g.b_so + zi * g.b_si;
+  const int64_t aoff = zo * g.a_so + zi * g.a_si, boff = zo * g.b_so + zi * g.b_si;
+  const int nseg = n0 < g.seg_n ? g.nseg : 1;
 
   TileLoader<BM, NT, A_K> la;
   TileLoader<BN, NT, B_K> lb;
@@ -239,33 +251,50 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+  const int nk1 = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;  // k steps per segment
+  const int nk = nk1 * nseg;
+  // Step t reads segment t / nk1 at k = kbeg + (t % nk1) * BK.
+  auto issue = [&](int t) {
+    const int sg = (t >= nk1) + (t >= 2 * nk1);
+    const int k0 = kbeg + (t - sg * nk1) * BK;
+    la.load(static_cast<const bf16*>(g.seg_a[sg]) + aoff, g.lda, m0, g.M, k0, kend, tid);
+    lb.load(static_cast<const bf16*>(g.seg_b[sg]) + boff, g.ldb, n0, g.N, k0, kend, tid);
+  };
+  // Three-stage pipeline: LDS buffer t & 1 holds the tile being multiplied, the other
+  // buffer receives tile t + 1 (loaded into registers during step t - 1), and the
+  // registers receive tile t + 2. A step's body has no branches (loads past the end of
+  // the k range are masked to zero like any other out-of-range load), so it is one
+  // scheduling region in which the hints below interleave the LDS reads of the next
+  // fragments, the LDS writes of tile t + 1 and the global loads of tile t + 2 between
+  // the MFMAs.
   if (nk > 0) {
-    la.load(A, g.lda, m0, g.M, kbeg, kend, tid);
-    lb.load(B, g.ldb, n0, g.N, kbeg, kend, tid);
+    issue(0);
     la.store(smem, tid);
     lb.store(smem + BM * BK, tid);
+    issue(nk > 1 ? 1 : 0);
     __syncthreads();
+    constexpr int KS = BK / 16;
+    constexpr int NMF = KS * TM * TN;                  // MFMAs per step
+    constexpr int NDR = (KS - 1) * (TM + TN);          // fragment reads issued inside the step
+    constexpr int NDW = TileLoader<BM, NT, A_K>::NDSW + TileLoader<BN, NT, B_K>::NDSW;  // LDS writes
+    constexpr int NVM = TileLoader<BM, NT, A_K>::NREG + TileLoader<BN, NT, B_K>::NREG;  // global loads
     for (int t = 0; t < nk; ++t) {
       const int cur = t & 1;
-      if (t + 1 < nk) {
-        la.load(A, g.lda, m0, g.M, kbeg + (t + 1) * BK, kend, tid);
-        lb.load(B, g.ldb, n0, g.N, kbeg + (t + 1) * BK, kend, tid);
-      }
       const bf16* sA = smem + cur * (BM + BN) * BK;
       const bf16* sB = sA + BM * BK;
-      // 32x32x16 operands: lane l supplies row (l & 31) and 8 consecutive k starting at
-      // 8 * (l >> 5) of the 16-wide k step. Fragments of step ks+1 are read while the
-      // MFMAs of step ks run.
+      bf16* nxt = smem + (cur ^ 1) * (BM + BN) * BK;
+      // 32x32x16 operands: lane l supplies row (l & 31) and 8 consecutive k starting
+      // at 8 * (l >> 5) of the 16-wide k step.
       bf16x8 af[2][TM], bfr[2][TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i) af[0][i] = *reinterpret_cast<const bf16x8*>(sA + swz(wm0 + i * 32 + (lane & 31), lane >> 5));
 #pragma unroll
       for (int j = 0; j < TN; ++j) bfr[0][j] = *reinterpret_cast<const bf16x8*>(sB + swz(wn0 + j * 32 + (lane & 31), lane >> 5));
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
+      for (int ks = 0; ks < KS; ++ks) {
         const int cb = ks & 1, nb = cb ^ 1;
-        if (ks + 1 < BK / 16) {
+        if (ks + 1 < KS) {
           const int ch = (ks + 1) * 2 + (lane >> 5);
 #pragma unroll
           for (int i = 0; i < TM; ++i) af[nb][i] = *reinterpret_cast<const bf16x8*>(sA + swz(wm0 + i * 32 + (lane & 31), ch));
@@ -277,11 +306,20 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
           for (int j = 0; j < TN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cb][j], af[cb][i], acc[i][j], 0, 0, 0);
+        if (ks == 0) {
+          la.store(nxt, tid);
+          lb.store(nxt + BM * BK, tid);
+          issue(t + 2 < nk ? t + 2 : nk - 1);  // past the last step: a harmless reload
+        }
       }
-      if (t + 1 < nk) {
-        bf16* nxt = smem + (cur ^ 1) * (BM + BN) * BK;
-        la.store(nxt, tid);
-        lb.store(nxt + BM * BK, tid);
+      // Interleave: every MFMA is followed by one fragment read while they last, and
+      // the LDS writes and global loads are spread over the remaining MFMA slots.
+#pragma unroll
+      for (int q = 0; q < NMF; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (q < NDR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (q >= NMF / 4 && q < NMF / 4 + NDW) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+        if (q >= NMF / 8 && q < NMF / 8 + NVM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
       __syncthreads();
     }

@@ -99,13 +99,17 @@ size_t carve_layer_saved(const Dims& d, void* base, LayerSaved* s) {
 
 struct LayerFwdWs {
   float* S;
-  void* o;  // out-projection partial, then FC2 partial
+  void* o;       // out-projection partial, then FC2 partial
+  void* u_lo;    // bf16 path: rounding remainder of U
+  void* qkv_lo;  // bf16 path: rounding remainders of Q and K, in the QKV layout
 };
 
 size_t carve_layer_fwd_ws(const Dims& d, void* base, LayerFwdWs* w) {
   Carver c(base);
   w->S = c.take<float>(d.B * d.at * d.seq * d.seq * 4);
   w->o = c.take(d.M * d.h * d.es);
+  w->u_lo = d.bf16 ? c.take(d.M * d.h * 2) : nullptr;
+  w->qkv_lo = d.bf16 ? c.take(d.M * d.qkv * 2) : nullptr;
   return c.off;
 }
 
@@ -228,6 +232,10 @@ GemmArgs plain(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, 
   g.K = (int)K;
   g.zdiv = 1;
   g.alpha = 1.0f;
+  g.seg_a[0] = A;
+  g.seg_b[0] = B;
+  g.nseg = 1;
+  g.seg_n = 1 << 30;
   return g;
 }
 
@@ -260,20 +268,38 @@ int layer_fwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, void
   const int batch = (int)(d.B * d.at);
   Attn at{d};
 
-  // F1 LayerNorm 1
-  q.run("ln1_fwd", 0, 2 * Mh * es, [&] {
-    return launch_ln_fwd(bf, x, w.ln1_g, w.ln1_b, sv.u, sv.mean1, sv.rstd1, (int)d.M, (int)d.h, kLnEps, stream);
+  // F1 LayerNorm 1 (bf16 path: also the rounding remainder U_lo of U)
+  q.run("ln1_fwd", 0, Mh * es * (bf ? 3 : 2), [&] {
+    return launch_ln_fwd(bf, x, w.ln1_g, w.ln1_b, sv.u, ws.u_lo, sv.mean1, sv.rstd1, (int)d.M, (int)d.h, kLnEps,
+                         stream);
   });
-  // F2 column-parallel QKV projection + bias
-  q.run("qkv_fwd", gflop(d.M, d.qkv, d.h), 0, [&] {
+  // F2 column-parallel QKV projection + bias. bf16 path: the Q and K columns are formed
+  // from U_hi + U_lo (a second K segment) and stored as hi + lo bf16 pairs, so the
+  // softmax logits, whose sharp maxima amplify input rounding, see Q and K to ~16 bits.
+  q.run("qkv_fwd", gflop(d.M, d.qkv, d.h) + (bf ? gflop(d.M, 2 * d.hs, d.h) : 0), 0, [&] {
     GemmArgs g = plain(sv.u, d.h, w.w_qkv, d.h, sv.qkv, d.qkv, d.M, d.qkv, d.h);
     g.vec = w.b_qkv;
-    return gemm(d, g, true, true, EPI_BIAS, 1, stream);
+    if (!bf) return gemm(d, g, true, true, EPI_BIAS, 1, stream);
+    g.seg_a[1] = ws.u_lo;
+    g.seg_b[1] = w.w_qkv;
+    g.nseg = 2;
+    g.seg_n = (int)(2 * d.hs);
+    g.C2 = ws.qkv_lo;
+    return gemm(d, g, true, true, EPI_BIAS_SPLIT, 1, stream);
   });
-  // F3 scores S = Q K^T / sqrt(d), causal tiles only, fp32
-  q.run("attn_scores", at.flops(), 0, [&] {
+  // F3 scores S = Q K^T / sqrt(d), causal tiles only, fp32 (bf16 path:
+  // Q_hi K_hi^T + Q_hi K_lo^T + Q_lo K_hi^T)
+  q.run("attn_scores", at.flops() * (bf ? 3 : 1), 0, [&] {
     GemmArgs g = plain(sv.qkv, d.qkv, static_cast<const char*>(sv.qkv) + d.hs * d.es, d.qkv, ws.S, d.seq, d.seq,
                        d.seq, d.d);
+    if (bf) {
+      const char* lo = static_cast<const char*>(ws.qkv_lo);
+      g.seg_a[1] = sv.qkv;
+      g.seg_b[1] = lo + d.hs * d.es;
+      g.seg_a[2] = lo;
+      g.seg_b[2] = static_cast<const char*>(sv.qkv) + d.hs * d.es;
+      g.nseg = 3;
+    }
     at.head_operand(d.qkv, g.a_so, g.a_si);
     at.head_operand(d.qkv, g.b_so, g.b_si);
     g.c_so = d.at * d.seq * d.seq;

@@ -19,8 +19,9 @@ template <typename T, bool ADD, int CPT>
 __global__ __launch_bounds__(kLnThreads) void ln_fwd_kernel(const T* __restrict__ x, const T* __restrict__ o,
                                                             const T* __restrict__ bias, const T* __restrict__ gamma,
                                                             const T* __restrict__ beta, float* __restrict__ x2,
-                                                            T* __restrict__ y, float* __restrict__ mean,
-                                                            float* __restrict__ rstd, int h, float eps) {
+                                                            T* __restrict__ y, T* __restrict__ ylo,
+                                                            float* __restrict__ mean, float* __restrict__ rstd, int h,
+                                                            float eps) {
   constexpr int NW = kLnThreads / 64;
   __shared__ float red[NW];
   const int64_t row = blockIdx.x;
@@ -75,6 +76,12 @@ __global__ __launch_bounds__(kLnThreads) void ln_fwd_kernel(const T* __restrict_
 #pragma unroll
       for (int e = 0; e < 8; ++e) out[e] = (v[c][e] - mu) * rs * gv[e] + bv[e];
       store8(y + row * h + (int64_t)ch * 8, out);
+      if (ylo) {
+        float lo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lo[e] = out[e] - to_f32(from_f32<T>(out[e]));
+        store8(ylo + row * h + (int64_t)ch * 8, lo);
+      }
     }
   }
 }
@@ -319,19 +326,19 @@ void colsum_geometry(int rows, int cols, int& xblocks, int& rpb, int& nrb) {
 
 template <typename T, bool ADD, int CPT>
 void ln_fwd_launch(const void* x, const void* o, const void* bias, const void* gamma, const void* beta, float* x2,
-                   void* y, float* mean, float* rstd, int rows, int h, float eps, hipStream_t s) {
+                   void* y, void* ylo, float* mean, float* rstd, int rows, int h, float eps, hipStream_t s) {
   hipLaunchKernelGGL((ln_fwd_kernel<T, ADD, CPT>), dim3(rows), dim3(kLnThreads), 0, s, (const T*)x, (const T*)o,
-                     (const T*)bias, (const T*)gamma, (const T*)beta, x2, (T*)y, mean, rstd, h, eps);
+                     (const T*)bias, (const T*)gamma, (const T*)beta, x2, (T*)y, (T*)ylo, mean, rstd, h, eps);
 }
 
 template <typename T, bool ADD>
 hipError_t ln_fwd_t(const void* x, const void* o, const void* bias, const void* gamma, const void* beta, float* x2,
-                    void* y, float* mean, float* rstd, int rows, int h, float eps, hipStream_t s) {
+                    void* y, void* ylo, float* mean, float* rstd, int rows, int h, float eps, hipStream_t s) {
   switch (ln_cpt(h)) {
-    case 1: ln_fwd_launch<T, ADD, 1>(x, o, bias, gamma, beta, x2, y, mean, rstd, rows, h, eps, s); break;
-    case 2: ln_fwd_launch<T, ADD, 2>(x, o, bias, gamma, beta, x2, y, mean, rstd, rows, h, eps, s); break;
-    case 4: ln_fwd_launch<T, ADD, 4>(x, o, bias, gamma, beta, x2, y, mean, rstd, rows, h, eps, s); break;
-    default: ln_fwd_launch<T, ADD, 8>(x, o, bias, gamma, beta, x2, y, mean, rstd, rows, h, eps, s); break;
+    case 1: ln_fwd_launch<T, ADD, 1>(x, o, bias, gamma, beta, x2, y, ylo, mean, rstd, rows, h, eps, s); break;
+    case 2: ln_fwd_launch<T, ADD, 2>(x, o, bias, gamma, beta, x2, y, ylo, mean, rstd, rows, h, eps, s); break;
+    case 4: ln_fwd_launch<T, ADD, 4>(x, o, bias, gamma, beta, x2, y, ylo, mean, rstd, rows, h, eps, s); break;
+    default: ln_fwd_launch<T, ADD, 8>(x, o, bias, gamma, beta, x2, y, ylo, mean, rstd, rows, h, eps, s); break;
   }
   return hipGetLastError();
 }
@@ -398,19 +405,21 @@ hipError_t softmax_t(const float* S, void* P, int nmat, int seq, hipStream_t s) 
 
 }  // namespace
 
-hipError_t launch_ln_fwd(bool is_bf16, const void* x, const void* gamma, const void* beta, void* y, float* mean,
-                         float* rstd, int rows, int h, float eps, hipStream_t s) {
+hipError_t launch_ln_fwd(bool is_bf16, const void* x, const void* gamma, const void* beta, void* y, void* y_lo,
+                         float* mean, float* rstd, int rows, int h, float eps, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  return is_bf16 ? ln_fwd_t<bf16, false>(x, nullptr, nullptr, gamma, beta, nullptr, y, mean, rstd, rows, h, eps, s)
-                 : ln_fwd_t<float, false>(x, nullptr, nullptr, gamma, beta, nullptr, y, mean, rstd, rows, h, eps, s);
+  return is_bf16
+             ? ln_fwd_t<bf16, false>(x, nullptr, nullptr, gamma, beta, nullptr, y, y_lo, mean, rstd, rows, h, eps, s)
+             : ln_fwd_t<float, false>(x, nullptr, nullptr, gamma, beta, nullptr, y, nullptr, mean, rstd, rows, h, eps,
+                                      s);
 }
 
 hipError_t launch_add_ln_fwd(bool is_bf16, const void* x, const void* o, const void* bias, const void* gamma,
                              const void* beta, float* x2, void* y, float* mean, float* rstd, int rows, int h,
                              float eps, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  return is_bf16 ? ln_fwd_t<bf16, true>(x, o, bias, gamma, beta, x2, y, mean, rstd, rows, h, eps, s)
-                 : ln_fwd_t<float, true>(x, o, bias, gamma, beta, x2, y, mean, rstd, rows, h, eps, s);
+  return is_bf16 ? ln_fwd_t<bf16, true>(x, o, bias, gamma, beta, x2, y, nullptr, mean, rstd, rows, h, eps, s)
+                 : ln_fwd_t<float, true>(x, o, bias, gamma, beta, x2, y, nullptr, mean, rstd, rows, h, eps, s);
 }
 
 hipError_t launch_ln_bwd(bool is_bf16, const void* dy, const void* x, bool x_f32, const void* gamma,

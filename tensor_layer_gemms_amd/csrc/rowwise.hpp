@@ -18,9 +18,10 @@ constexpr int kSoftmaxMaxSeq = 4096;
 // T below is the activation type: bf16 (is_bf16) or fp32. The residual stream X2 and
 // its gradient dX2 are kept in fp32 whatever T is.
 
-// y = LN(x); saves the row mean and 1/sqrt(var + eps) (fp32).
-hipError_t launch_ln_fwd(bool is_bf16, const void* x, const void* gamma, const void* beta, void* y, float* mean,
-                         float* rstd, int rows, int h, float eps, hipStream_t s);
+// y = LN(x); saves the row mean and 1/sqrt(var + eps) (fp32). With y_lo (bf16 only),
+// also writes the rounding remainder y_lo = bf16(y - bf16(y)).
+hipError_t launch_ln_fwd(bool is_bf16, const void* x, const void* gamma, const void* beta, void* y, void* y_lo,
+                         float* mean, float* rstd, int rows, int h, float eps, hipStream_t s);
 
 // x2 = x + o + bias (fp32, unrounded), y = LN(x2).
 hipError_t launch_add_ln_fwd(bool is_bf16, const void* x, const void* o, const void* bias, const void* gamma,

@@ -10,8 +10,8 @@ rounded to 8 significant bits, and a CPU model of exactly those roundings
 (tests/precision_model.py) shows that at the 175B shape the single rounding of the
 LayerNorm output feeding the QKV GEMM already puts the largest elementwise error of Out
 at 3.8% and of dX at 10% of their RMS (near-tied logits of the peaked causal softmax
-flip), while every normwise error stays below 1.6%. The literal max/RMS ratio is
-printed for every tensor.
+flip), while normwise errors stay small. The literal max/RMS ratio is printed for every
+tensor.
 """
 from __future__ import annotations
 

@@ -23,10 +23,14 @@ import numpy as np
 import seeded_inputs as si
 from oracle.layer import gelu, gelu_grad, layernorm_bwd, layernorm_fwd
 
-# Tensors the bf16 HIP path stores in bf16 (the residual stream X2 and its gradient dX2
-# are kept in fp32 and so are not listed).
-ROUNDED = frozenset({"u", "qkv", "p", "ctx", "o", "v2", "a", "z", "y", "out",
+# Rounding points of the bf16 HIP path. The residual stream X2 and its gradient dX2 are
+# fp32. U enters the QKV GEMM as U_hi + U_lo and Q, K enter the score GEMM as hi + lo
+# pairs, so neither is rounded there ("u_qkv", "qk_fwd" absent); the backward uses the
+# single bf16 U, Q, K ("u", "qk") and V is bf16 throughout ("v").
+ROUNDED = frozenset({"u", "qk", "v", "p", "ctx", "o", "v2", "a", "z", "y", "out",
                      "da", "dv2", "dx2_operand", "dctx", "ds", "dqkv", "du", "dx"})
+# A plain bf16 path: U rounded before the QKV GEMM and Q, K rounded before the scores.
+PLAIN_BF16 = ROUNDED | {"u_qkv", "qk_fwd"}
 
 
 def _rb(a) -> np.ndarray:
@@ -41,18 +45,25 @@ def layer(case: si.Case, rounded: Iterable[str]):
     B, s, d = sh.micro_batch, sh.seq, sh.head_dim
     p = {k: v.astype(np.float64) for k, v in case.layers[0].items()}
     x = case.x.astype(np.float64)
-    u, mu1, rs1 = layernorm_fwd(x, p["ln1_g"], p["ln1_b"])
-    u = r("u", u)
-    qkv = r("qkv", u @ p["w_qkv"].T + p["b_qkv"])
-    at = qkv.shape[1] // (3 * d)
+    u_exact, mu1, rs1 = layernorm_fwd(x, p["ln1_g"], p["ln1_b"])
+    u = r("u", u_exact)
+    qkv_exact = (u if "u_qkv" in R else u_exact) @ p["w_qkv"].T + p["b_qkv"]
+    at = qkv_exact.shape[1] // (3 * d)
     cols = lambda w, k: slice(w * at * d + k * d, w * at * d + (k + 1) * d)  # noqa: E731
+    qk_cols = slice(0, 2 * at * d)
+    v_cols = slice(2 * at * d, 3 * at * d)
+    qkv = qkv_exact.copy()                      # as used by the backward
+    qkv[:, qk_cols] = r("qk", qkv_exact[:, qk_cols])
+    qkv[:, v_cols] = r("v", qkv_exact[:, v_cols])
+    qkv_s = qkv_exact.copy()                    # as used by the score product
+    qkv_s[:, qk_cols] = r("qk_fwd", qkv_exact[:, qk_cols])
     ctx = np.zeros((B * s, at * d))
     P = np.zeros((B, at, s, s))
     vis = np.tril(np.ones((s, s), bool))
     for b in range(B):
         rows = slice(b * s, (b + 1) * s)
         for k in range(at):
-            S = np.where(vis, qkv[rows, cols(0, k)] @ qkv[rows, cols(1, k)].T / math.sqrt(d), -np.inf)
+            S = np.where(vis, qkv_s[rows, cols(0, k)] @ qkv_s[rows, cols(1, k)].T / math.sqrt(d), -np.inf)
             e = np.exp(S - S.max(1, keepdims=True))
             P[b, k] = r("p", e / e.sum(1, keepdims=True))
             ctx[rows, k * d:(k + 1) * d] = P[b, k] @ qkv[rows, cols(2, k)]
@@ -118,5 +129,5 @@ if __name__ == "__main__":
     case = si.workload_case(name)
     ref = layer(case, ())
     _print("bf16 HIP path rounding set", metrics(layer(case, ROUNDED), ref))
-    _print("only the QKV-GEMM operand U rounded", metrics(layer(case, {"u"}), ref))
-    _print("bf16 path with exact U and QKV", metrics(layer(case, ROUNDED - {"u", "qkv"}), ref))
+    _print("plain bf16 path (U and Q, K rounded before their products)", metrics(layer(case, PLAIN_BF16), ref))
+    _print("only the QKV-GEMM operand U rounded", metrics(layer(case, {"u_qkv"}), ref))

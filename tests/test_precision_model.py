@@ -3,7 +3,7 @@ import numpy as np
 
 import oracle
 import seeded_inputs as si
-from precision_model import ROUNDED, layer, metrics
+from precision_model import PLAIN_BF16, ROUNDED, layer, metrics
 
 
 def _case():
@@ -28,3 +28,11 @@ def test_bf16_rounding_stays_within_normwise_bar():
     for k, (rms_rel, _, max_rel) in m.items():
         assert rms_rel < 2e-2 and max_rel < 2e-2, (k, m[k])
     assert max(v[0] for v in m.values()) > 1e-4  # the roundings are really applied
+
+
+def test_compensated_qk_is_more_accurate_than_plain_bf16():
+    """The hi/lo treatment of U and Q, K lowers the error of the attention gradients."""
+    case = _case()
+    ref = layer(case, ())
+    ours, plain = metrics(layer(case, ROUNDED), ref), metrics(layer(case, PLAIN_BF16), ref)
+    assert ours["w_qkv"][0] < plain["w_qkv"][0] and ours["dx"][0] < plain["dx"][0]
