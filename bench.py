@@ -83,8 +83,9 @@ def copy_probe(nbytes: int) -> None:
     print(json.dumps({"copy_probe_bytes": nbytes}), flush=True)
 
 
-def cpu_baseline(case, shape):
-    """The fp64 oracle, as it stands, on one full step of the same workload."""
+def cpu_baseline(case, shape, min_seconds: float = 10.0, max_steps: int = 5):
+    """The fp64 oracle, as it stands, on whole steps of the same workload: repeated until
+    at least min_seconds of CPU work (at most max_steps steps)."""
     import numpy as np
     import oracle
     import seeded_inputs as si
@@ -94,14 +95,17 @@ def cpu_baseline(case, shape):
     except Exception:  # pragma: no cover - threadpoolctl missing
         threads = os.cpu_count() or 1
     t0 = time.perf_counter()
-    out, c = oracle.layer_fwd(case.x, case.layers[:1], shape.micro_batch, shape.seq, shape.head_dim)
-    dx, g = oracle.layer_bwd(case.dout, c, case.layers[:1])
+    steps = 0
+    while steps < max_steps and (steps == 0 or time.perf_counter() - t0 < min_seconds):
+        out, c = oracle.layer_fwd(case.x, case.layers[:1], shape.micro_batch, shape.seq, shape.head_dim)
+        dx, g = oracle.layer_bwd(case.dout, c, case.layers[:1])
+        del out, c, dx, g
+        steps += 1
     dt = time.perf_counter() - t0
-    del out, c, dx, g
-    flops = si.model_flops(shape)
+    flops = steps * si.model_flops(shape)
     return {"value": round(flops / dt / 1e12, 4), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"one full fwd+bwd step of {case.shape.h}-wide shard (M={shape.tokens}) in NumPy fp64, "
-                      f"{dt:.1f} s", "seconds": round(dt, 2)}
+            "sample": f"{steps} full fwd+bwd step(s) of the same shard (h={case.shape.h}, M={shape.tokens}) in "
+                      f"NumPy fp64, {dt:.1f} s", "seconds": round(dt, 2)}
 
 
 def main():
