@@ -40,7 +40,9 @@ constexpr int kCausalChunk = 256;
 
 // K segments (bf16 path): the contraction may run over nseg segments of K each, segment s
 // reading A from seg_a[s] and B from seg_b[s] with the strides of A and B (segment 0 is
-// A and B). Tiles whose first column is >= seg_n run segment 0 only. This forms
+// A and B). Tiles whose first column is >= seg_n run segment 0 only, and the later
+// segments read zeros for the B rows (output columns) >= seg_n of a tile that straddles
+// seg_n, so no column's arithmetic depends on the tile shape. This forms
 // hi/lo-compensated products, e.g. (U_hi + U_lo) W^T or Q_hi K_hi^T + Q_hi K_lo^T +
 // Q_lo K_hi^T, with bf16 MFMA operands.
 constexpr int kMaxSeg = 3;

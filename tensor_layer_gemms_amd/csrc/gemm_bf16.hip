@@ -1,6 +1,11 @@
-// bf16 MFMA GEMM launcher: picks a tile shape for the problem and the instantiation
-// for (operand layouts, epilogue).
-#include "gemm_kernels.hpp"
+// bf16 MFMA GEMM launcher: picks a kernel and tile shape for the problem and the
+// instantiation for (operand layouts, epilogue).
+//
+// The LDS-DMA kernel (gemm_dma.hpp) runs every problem whose operands it can address:
+// 16-byte aligned bases and strides, M, N, K multiples of 8, and every byte offset an
+// operand tile needs below 4 GiB (its buffer resource takes 32-bit offsets). Anything
+// else runs on the register-staged kernel (gemm_kernels.hpp).
+#include "gemm_dma.hpp"
 
 namespace mt {
 
@@ -9,25 +14,31 @@ namespace {
 constexpr int kNumCUs = 256;
 
 struct TileCfg {
-  int bm, bn, wm, wn;
-  float eff;  // relative per-tile throughput, measured on the layer's shapes
+  int bm, bn, per_cu;  // tile, work-groups resident per CU (LDS-limited)
+  float eff;           // relative throughput of a CU running per_cu such tiles
 };
-// Candidates per operand layout: forward (A, B k-contiguous), input gradient (B
-// n-contiguous), weight gradient (both token-strided).
-constexpr TileCfg kFwd[] = {{256, 256, 2, 4, 1.0f}, {128, 128, 2, 2, 0.85f}};
-constexpr TileCfg kDgrad[] = {{256, 128, 2, 4, 1.0f}, {256, 256, 2, 4, 0.95f}, {128, 128, 2, 2, 0.8f}};
-constexpr TileCfg kWgrad[] = {{256, 256, 2, 2, 1.0f}, {128, 256, 2, 2, 0.9f}, {128, 128, 2, 2, 0.8f}};
+// DMA kernel candidates. Both k-contiguous: 256x256 (8 waves), 256x192 (8 waves),
+// 128x128 (4 waves, two per CU). With an m-contiguous operand the tile side along it
+// must be a power of two: 256x256 or 128x128.
+constexpr TileCfg kDmaNT[] = {{256, 256, 1, 1.0f}, {256, 192, 1, 0.95f}, {128, 128, 2, 0.82f}};
+constexpr TileCfg kDmaT[] = {{256, 256, 1, 1.0f}, {128, 128, 2, 0.85f}};
+// Register-staged kernel candidates per operand layout.
+constexpr TileCfg kFwd[] = {{256, 256, 1, 1.0f}, {128, 128, 1, 0.85f}};
+constexpr TileCfg kDgrad[] = {{256, 128, 1, 1.0f}, {256, 256, 1, 0.95f}, {128, 128, 1, 0.8f}};
+constexpr TileCfg kWgrad[] = {{256, 256, 1, 1.0f}, {128, 256, 1, 0.9f}, {128, 128, 1, 0.8f}};
 
-// Pick the candidate with the least estimated time: whole waves of tiles over the CUs
-// times tile area over the candidate's throughput.
+// Pick the candidate with the least estimated time: whole rounds of tiles over the
+// resident slots, each round costing the tile area of one CU's tiles over the
+// candidate's throughput.
 template <int N>
 int pick(const TileCfg (&c)[N], const GemmArgs& g, int batch) {
   int best = 0;
   double best_cost = 1e300;
   for (int i = 0; i < N; ++i) {
     const long tiles = (long)((g.M + c[i].bm - 1) / c[i].bm) * ((g.N + c[i].bn - 1) / c[i].bn) * batch;
-    const long waves = (tiles + kNumCUs - 1) / kNumCUs;
-    const double cost = (double)waves * c[i].bm * c[i].bn / c[i].eff;
+    const long slots = (long)kNumCUs * c[i].per_cu;
+    const long rounds = (tiles + slots - 1) / slots;
+    const double cost = (double)rounds * c[i].bm * c[i].bn * c[i].per_cu / c[i].eff;
     if (cost < best_cost * 0.999) {
       best_cost = cost;
       best = i;
@@ -41,6 +52,14 @@ hipError_t run(const GemmArgs& g, int batch, hipStream_t s) {
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
   hipLaunchKernelGGL((gemm_bf16_kernel<AK, BK, BM, BN, WM, WN, KIND>), dim3(tiles, batch), dim3(64 * WM * WN), 0, s,
                      g);
+  return hipGetLastError();
+}
+
+template <bool AK, bool BK, int BM, int BN, int WM, int WN, int KIND>
+hipError_t run_dma(const GemmArgs& g, int batch, hipStream_t s) {
+  const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_dma_kernel<AK, BK, BM, BN, 64, 2, WM, WN, KIND>), dim3(tiles, batch), dim3(64 * WM * WN),
+                     0, s, g);
   return hipGetLastError();
 }
 
@@ -69,6 +88,44 @@ hipError_t run_tile(const GemmArgs& g, int batch, hipStream_t s) {
   }
 }
 
+template <bool AK, bool BK, int KIND>
+hipError_t run_dma_tile(const GemmArgs& g, int batch, hipStream_t s) {
+  if (g.causal != CAUSAL_NONE) return run_dma<AK, BK, 128, 128, 2, 2, KIND>(g, batch, s);
+  if constexpr (AK && BK) {
+    switch (pick(kDmaNT, g, batch)) {
+      case 0: return run_dma<AK, BK, 256, 256, 2, 4, KIND>(g, batch, s);
+      case 1: return run_dma<AK, BK, 256, 192, 4, 2, KIND>(g, batch, s);
+      default: return run_dma<AK, BK, 128, 128, 2, 2, KIND>(g, batch, s);
+    }
+  } else {
+    switch (pick(kDmaT, g, batch)) {
+      case 0: return run_dma<AK, BK, 256, 256, 2, 4, KIND>(g, batch, s);
+      default: return run_dma<AK, BK, 128, 128, 2, 2, KIND>(g, batch, s);
+    }
+  }
+}
+
+// Whether the DMA kernel can address the problem (see the file comment).
+bool dma_ok(const GemmArgs& g, bool a_k, bool b_k) {
+  auto a16 = [](const void* p) { return ((uintptr_t)p & 15u) == 0; };
+  if (g.M % 8 || g.N % 8 || g.K % 8 || g.lda % 8 || g.ldb % 8) return false;
+  if (g.a_so % 8 || g.a_si % 8 || g.b_so % 8 || g.b_si % 8) return false;
+  for (int s = 0; s < g.nseg; ++s)
+    if (!a16(g.seg_a[s]) || !a16(g.seg_b[s])) return false;
+  const uint64_t lim = 0xFFFFFFF0ull;
+  // largest byte offset from a tile's base: k-contiguous 256 rows of ld, m-contiguous
+  // K rows of ld
+  const uint64_t a_span = (uint64_t)(a_k ? 256 : g.K) * (uint64_t)g.lda * 2u;
+  const uint64_t b_span = (uint64_t)(b_k ? 256 : g.K) * (uint64_t)g.ldb * 2u;
+  return a_span < lim && b_span < lim;
+}
+
+template <bool AK, bool BK, int KIND>
+hipError_t dispatch(const GemmArgs& g, int batch, hipStream_t s) {
+  if (dma_ok(g, AK, BK)) return run_dma_tile<AK, BK, KIND>(g, batch, s);
+  return run_tile<AK, BK, KIND>(g, batch, s);
+}
+
 }  // namespace
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, bool a_k, bool b_k, int kind, int batch, hipStream_t s) {
@@ -77,22 +134,22 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, bool a_k, bool b_k, int kind, int
     return hipErrorInvalidValue;
   if (a_k && b_k) {  // forward products (X W^T, Q K^T, dctx V^T)
     switch (kind) {
-      case EPI_STORE: return run_tile<true, true, EPI_STORE>(g, batch, s);
-      case EPI_STORE_F32: return run_tile<true, true, EPI_STORE_F32>(g, batch, s);
-      case EPI_BIAS: return run_tile<true, true, EPI_BIAS>(g, batch, s);
-      case EPI_BIAS_SPLIT: return run_tile<true, true, EPI_BIAS_SPLIT>(g, batch, s);
-      case EPI_BIAS_GELU: return run_tile<true, true, EPI_BIAS_GELU>(g, batch, s);
-      case EPI_DSOFTMAX: return run_tile<true, true, EPI_DSOFTMAX>(g, batch, s);
+      case EPI_STORE: return dispatch<true, true, EPI_STORE>(g, batch, s);
+      case EPI_STORE_F32: return dispatch<true, true, EPI_STORE_F32>(g, batch, s);
+      case EPI_BIAS: return dispatch<true, true, EPI_BIAS>(g, batch, s);
+      case EPI_BIAS_SPLIT: return dispatch<true, true, EPI_BIAS_SPLIT>(g, batch, s);
+      case EPI_BIAS_GELU: return dispatch<true, true, EPI_BIAS_GELU>(g, batch, s);
+      case EPI_DSOFTMAX: return dispatch<true, true, EPI_DSOFTMAX>(g, batch, s);
     }
   } else if (a_k && !b_k) {  // input gradients (dY W), P V, dS K
     switch (kind) {
-      case EPI_STORE: return run_tile<true, false, EPI_STORE>(g, batch, s);
-      case EPI_DGELU: return run_tile<true, false, EPI_DGELU>(g, batch, s);
+      case EPI_STORE: return dispatch<true, false, EPI_STORE>(g, batch, s);
+      case EPI_DGELU: return dispatch<true, false, EPI_DGELU>(g, batch, s);
     }
   } else if (!a_k && !b_k) {  // weight gradients (dY^T X), P^T dC, dS^T Q
     switch (kind) {
-      case EPI_STORE: return run_tile<false, false, EPI_STORE>(g, batch, s);
-      case EPI_STORE_F32: return run_tile<false, false, EPI_STORE_F32>(g, batch, s);
+      case EPI_STORE: return dispatch<false, false, EPI_STORE>(g, batch, s);
+      case EPI_STORE_F32: return dispatch<false, false, EPI_STORE_F32>(g, batch, s);
     }
   }
   return hipErrorInvalidValue;

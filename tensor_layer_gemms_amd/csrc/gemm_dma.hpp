@@ -1,0 +1,247 @@
+// MFMA GEMM fed by LDS-DMA loads, for every operand layout of the layer.
+//
+// Each lane's 16-byte global load is written by the memory system straight into LDS
+// (buffer_load ... lds): no staging registers, no LDS store instructions, no register
+// transposes. A k-contiguous operand tile is kept in LDS as rows of k ([rows][BK]) and
+// read with ds_read_b128; an m-contiguous operand tile (token-strided wgrad operands,
+// the weight of a dgrad, V in P V) is kept as it lies in memory ([BK][rows]) and read
+// with the transposing ds_read_b64_tr_b16, which hands each lane 4 consecutive k of one
+// m. Out-of-range rows and the k tail read zeros through the buffer resource's range
+// check. An NS-deep ring of LDS stages keeps NS-1 stages of loads in flight while one
+// stage is multiplied.
+#pragma once
+
+#include "gemm_kernels.hpp"
+
+namespace mt {
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
+
+// s_waitcnt with vmcnt <= n and the other counters left alone (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// LDS placement of 16-byte chunks.
+// k-contiguous tile [rows][BK] (BK = 32 or 64): chunk c of row r sits at c ^ f(r); f
+// spreads the 16 rows one ds_read_b128 quarter-wave touches (same chunk) over the 64
+// banks.
+template <int BK>
+__device__ __forceinline__ int kc_swz(int row, int chunk) {
+  if constexpr (BK == 64) return chunk ^ ((row >> 1) & 7);
+  else return chunk ^ ((row >> 2) & 3);
+}
+// m-contiguous tile [BK][rows] (rows a power of two >= 128): chunk c of k-row r sits at
+// c ^ 4 (r & 3). A half-wave transposing read covers 4 consecutive k-rows x 32
+// consecutive m = 4 rows x 4 chunks; the XOR moves the 4 rows to 4 different 64-byte
+// bank groups.
+__device__ __forceinline__ int mc_swz(int krow, int chunk) { return chunk ^ ((krow & 3) << 2); }
+
+// DMA loads of one ROWS x BK operand tile (ROWS along m or n). The tile is 2 ROWS BK
+// bytes = ROWS BK / 512 wave instructions of 1 KB; wave w issues instructions w, w + NW,
+// ... Lane L of instruction q fills LDS bytes [q 1024 + 16 L, +16): LDS row
+// q RPI + L / CPR, stored chunk L % CPR, which holds the logical chunk the swizzle maps
+// there.
+template <int ROWS, int BK, int NW, bool KC>
+struct DmaLoader {
+  static constexpr int ROW_ELEMS = KC ? BK : ROWS;  // elements per LDS row
+  static constexpr int CPR = ROW_ELEMS / 8;          // 16-byte chunks per LDS row
+  static constexpr int RPI = 64 / CPR;               // LDS rows per wave instruction
+  static constexpr int INSTR = ROWS * BK / 512;      // instructions per tile
+  static constexpr int PER_WAVE = INSTR / NW;        // instructions per wave
+  static_assert(INSTR % NW == 0, "tile must split evenly over the waves");
+  static_assert(KC || (ROWS >= 128 && (ROWS & (ROWS - 1)) == 0), "m-contiguous tiles: power of two >= 128");
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t invalid;  // an offset at the end of the range: reads zeros
+  int64_t ld;
+  int rows_valid;
+
+  // KC: base = element (row0, 0), rows_valid rows left; the range ends after them.
+  // !KC: base = element (k = 0, row0); the range is the K x ld block; rows past
+  // rows_valid are masked per lane.
+  __device__ __forceinline__ void init(const bf16* base, int64_t ld_, int rows_valid_, int kdim) {
+    ld = ld_;
+    rows_valid = rows_valid_;
+    uint64_t bytes;
+    if constexpr (KC) bytes = rows_valid_ > 0 ? (uint64_t)rows_valid_ * (uint64_t)ld_ * 2u : 0u;
+    else bytes = (uint64_t)kdim * (uint64_t)ld_ * 2u;
+    invalid = bytes < 0xFFFFFFF0ull ? (uint32_t)bytes : 0xFFFFFFF0u;
+    rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base), (short)0, (int)invalid, 0x00020000);
+  }
+
+  __device__ __forceinline__ void issue(bf16* lds_stage, int k0, int kend, int wave, int lane) const {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int q = wave + i * NW;
+      const int r = q * RPI + lane / CPR;
+      const int p = lane % CPR;
+      uint32_t off;
+      if constexpr (KC) {
+        const int k = k0 + kc_swz<BK>(r, p) * 8;
+        off = k < kend ? (uint32_t)(r * ld + k) * 2u : invalid;
+      } else {
+        const int k = k0 + r, m = mc_swz(r, p) * 8;
+        off = (k < kend && m < rows_valid) ? (uint32_t)(k * ld + m) * 2u : invalid;
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(lds_stage + q * 512), 16, off, 0, 0, 0);
+    }
+  }
+};
+
+// Operand fragment reads for the 32x32x16 MFMA: lane l gets rows (l & 31) of the
+// 32-row block and k = 8 (l >> 5) + 0..7 of the 16-k step.
+template <int ROWS, int BK, bool KC>
+struct FragReader {
+  int off;  // per-lane element offset of the block at k-step 0
+  int row;  // KC: this lane's tile row
+  __device__ __forceinline__ void init(int row0, int lane) {
+    if constexpr (KC) {
+      row = row0 + (lane & 31);
+      off = row * BK;
+    } else {
+      // Transposing read: within a 16-lane group, lane L addresses 4 consecutive m at
+      // k-row (L >> 2), m offset 4 (L & 3); lane j of the group then receives the
+      // 4 k-rows of m offset j. Two reads (k-rows 0..3 and 4..7) give the 8 k.
+      const int kr = 8 * (lane >> 5) + ((lane >> 2) & 3);
+      const int m = row0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      off = kr * ROWS + (mc_swz(kr, m >> 3) << 3) + (m & 7);
+    }
+  }
+  __device__ __forceinline__ bf16x8 read(const bf16* tile, int ks, int lane) const {
+    if constexpr (KC) {
+      return *reinterpret_cast<const bf16x8*>(tile + off + (kc_swz<BK>(row, 2 * ks + (lane >> 5)) << 3));
+    } else {
+      const bf16* p = tile + off + ks * 16 * ROWS;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(p));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(p + 4 * ROWS));
+      const auto v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      return __builtin_bit_cast(bf16x8, v);
+    }
+  }
+};
+
+template <bool A_K, bool B_K, int BM, int BN, int BK, int NS, int WM, int WN, int KIND>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs g) {
+  constexpr int NW = WM * WN;
+  constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
+  constexpr int STAGE = (BM + BN) * BK;  // bf16 elements per stage
+  static_assert(TM >= 1 && TN >= 1 && BM % (WM * 32) == 0 && BN % (WN * 32) == 0, "wave tile of 32x32 blocks");
+  __shared__ __attribute__((aligned(1024))) bf16 smem[NS * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm0 = (wave / WN) * (BM / WM), wn0 = (wave % WN) * (BN / WN);
+  const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+  int tm, tn;
+  map_tile<4>(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  if (g.causal == CAUSAL_SKIP_UPPER && n0 > m0 + BM - 1) return;
+  int kbeg, kend;
+  causal_k_range(g, m0, BM, kbeg, kend);
+  const int z = blockIdx.y, zo = z / g.zdiv, zi = z % g.zdiv;
+  const int64_t aoff = zo * g.a_so + zi * g.a_si + (A_K ? (int64_t)m0 * g.lda : (int64_t)m0);
+  const int64_t boff = zo * g.b_so + zi * g.b_si + (B_K ? (int64_t)n0 * g.ldb : (int64_t)n0);
+  const int nseg = n0 < g.seg_n ? g.nseg : 1;
+
+  DmaLoader<BM, BK, NW, A_K> la[kMaxSeg];
+  DmaLoader<BN, BK, NW, B_K> lb[kMaxSeg];
+#pragma unroll
+  for (int s = 0; s < kMaxSeg; ++s) {
+    if (s < nseg) {
+      la[s].init(static_cast<const bf16*>(g.seg_a[s]) + aoff, g.lda, g.M - m0, g.K);
+      lb[s].init(static_cast<const bf16*>(g.seg_b[s]) + boff, g.ldb, (s ? min(g.N, g.seg_n) : g.N) - n0, g.K);
+    }
+  }
+  FragReader<BM, BK, A_K> ra[TM];
+  FragReader<BN, BK, B_K> rb[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) ra[i].init(wm0 + i * 32, lane);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) rb[j].init(wn0 + j * 32, lane);
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk1 = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+  const int nk = nk1 * nseg;
+  auto issue = [&](int t) {  // loads of step t into stage t % NS
+    const int sg = (t >= nk1) + (t >= 2 * nk1);
+    const int k0 = kbeg + (t - sg * nk1) * BK;
+    bf16* st = smem + (t % NS) * STAGE;
+    if (sg == 0) {
+      la[0].issue(st, k0, kend, wave, lane);
+      lb[0].issue(st + BM * BK, k0, kend, wave, lane);
+    } else if (sg == 1) {
+      la[1].issue(st, k0, kend, wave, lane);
+      lb[1].issue(st + BM * BK, k0, kend, wave, lane);
+    } else {
+      la[2].issue(st, k0, kend, wave, lane);
+      lb[2].issue(st + BM * BK, k0, kend, wave, lane);
+    }
+  };
+  constexpr int LOADS = DmaLoader<BM, BK, NW, A_K>::PER_WAVE + DmaLoader<BN, BK, NW, B_K>::PER_WAVE;
+
+  if (nk > 0) {
+#pragma unroll
+    for (int p = 0; p < NS - 1; ++p)
+      if (p < nk) issue(p);
+    for (int t = 0; t < nk; ++t) {
+      // This wave's loads of step t are complete when at most the loads of the steps
+      // after it (up to NS-2 of them) are outstanding; the barrier makes every wave's
+      // loads visible and frees the stage multiplied in step t-1 for reuse.
+      if (nk - 1 - t >= NS - 2) wait_vmcnt<(NS - 2) * LOADS>();
+      else wait_vmcnt<0>();
+      __syncthreads();
+      if (t + NS - 1 < nk) issue(t + NS - 1);
+      const bf16* sA = smem + (t % NS) * STAGE;
+      const bf16* sB = sA + BM * BK;
+      bf16x8 af[2][TM], bfr[2][TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[0][i] = ra[i].read(sA, 0, lane);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bfr[0][j] = rb[j].read(sB, 0, lane);
+#pragma unroll
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        const int cb = ks & 1, nb = cb ^ 1;
+        if (ks + 1 < BK / 16) {
+#pragma unroll
+          for (int i = 0; i < TM; ++i) af[nb][i] = ra[i].read(sA, ks + 1, lane);
+#pragma unroll
+          for (int j = 0; j < TN; ++j) bfr[nb][j] = rb[j].read(sB, ks + 1, lane);
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cb][j], af[cb][i], acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+
+  const int64_t coff = zo * g.c_so + zi * g.c_si;
+  const int64_t voff = (int64_t)z * g.vec_bs;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int m = m0 + wm0 + i * 32 + (lane & 31);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn0 + j * 32 + q * 8 + (lane >> 5) * 4;
+        float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        if (m < g.M && n < g.N) epi_store4<KIND>(g, coff, voff, m, n, v);
+      }
+    }
+  }
+}
+
+}  // namespace mt

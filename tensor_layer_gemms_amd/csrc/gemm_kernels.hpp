@@ -258,7 +258,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
     const int sg = (t >= nk1) + (t >= 2 * nk1);
     const int k0 = kbeg + (t - sg * nk1) * BK;
     la.load(static_cast<const bf16*>(g.seg_a[sg]) + aoff, g.lda, m0, g.M, k0, kend, tid);
-    lb.load(static_cast<const bf16*>(g.seg_b[sg]) + boff, g.ldb, n0, g.N, k0, kend, tid);
+    lb.load(static_cast<const bf16*>(g.seg_b[sg]) + boff, g.ldb, n0, sg ? min(g.N, g.seg_n) : g.N, k0, kend, tid);
   };
   // Three-stage pipeline: LDS buffer t & 1 holds the tile being multiplied, the other
   // buffer receives tile t + 1 (loaded into registers during step t - 1), and the

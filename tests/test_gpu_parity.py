@@ -183,7 +183,10 @@ def test_stage_h8192_micro_batch_sampled(mb):
     sequence 0's inputs are the same seeded rows at every micro-batch size, so the rows
     of sequence 0 of Out and dX must match the micro-batch-1 oracle. Weight gradients
     are sums over sequences: those of the mb-sequence batch must equal the sum of the
-    per-sequence runs (linearity, checked on the GPU path itself)."""
+    per-sequence runs (linearity, checked on the GPU path itself). Every per-token value
+    of the path is computed with the same arithmetic at any micro-batch (no tile choice
+    changes an element's accumulation order or operands), so the two sides differ only
+    in the fp32 summation order over tokens: the bar is the fp32 one."""
     from gpu_support import compare
     w = si.WORKLOADS[f"gpt_h8192_stage_mb{mb}"]
     case = si.workload_case(f"gpt_h8192_stage_mb{mb}")
@@ -200,4 +203,4 @@ def test_stage_h8192_micro_batch_sampled(mb):
         total = gb if total is None else [{k: t[k] + g[k] for k in t} for t, g in zip(total, gb)]
     for l in range(w.layers):
         for k in ("w_qkv", "w_fc1", "b_o", "ln1_g"):
-            assert compare(f"l{l}.{k} sum", grads[l][k], total[l][k], TOL["bf16"], True)[0]
+            assert compare(f"l{l}.{k} sum", grads[l][k], total[l][k], TOL["fp32"], True)[0]
