@@ -5,6 +5,8 @@
 // 16-byte aligned bases and strides, M, N, K multiples of 8, and every byte offset an
 // operand tile needs below 4 GiB (its buffer resource takes 32-bit offsets). Anything
 // else runs on the register-staged kernel (gemm_kernels.hpp).
+#include <algorithm>
+
 #include "gemm_dma.hpp"
 
 namespace mt {
@@ -126,7 +128,48 @@ hipError_t dispatch(const GemmArgs& g, int batch, hipStream_t s) {
   return run_tile<AK, BK, KIND>(g, batch, s);
 }
 
+// Paired launch with tile config (BM, BN, WM, WN) for both problems.
+template <int BM, int BN, int WM, int WN, int KIND0>
+hipError_t run_pair(const GemmArgs& g0, const GemmArgs& g1, hipStream_t s) {
+  const int t0 = ((g0.M + BM - 1) / BM) * ((g0.N + BN - 1) / BN);
+  const int t1 = ((g1.M + BM - 1) / BM) * ((g1.N + BN - 1) / BN);
+  const int first = g1.K > g0.K ? 1 : 0;  // deeper contraction first
+  typedef DmaProblem<true, false, BM, BN, WM, WN, KIND0> P0;
+  typedef DmaProblem<false, false, BM, BN, WM, WN, EPI_STORE_F32> P1;
+  hipLaunchKernelGGL((gemm_dma_pair_kernel<P0, P1>), dim3(t0 + t1), dim3(64 * WM * WN), 0, s, g0, g1, first,
+                     first ? t1 : t0);
+  return hipGetLastError();
+}
+
+// Estimated time of a paired launch: the larger of the mean work per resident slot and
+// the deepest single tile, in tile-k-steps, times the CU's share of tile area over the
+// candidate's throughput.
+double pair_cost(const TileCfg& c, const GemmArgs& g0, const GemmArgs& g1) {
+  auto tiles = [&](const GemmArgs& g) { return (double)((g.M + c.bm - 1) / c.bm) * ((g.N + c.bn - 1) / c.bn); };
+  const double s0 = (g0.K + 63) / 64, s1 = (g1.K + 63) / 64;
+  const double slots = (double)kNumCUs * c.per_cu;
+  const double t = std::max((tiles(g0) * s0 + tiles(g1) * s1) / slots, std::max(s0, s1));
+  return t * c.bm * c.bn * c.per_cu / c.eff;
+}
+
+template <int KIND0>
+hipError_t pair_dispatch(const GemmArgs& g0, const GemmArgs& g1, hipStream_t s) {
+  if (pair_cost(kDmaT[0], g0, g1) <= pair_cost(kDmaT[1], g0, g1))
+    return run_pair<256, 256, 2, 4, KIND0>(g0, g1, s);
+  return run_pair<128, 128, 2, 2, KIND0>(g0, g1, s);
+}
+
 }  // namespace
+
+hipError_t launch_gemm_bf16_pair(const GemmArgs& g0, bool a_k0, bool b_k0, int kind0, const GemmArgs& g1, bool a_k1,
+                                 bool b_k1, int kind1, hipStream_t s) {
+  if (!(a_k0 && !b_k0 && !a_k1 && !b_k1 && kind1 == EPI_STORE_F32)) return hipErrorNotSupported;
+  if (kind0 != EPI_STORE && kind0 != EPI_DGELU) return hipErrorNotSupported;
+  for (const GemmArgs* g : {&g0, &g1})
+    if (g->causal != CAUSAL_NONE || g->nseg != 1 || g->M <= 0 || g->N <= 0) return hipErrorNotSupported;
+  if (!dma_ok(g0, true, false) || !dma_ok(g1, false, false)) return hipErrorNotSupported;
+  return kind0 == EPI_DGELU ? pair_dispatch<EPI_DGELU>(g0, g1, s) : pair_dispatch<EPI_STORE>(g0, g1, s);
+}
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, bool a_k, bool b_k, int kind, int batch, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0 || batch <= 0) return hipSuccess;

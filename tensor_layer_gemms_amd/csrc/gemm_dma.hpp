@@ -125,24 +125,25 @@ struct FragReader {
   }
 };
 
+// One output tile: bid = tile index of the problem, z = batch index, smem = the
+// launch's LDS ring (at least NS (BM + BN) BK elements).
 template <bool A_K, bool B_K, int BM, int BN, int BK, int NS, int WM, int WN, int KIND>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs g) {
+__device__ __forceinline__ void gemm_dma_tile(const GemmArgs& g, int bid, int z, bf16* smem) {
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
   constexpr int STAGE = (BM + BN) * BK;  // bf16 elements per stage
   static_assert(TM >= 1 && TN >= 1 && BM % (WM * 32) == 0 && BN % (WN * 32) == 0, "wave tile of 32x32 blocks");
-  __shared__ __attribute__((aligned(1024))) bf16 smem[NS * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm0 = (wave / WN) * (BM / WM), wn0 = (wave % WN) * (BN / WN);
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
   int tm, tn;
-  map_tile<4>(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  map_tile<4>(bid, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   if (g.causal == CAUSAL_SKIP_UPPER && n0 > m0 + BM - 1) return;
   int kbeg, kend;
   causal_k_range(g, m0, BM, kbeg, kend);
-  const int z = blockIdx.y, zo = z / g.zdiv, zi = z % g.zdiv;
+  const int zo = z / g.zdiv, zi = z % g.zdiv;
   const int64_t aoff = zo * g.a_so + zi * g.a_si + (A_K ? (int64_t)m0 * g.lda : (int64_t)m0);
   const int64_t boff = zo * g.b_so + zi * g.b_si + (B_K ? (int64_t)n0 * g.ldb : (int64_t)n0);
   const int nseg = n0 < g.seg_n ? g.nseg : 1;
@@ -242,6 +243,37 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs g) {
       }
     }
   }
+}
+
+template <bool A_K, bool B_K, int BM, int BN, int BK, int NS, int WM, int WN, int KIND>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) bf16 smem[NS * (BM + BN) * BK];
+  gemm_dma_tile<A_K, B_K, BM, BN, BK, NS, WM, WN, KIND>(g, blockIdx.x, blockIdx.y, smem);
+}
+
+// Compile-time description of one problem of a paired launch.
+template <bool A_K, bool B_K, int BM, int BN, int WM, int WN, int KIND>
+struct DmaProblem {
+  static constexpr int kBM = BM, kBN = BN, kThreads = 64 * WM * WN, kSmem = 2 * (BM + BN) * 64;
+  static __device__ __forceinline__ void tile(const GemmArgs& g, int bid, bf16* smem) {
+    gemm_dma_tile<A_K, B_K, BM, BN, 64, 2, WM, WN, KIND>(g, bid, 0, smem);
+  }
+};
+
+// Two independent, unbatched problems in one launch. Blocks [0, tiles_first) run the
+// problem named by `first` (0 or 1), the remaining blocks the other one, so the second
+// problem's tiles fill the CUs the first one leaves idle.
+template <class P0, class P1>
+__global__ __launch_bounds__(P0::kThreads) void gemm_dma_pair_kernel(GemmArgs g0, GemmArgs g1, int first,
+                                                                      int tiles_first) {
+  static_assert(P0::kThreads == P1::kThreads, "paired problems share the work-group size");
+  constexpr int SMEM = P0::kSmem > P1::kSmem ? P0::kSmem : P1::kSmem;
+  __shared__ __attribute__((aligned(1024))) bf16 smem[SMEM];
+  const int bid = blockIdx.x;
+  const bool in_first = bid < tiles_first;
+  const int local = in_first ? bid : bid - tiles_first;
+  if (in_first == (first == 0)) P0::tile(g0, local, smem);
+  else P1::tile(g1, local, smem);
 }
 
 }  // namespace mt

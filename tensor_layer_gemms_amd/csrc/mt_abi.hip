@@ -243,6 +243,19 @@ hipError_t gemm(const Dims& d, const GemmArgs& g, bool a_k, bool b_k, int kind, 
   return d.bf16 ? launch_gemm_bf16(g, a_k, b_k, kind, batch, s) : launch_gemm_f32(g, a_k, b_k, kind, batch, s);
 }
 
+// Input gradient dg (A k-contiguous, B n-contiguous; epilogue dkind) and weight
+// gradient wg (both operands token-strided, fp32 out) of one linear layer: one paired
+// launch where the bf16 path supports it, else the two one after the other.
+hipError_t gemm_dgrad_wgrad(const Dims& d, const GemmArgs& dg, int dkind, const GemmArgs& wg, hipStream_t s) {
+  if (d.bf16) {
+    const hipError_t e = launch_gemm_bf16_pair(dg, true, false, dkind, wg, false, false, EPI_STORE_F32, s);
+    if (e != hipErrorNotSupported) return e;
+  }
+  const hipError_t e = gemm(d, wg, false, false, EPI_STORE_F32, 1, s);
+  if (e != hipSuccess) return e;
+  return gemm(d, dg, true, false, dkind, 1, s);
+}
+
 double gflop(double m, double n, double k) { return 2.0 * m * n * k; }
 
 // Per-head attention products over (b, k) pairs: batch z = b * at + k.
@@ -371,27 +384,21 @@ int layer_bwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, cons
     return launch_colsum(bf, 0, dout, false, nullptr, false, nullptr, nullptr, gr.b_fc2, nullptr, ws.part, M,
                          (int)d.h, stream);
   });
-  q.run("fc2_wgrad", gflop(d.h, d.ft, d.M), 0, [&] {
-    GemmArgs g = plain(dout, d.h, sv.z, d.ft, gr.w_fc2, d.ft, d.h, d.ft, d.M);
-    return gemm(d, g, false, false, EPI_STORE_F32, 1, stream);
-  });
-  q.run("fc2_dgrad", gflop(d.M, d.ft, d.h), 0, [&] {
-    GemmArgs g = plain(dout, d.h, w.w_fc2, d.ft, ws.da, d.ft, d.M, d.ft, d.h);
-    g.aux = sv.a;
-    return gemm(d, g, true, false, EPI_DGELU, 1, stream);
+  q.run("fc2_dgrad_wgrad", 2 * gflop(d.M, d.ft, d.h), 0, [&] {
+    GemmArgs dg = plain(dout, d.h, w.w_fc2, d.ft, ws.da, d.ft, d.M, d.ft, d.h);
+    dg.aux = sv.a;
+    const GemmArgs wg = plain(dout, d.h, sv.z, d.ft, gr.w_fc2, d.ft, d.h, d.ft, d.M);
+    return gemm_dgrad_wgrad(d, dg, EPI_DGELU, wg, stream);
   });
   // B2 FC1: db_fc1, dW1 = dA^T V2, dV2 = dA W1 (partial)
   q.run("db_fc1", 0, d.M * d.ft * es, [&] {
     return launch_colsum(bf, 0, ws.da, false, nullptr, false, nullptr, nullptr, gr.b_fc1, nullptr, ws.part, M,
                          (int)d.ft, stream);
   });
-  q.run("fc1_wgrad", gflop(d.ft, d.h, d.M), 0, [&] {
-    GemmArgs g = plain(ws.da, d.ft, sv.v2, d.h, gr.w_fc1, d.h, d.ft, d.h, d.M);
-    return gemm(d, g, false, false, EPI_STORE_F32, 1, stream);
-  });
-  q.run("fc1_dgrad", gflop(d.M, d.h, d.ft), 0, [&] {
-    GemmArgs g = plain(ws.da, d.ft, w.w_fc1, d.h, ws.dv2, d.h, d.M, d.h, d.ft);
-    return gemm(d, g, true, false, EPI_STORE, 1, stream);
+  q.run("fc1_dgrad_wgrad", 2 * gflop(d.M, d.h, d.ft), 0, [&] {
+    const GemmArgs dg = plain(ws.da, d.ft, w.w_fc1, d.h, ws.dv2, d.h, d.M, d.h, d.ft);
+    const GemmArgs wg = plain(ws.da, d.ft, sv.v2, d.h, gr.w_fc1, d.h, d.ft, d.h, d.M);
+    return gemm_dgrad_wgrad(d, dg, EPI_STORE, wg, stream);
   });
   // B3 dX2 = dOut + LN2-backward(AR(dV2)) (written as the GEMM operand and as an fp32
   // copy for the residual path); dgamma2, dbeta2; db_o = colsum(dX2)
@@ -408,13 +415,10 @@ int layer_bwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, cons
                          (int)d.h, stream);
   });
   // B4 out-projection: dW_o = dX2^T ctx, dctx = dX2 W_o
-  q.run("out_proj_wgrad", gflop(d.h, d.hs, d.M), 0, [&] {
-    GemmArgs g = plain(ws.dx2, d.h, sv.ctx, d.hs, gr.w_o, d.hs, d.h, d.hs, d.M);
-    return gemm(d, g, false, false, EPI_STORE_F32, 1, stream);
-  });
-  q.run("out_proj_dgrad", gflop(d.M, d.hs, d.h), 0, [&] {
-    GemmArgs g = plain(ws.dx2, d.h, w.w_o, d.hs, ws.dctx, d.hs, d.M, d.hs, d.h);
-    return gemm(d, g, true, false, EPI_STORE, 1, stream);
+  q.run("out_proj_dgrad_wgrad", 2 * gflop(d.M, d.hs, d.h), 0, [&] {
+    const GemmArgs dg = plain(ws.dx2, d.h, w.w_o, d.hs, ws.dctx, d.hs, d.M, d.hs, d.h);
+    const GemmArgs wg = plain(ws.dx2, d.h, sv.ctx, d.hs, gr.w_o, d.hs, d.h, d.hs, d.M);
+    return gemm_dgrad_wgrad(d, dg, EPI_STORE, wg, stream);
   });
   // B5/B6 attention: D = rowsum(dctx * ctx) = rowsum(P * dP); dS = P * (dctx V^T - D)
   q.run("attn_rowdot", 0, 2.0 * d.M * d.hs * es, [&] {
@@ -472,13 +476,10 @@ int layer_bwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, cons
     return launch_colsum(bf, 0, ws.dqkv, false, nullptr, false, nullptr, nullptr, gr.b_qkv, nullptr, ws.part, M,
                          (int)d.qkv, stream);
   });
-  q.run("qkv_wgrad", gflop(d.qkv, d.h, d.M), 0, [&] {
-    GemmArgs g = plain(ws.dqkv, d.qkv, sv.u, d.h, gr.w_qkv, d.h, d.qkv, d.h, d.M);
-    return gemm(d, g, false, false, EPI_STORE_F32, 1, stream);
-  });
-  q.run("qkv_dgrad", gflop(d.M, d.h, d.qkv), 0, [&] {
-    GemmArgs g = plain(ws.dqkv, d.qkv, w.w_qkv, d.h, ws.dv2, d.h, d.M, d.h, d.qkv);
-    return gemm(d, g, true, false, EPI_STORE, 1, stream);
+  q.run("qkv_dgrad_wgrad", 2 * gflop(d.M, d.h, d.qkv), 0, [&] {
+    const GemmArgs dg = plain(ws.dqkv, d.qkv, w.w_qkv, d.h, ws.dv2, d.h, d.M, d.h, d.qkv);
+    const GemmArgs wg = plain(ws.dqkv, d.qkv, sv.u, d.h, gr.w_qkv, d.h, d.qkv, d.h, d.M);
+    return gemm_dgrad_wgrad(d, dg, EPI_STORE, wg, stream);
   });
   // B8 dX = dX2 + LN1-backward(AR(dU)); dgamma1, dbeta1
   q.run("ln1_bwd", 0, Mh * (3 * es + 4), [&] {
@@ -512,26 +513,20 @@ int mlp_fwd_impl(const Dims& d, const void* x, const void* w1, const void* b1, c
 int mlp_bwd_impl(const Dims& d, const void* x, const void* w1, const void* w2, const MlpSaved& sv, const void* dy,
                  void* dx, float* dw1, float* db1, float* dw2, const MlpWs& ws, hipStream_t stream) {
   Seq q(stream);
-  q.run("fc2_wgrad", gflop(d.h, d.ft, d.M), 0, [&] {
-    GemmArgs g = plain(dy, d.h, sv.z, d.ft, dw2, d.ft, d.h, d.ft, d.M);
-    return gemm(d, g, false, false, EPI_STORE_F32, 1, stream);
-  });
-  q.run("fc2_dgrad", gflop(d.M, d.ft, d.h), 0, [&] {
-    GemmArgs g = plain(dy, d.h, w2, d.ft, ws.da, d.ft, d.M, d.ft, d.h);
-    g.aux = sv.a;
-    return gemm(d, g, true, false, EPI_DGELU, 1, stream);
+  q.run("fc2_dgrad_wgrad", 2 * gflop(d.M, d.ft, d.h), 0, [&] {
+    GemmArgs dg = plain(dy, d.h, w2, d.ft, ws.da, d.ft, d.M, d.ft, d.h);
+    dg.aux = sv.a;
+    const GemmArgs wg = plain(dy, d.h, sv.z, d.ft, dw2, d.ft, d.h, d.ft, d.M);
+    return gemm_dgrad_wgrad(d, dg, EPI_DGELU, wg, stream);
   });
   q.run("db_fc1", 0, (double)d.M * d.ft * d.es, [&] {
     return launch_colsum(d.bf16, 0, ws.da, false, nullptr, false, nullptr, nullptr, db1, nullptr, ws.part, (int)d.M,
                          (int)d.ft, stream);
   });
-  q.run("fc1_wgrad", gflop(d.ft, d.h, d.M), 0, [&] {
-    GemmArgs g = plain(ws.da, d.ft, x, d.h, dw1, d.h, d.ft, d.h, d.M);
-    return gemm(d, g, false, false, EPI_STORE_F32, 1, stream);
-  });
-  q.run("fc1_dgrad", gflop(d.M, d.h, d.ft), 0, [&] {
-    GemmArgs g = plain(ws.da, d.ft, w1, d.h, dx, d.h, d.M, d.h, d.ft);
-    return gemm(d, g, true, false, EPI_STORE, 1, stream);
+  q.run("fc1_dgrad_wgrad", 2 * gflop(d.M, d.h, d.ft), 0, [&] {
+    const GemmArgs dg = plain(ws.da, d.ft, w1, d.h, dx, d.h, d.M, d.h, d.ft);
+    const GemmArgs wg = plain(ws.da, d.ft, x, d.h, dw1, d.h, d.ft, d.h, d.M);
+    return gemm_dgrad_wgrad(d, dg, EPI_STORE, wg, stream);
   });
   return q.status();
 }

@@ -157,6 +157,7 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(const TA* __restric
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[k][e] = 0.f;
   if (chunk < nch) {
+#pragma unroll 4
     for (int r = r0 + rl; r < r1; r += 4) {
       const int64_t off = (int64_t)r * cols + (int64_t)chunk * 8;
       float av[8];
@@ -192,18 +193,36 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(const TA* __restric
   }
 }
 
-// Stage 2: sum the row-slab partials in slab order.
+// Stage 2: sum the row-slab partials. Block: 64 columns x 4 slab groups; group g sums
+// slabs g, g + 4, ... in four interleaved chains (independent loads in flight), then the
+// groups are added in a fixed order. The order depends on the geometry only.
 __global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restrict__ part, float* __restrict__ out0,
                                                            float* __restrict__ out1, int nrb, int cols, int mode) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= cols) return;
-  float s = 0.f;
-  for (int b = 0; b < nrb; ++b) s += part[(int64_t)b * cols + c];
-  out0[c] = s;
-  if (mode == 1) {
-    float t = 0.f;
-    for (int b = 0; b < nrb; ++b) t += part[((int64_t)nrb + b) * cols + c];
-    out1[c] = t;
+  __shared__ float red[2][4][64];
+  const int lane = threadIdx.x & 63, grp = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + lane;
+  float s[2] = {0.f, 0.f};
+  if (c < cols) {
+    for (int k = 0; k < (mode == 1 ? 2 : 1); ++k) {
+      const float* p = part + (int64_t)k * nrb * cols + c;
+      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+      int b = grp;
+      for (; b + 12 < nrb; b += 16) {
+        a0 += p[(int64_t)b * cols];
+        a1 += p[(int64_t)(b + 4) * cols];
+        a2 += p[(int64_t)(b + 8) * cols];
+        a3 += p[(int64_t)(b + 12) * cols];
+      }
+      for (; b < nrb; b += 4) a0 += p[(int64_t)b * cols];
+      s[k] = (a0 + a1) + (a2 + a3);
+    }
+  }
+  red[0][grp][lane] = s[0];
+  red[1][grp][lane] = s[1];
+  __syncthreads();
+  if (grp == 0 && c < cols) {
+    out0[c] = (red[0][0][lane] + red[0][1][lane]) + (red[0][2][lane] + red[0][3][lane]);
+    if (mode == 1) out1[c] = (red[1][0][lane] + red[1][1][lane]) + (red[1][2][lane] + red[1][3][lane]);
   }
 }
 
@@ -385,7 +404,7 @@ hipError_t colsum_t(int mode, const void* a, const void* x, const float* mean, c
                        (const TX*)x, mean, rstd, partial, rows, cols, rpb, nrb);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(colsum_final_kernel, dim3((cols + 255) / 256), dim3(256), 0, s, partial, out0, out1, nrb, cols,
+  hipLaunchKernelGGL(colsum_final_kernel, dim3((cols + 63) / 64), dim3(256), 0, s, partial, out0, out1, nrb, cols,
                      mode);
   return hipGetLastError();
 }
