@@ -27,8 +27,9 @@ METRIC = "model TFLOP/s per GPU, GPT layer-shard fwd+bwd; % of bf16 MFMA peak"
 # HBM traffic of the dominant kernel, measured with rocprofv3 counters and committed as a
 # summary; it is reported only while the GEMM sources hash to the value recorded there.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fc1_fwd_gpt175b_tp8_traffic.txt")
-GEMM_SOURCES = ["tensor_layer_gemms_amd/csrc/gemm_kernels.hpp", "tensor_layer_gemms_amd/csrc/gemm_bf16.hip",
-                "tensor_layer_gemms_amd/csrc/gemm.hpp", "tensor_layer_gemms_amd/csrc/device_common.hpp"]
+GEMM_SOURCES = ["tensor_layer_gemms_amd/csrc/gemm_dma.hpp", "tensor_layer_gemms_amd/csrc/gemm_kernels.hpp",
+                "tensor_layer_gemms_amd/csrc/gemm_bf16.hip", "tensor_layer_gemms_amd/csrc/gemm.hpp",
+                "tensor_layer_gemms_amd/csrc/device_common.hpp"]
 
 
 def gemm_source_hash() -> str:

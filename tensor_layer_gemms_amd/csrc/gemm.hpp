@@ -73,10 +73,11 @@ hipError_t launch_gemm_f32(const GemmArgs& g, bool a_kcontig, bool b_kcontig, in
                            hipStream_t stream);
 // Two independent unbatched, non-causal bf16 problems in one launch (an input gradient
 // and a weight gradient of the same layer): the tiles of the deeper contraction first,
-// then the other problem's, which fill the CUs the first leaves idle. Supported pairs:
-// (A k-contiguous, B n-contiguous; EPI_STORE or EPI_DGELU) with (both token-strided;
-// EPI_STORE_F32), each addressable by the DMA kernel. Returns hipErrorNotSupported for
-// anything else, without launching; the caller then runs the two one after the other.
+// then the other problem's, which fill the CUs the first leaves idle. Supported pairs,
+// each problem addressable by the DMA kernel: (A k-contiguous, B n-contiguous; EPI_STORE
+// or EPI_DGELU) with (both token-strided; EPI_STORE_F32), and two both-k-contiguous
+// EPI_STORE_F32 problems. Returns hipErrorNotSupported for anything else, without
+// launching; the caller then runs the two one after the other.
 hipError_t launch_gemm_bf16_pair(const GemmArgs& g0, bool a_k0, bool b_k0, int kind0, const GemmArgs& g1, bool a_k1,
                                  bool b_k1, int kind1, hipStream_t stream);
 

@@ -16,12 +16,13 @@ namespace {
 constexpr int kNumCUs = 256;
 
 struct TileCfg {
-  int bm, bn, per_cu;  // tile, work-groups resident per CU (LDS-limited)
+  int bm, bn, per_cu;  // tile, work-groups resident per CU (LDS- or register-limited)
   float eff;           // relative throughput of a CU running per_cu such tiles
 };
-// DMA kernel candidates. Both k-contiguous: 256x256 (8 waves), 256x192 (8 waves),
-// 128x128 (4 waves, two per CU). With an m-contiguous operand the tile side along it
-// must be a power of two: 256x256 or 128x128.
+// DMA kernel candidates (k-step 64; measured on the layer's shapes). Both k-contiguous:
+// 256x256 (8 waves), 256x192 (8 waves), 128x128 (4 waves, two per CU). With an
+// m-contiguous operand the tile side along it must be a power of two: 256x256 or
+// 128x128.
 constexpr TileCfg kDmaNT[] = {{256, 256, 1, 1.0f}, {256, 192, 1, 0.95f}, {128, 128, 2, 0.82f}};
 constexpr TileCfg kDmaT[] = {{256, 256, 1, 1.0f}, {128, 128, 2, 0.85f}};
 // Register-staged kernel candidates per operand layout.
@@ -57,10 +58,10 @@ hipError_t run(const GemmArgs& g, int batch, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <bool AK, bool BK, int BM, int BN, int WM, int WN, int KIND>
+template <bool AK, bool BK, int BM, int BN, int KT, int WM, int WN, int KIND>
 hipError_t run_dma(const GemmArgs& g, int batch, hipStream_t s) {
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_dma_kernel<AK, BK, BM, BN, 64, 2, WM, WN, KIND>), dim3(tiles, batch), dim3(64 * WM * WN),
+  hipLaunchKernelGGL((gemm_dma_kernel<AK, BK, BM, BN, KT, 2, WM, WN, KIND>), dim3(tiles, batch), dim3(64 * WM * WN),
                      0, s, g);
   return hipGetLastError();
 }
@@ -92,17 +93,17 @@ hipError_t run_tile(const GemmArgs& g, int batch, hipStream_t s) {
 
 template <bool AK, bool BK, int KIND>
 hipError_t run_dma_tile(const GemmArgs& g, int batch, hipStream_t s) {
-  if (g.causal != CAUSAL_NONE) return run_dma<AK, BK, 128, 128, 2, 2, KIND>(g, batch, s);
+  if (g.causal != CAUSAL_NONE) return run_dma<AK, BK, 128, 128, 64, 2, 2, KIND>(g, batch, s);
   if constexpr (AK && BK) {
     switch (pick(kDmaNT, g, batch)) {
-      case 0: return run_dma<AK, BK, 256, 256, 2, 4, KIND>(g, batch, s);
-      case 1: return run_dma<AK, BK, 256, 192, 4, 2, KIND>(g, batch, s);
-      default: return run_dma<AK, BK, 128, 128, 2, 2, KIND>(g, batch, s);
+      case 0: return run_dma<AK, BK, 256, 256, 64, 2, 4, KIND>(g, batch, s);
+      case 1: return run_dma<AK, BK, 256, 192, 64, 4, 2, KIND>(g, batch, s);
+      default: return run_dma<AK, BK, 128, 128, 64, 2, 2, KIND>(g, batch, s);
     }
   } else {
     switch (pick(kDmaT, g, batch)) {
-      case 0: return run_dma<AK, BK, 256, 256, 2, 4, KIND>(g, batch, s);
-      default: return run_dma<AK, BK, 128, 128, 2, 2, KIND>(g, batch, s);
+      case 0: return run_dma<AK, BK, 256, 256, 64, 2, 4, KIND>(g, batch, s);
+      default: return run_dma<AK, BK, 128, 128, 64, 2, 2, KIND>(g, batch, s);
     }
   }
 }
@@ -129,14 +130,12 @@ hipError_t dispatch(const GemmArgs& g, int batch, hipStream_t s) {
 }
 
 // Paired launch with tile config (BM, BN, WM, WN) for both problems.
-template <int BM, int BN, int WM, int WN, int KIND0>
+template <class P0, class P1>
 hipError_t run_pair(const GemmArgs& g0, const GemmArgs& g1, hipStream_t s) {
-  const int t0 = ((g0.M + BM - 1) / BM) * ((g0.N + BN - 1) / BN);
-  const int t1 = ((g1.M + BM - 1) / BM) * ((g1.N + BN - 1) / BN);
+  const int t0 = ((g0.M + P0::kBM - 1) / P0::kBM) * ((g0.N + P0::kBN - 1) / P0::kBN);
+  const int t1 = ((g1.M + P1::kBM - 1) / P1::kBM) * ((g1.N + P1::kBN - 1) / P1::kBN);
   const int first = g1.K > g0.K ? 1 : 0;  // deeper contraction first
-  typedef DmaProblem<true, false, BM, BN, WM, WN, KIND0> P0;
-  typedef DmaProblem<false, false, BM, BN, WM, WN, EPI_STORE_F32> P1;
-  hipLaunchKernelGGL((gemm_dma_pair_kernel<P0, P1>), dim3(t0 + t1), dim3(64 * WM * WN), 0, s, g0, g1, first,
+  hipLaunchKernelGGL((gemm_dma_pair_kernel<P0, P1>), dim3(t0 + t1), dim3(P0::kThreads), 0, s, g0, g1, first,
                      first ? t1 : t0);
   return hipGetLastError();
 }
@@ -152,22 +151,38 @@ double pair_cost(const TileCfg& c, const GemmArgs& g0, const GemmArgs& g1) {
   return t * c.bm * c.bn * c.per_cu / c.eff;
 }
 
+// dgrad (A k-contiguous, B n-contiguous) + wgrad (both token-strided, fp32 out).
 template <int KIND0>
 hipError_t pair_dispatch(const GemmArgs& g0, const GemmArgs& g1, hipStream_t s) {
   if (pair_cost(kDmaT[0], g0, g1) <= pair_cost(kDmaT[1], g0, g1))
-    return run_pair<256, 256, 2, 4, KIND0>(g0, g1, s);
-  return run_pair<128, 128, 2, 2, KIND0>(g0, g1, s);
+    return run_pair<DmaProblem<true, false, 256, 256, 64, 2, 4, KIND0>,
+                    DmaProblem<false, false, 256, 256, 64, 2, 4, EPI_STORE_F32>>(g0, g1, s);
+  return run_pair<DmaProblem<true, false, 128, 128, 64, 2, 2, KIND0>,
+                  DmaProblem<false, false, 128, 128, 64, 2, 2, EPI_STORE_F32>>(g0, g1, s);
+}
+
+// Two both-k-contiguous problems, fp32 out.
+hipError_t pair_dispatch_nt(const GemmArgs& g0, const GemmArgs& g1, hipStream_t s) {
+  if (pair_cost(kDmaNT[0], g0, g1) <= pair_cost(kDmaNT[2], g0, g1))
+    return run_pair<DmaProblem<true, true, 256, 256, 64, 2, 4, EPI_STORE_F32>,
+                    DmaProblem<true, true, 256, 256, 64, 2, 4, EPI_STORE_F32>>(g0, g1, s);
+  return run_pair<DmaProblem<true, true, 128, 128, 64, 2, 2, EPI_STORE_F32>,
+                  DmaProblem<true, true, 128, 128, 64, 2, 2, EPI_STORE_F32>>(g0, g1, s);
 }
 
 }  // namespace
 
 hipError_t launch_gemm_bf16_pair(const GemmArgs& g0, bool a_k0, bool b_k0, int kind0, const GemmArgs& g1, bool a_k1,
                                  bool b_k1, int kind1, hipStream_t s) {
-  if (!(a_k0 && !b_k0 && !a_k1 && !b_k1 && kind1 == EPI_STORE_F32)) return hipErrorNotSupported;
-  if (kind0 != EPI_STORE && kind0 != EPI_DGELU) return hipErrorNotSupported;
   for (const GemmArgs* g : {&g0, &g1})
     if (g->causal != CAUSAL_NONE || g->nseg != 1 || g->M <= 0 || g->N <= 0) return hipErrorNotSupported;
-  if (!dma_ok(g0, true, false) || !dma_ok(g1, false, false)) return hipErrorNotSupported;
+  if (!dma_ok(g0, a_k0, b_k0) || !dma_ok(g1, a_k1, b_k1)) return hipErrorNotSupported;
+  if (a_k0 && b_k0 && a_k1 && b_k1) {
+    if (kind0 != EPI_STORE_F32 || kind1 != EPI_STORE_F32) return hipErrorNotSupported;
+    return pair_dispatch_nt(g0, g1, s);
+  }
+  if (!(a_k0 && !b_k0 && !a_k1 && !b_k1 && kind1 == EPI_STORE_F32)) return hipErrorNotSupported;
+  if (kind0 != EPI_STORE && kind0 != EPI_DGELU) return hipErrorNotSupported;
   return kind0 == EPI_DGELU ? pair_dispatch<EPI_DGELU>(g0, g1, s) : pair_dispatch<EPI_STORE>(g0, g1, s);
 }
 

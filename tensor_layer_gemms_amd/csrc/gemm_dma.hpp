@@ -7,8 +7,8 @@
 // the weight of a dgrad, V in P V) is kept as it lies in memory ([BK][rows]) and read
 // with the transposing ds_read_b64_tr_b16, which hands each lane 4 consecutive k of one
 // m. Out-of-range rows and the k tail read zeros through the buffer resource's range
-// check. An NS-deep ring of LDS stages keeps NS-1 stages of loads in flight while one
-// stage is multiplied.
+// check. Two LDS stages alternate: one is multiplied while the loads of the next fill the
+// other.
 #pragma once
 
 #include "gemm_kernels.hpp"
@@ -25,6 +25,23 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// LDS filled by DMA loads. The compiler does not see those loads as writes of the LDS
+// they fill; if the LDS array's address never escapes it even concludes that nothing
+// writes the array, and moves reads of a freshly filled stage above the barrier and
+// above the wait for the loads. dma_lds_escape hands the array's address to an opaque
+// asm once, so every later memory clobber may write it; dma_barrier puts memory
+// clobbers and scheduling barriers around the work-group barrier, which pins every LDS
+// access on its side.
+__device__ __forceinline__ void dma_lds_escape(void* lds) { asm volatile("" : : "v"(lds) : "memory"); }
+
+__device__ __forceinline__ void dma_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
 }
 
 // LDS placement of 16-byte chunks.
@@ -134,6 +151,7 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs& g, int bid, int z,
   constexpr int STAGE = (BM + BN) * BK;  // bf16 elements per stage
   static_assert(TM >= 1 && TN >= 1 && BM % (WM * 32) == 0 && BN % (WN * 32) == 0, "wave tile of 32x32 blocks");
 
+  dma_lds_escape(smem);
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm0 = (wave / WN) * (BM / WM), wn0 = (wave % WN) * (BN / WN);
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
@@ -189,21 +207,20 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs& g, int bid, int z,
       lb[2].issue(st + BM * BK, k0, kend, wave, lane);
     }
   };
-  constexpr int LOADS = DmaLoader<BM, BK, NW, A_K>::PER_WAVE + DmaLoader<BN, BK, NW, B_K>::PER_WAVE;
 
+  // Two-stage ring. At the start of step t this wave waits for its loads of step t
+  // (issued one step earlier); the barrier makes every wave's loads visible and frees
+  // the stage multiplied in step t - 1, which then receives the loads of step t + 1
+  // while step t is multiplied.
+  static_assert(NS == 2, "two-stage ring");
+  constexpr int KS = BK / 16;
   if (nk > 0) {
-#pragma unroll
-    for (int p = 0; p < NS - 1; ++p)
-      if (p < nk) issue(p);
+    issue(0);
     for (int t = 0; t < nk; ++t) {
-      // This wave's loads of step t are complete when at most the loads of the steps
-      // after it (up to NS-2 of them) are outstanding; the barrier makes every wave's
-      // loads visible and frees the stage multiplied in step t-1 for reuse.
-      if (nk - 1 - t >= NS - 2) wait_vmcnt<(NS - 2) * LOADS>();
-      else wait_vmcnt<0>();
-      __syncthreads();
-      if (t + NS - 1 < nk) issue(t + NS - 1);
-      const bf16* sA = smem + (t % NS) * STAGE;
+      wait_vmcnt<0>();
+      dma_barrier();
+      if (t + 1 < nk) issue(t + 1);
+      const bf16* sA = smem + (t & 1) * STAGE;
       const bf16* sB = sA + BM * BK;
       bf16x8 af[2][TM], bfr[2][TN];
 #pragma unroll
@@ -211,9 +228,9 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs& g, int bid, int z,
 #pragma unroll
       for (int j = 0; j < TN; ++j) bfr[0][j] = rb[j].read(sB, 0, lane);
 #pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
+      for (int ks = 0; ks < KS; ++ks) {
         const int cb = ks & 1, nb = cb ^ 1;
-        if (ks + 1 < BK / 16) {
+        if (ks + 1 < KS) {
 #pragma unroll
           for (int i = 0; i < TM; ++i) af[nb][i] = ra[i].read(sA, ks + 1, lane);
 #pragma unroll
@@ -252,11 +269,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs g) {
 }
 
 // Compile-time description of one problem of a paired launch.
-template <bool A_K, bool B_K, int BM, int BN, int WM, int WN, int KIND>
+template <bool A_K, bool B_K, int BM, int BN, int BK, int WM, int WN, int KIND>
 struct DmaProblem {
-  static constexpr int kBM = BM, kBN = BN, kThreads = 64 * WM * WN, kSmem = 2 * (BM + BN) * 64;
+  static constexpr int kBM = BM, kBN = BN, kThreads = 64 * WM * WN, kSmem = 2 * (BM + BN) * BK;
   static __device__ __forceinline__ void tile(const GemmArgs& g, int bid, bf16* smem) {
-    gemm_dma_tile<A_K, B_K, BM, BN, 64, 2, WM, WN, KIND>(g, bid, 0, smem);
+    gemm_dma_tile<A_K, B_K, BM, BN, BK, 2, WM, WN, KIND>(g, bid, 0, smem);
   }
 };
 

@@ -98,7 +98,7 @@ size_t carve_layer_saved(const Dims& d, void* base, LayerSaved* s) {
 }
 
 struct LayerFwdWs {
-  float* S;
+  float* S;      // scores; before them (bf16 path) the fp32 partials of the QKV projection
   void* o;       // out-projection partial, then FC2 partial
   void* u_lo;    // bf16 path: rounding remainder of U
   void* qkv_lo;  // bf16 path: rounding remainders of Q and K, in the QKV layout
@@ -106,7 +106,8 @@ struct LayerFwdWs {
 
 size_t carve_layer_fwd_ws(const Dims& d, void* base, LayerFwdWs* w) {
   Carver c(base);
-  w->S = c.take<float>(d.B * d.at * d.seq * d.seq * 4);
+  const int64_t qkv_partials = d.bf16 ? d.M * (d.qkv + 2 * d.hs) : 0;
+  w->S = c.take<float>(std::max<int64_t>(d.B * d.at * d.seq * d.seq, qkv_partials) * 4);
   w->o = c.take(d.M * d.h * d.es);
   w->u_lo = d.bf16 ? c.take(d.M * d.h * 2) : nullptr;
   w->qkv_lo = d.bf16 ? c.take(d.M * d.qkv * 2) : nullptr;
@@ -293,6 +294,20 @@ int layer_fwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, void
     GemmArgs g = plain(sv.u, d.h, w.w_qkv, d.h, sv.qkv, d.qkv, d.M, d.qkv, d.h);
     g.vec = w.b_qkv;
     if (!bf) return gemm(d, g, true, true, EPI_BIAS, 1, stream);
+    // The Q and K columns take U_hi W^T + U_lo W^T, twice the contraction of the V
+    // columns. The two products run as equal-depth problems of one launch into fp32
+    // partials (which fills the CUs evenly), and a pass adds them and the bias and
+    // splits Q, K into hi + lo.
+    float* hi = ws.S;
+    float* lo = ws.S + d.M * d.qkv;
+    const GemmArgs ghi = plain(sv.u, d.h, w.w_qkv, d.h, hi, d.qkv, d.M, d.qkv, d.h);
+    const GemmArgs glo = plain(ws.u_lo, d.h, w.w_qkv, d.h, lo, 2 * d.hs, d.M, 2 * d.hs, d.h);
+    const hipError_t e = launch_gemm_bf16_pair(ghi, true, true, EPI_STORE_F32, glo, true, true, EPI_STORE_F32, stream);
+    if (e == hipSuccess)
+      return launch_qkv_finish(hi, lo, w.b_qkv, sv.qkv, ws.qkv_lo, (int)d.M, (int)d.qkv, (int)(2 * d.hs), stream);
+    if (e != hipErrorNotSupported) return e;
+    // Operands the paired launch cannot address: one GEMM with a second K segment for
+    // the Q and K columns.
     g.seg_a[1] = ws.u_lo;
     g.seg_b[1] = w.w_qkv;
     g.nseg = 2;

