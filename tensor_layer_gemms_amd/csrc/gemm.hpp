@@ -81,4 +81,15 @@ hipError_t launch_gemm_f32(const GemmArgs& g, bool a_kcontig, bool b_kcontig, in
 hipError_t launch_gemm_bf16_pair(const GemmArgs& g0, bool a_k0, bool b_k0, int kind0, const GemmArgs& g1, bool a_k1,
                                  bool b_k1, int kind1, hipStream_t stream);
 
+// Input gradient with a deep, narrow contraction (K > 2 N): the number of k slices it is
+// split into (1, 2 or 4; depends on N and K only, so every token is computed the same way
+// at any batch size).
+int gemm_dgrad_splits(int64_t N, int64_t K);
+// The same pairing as above for an EPI_STORE input gradient dg (A k-contiguous, B
+// n-contiguous, unbatched) and a weight gradient wg, with dg split into
+// gemm_dgrad_splits(dg.N, dg.K) k slices written as fp32 to part ([splits, M, N]) and
+// summed in slice order into dg.C by a second pass. Returns hipErrorNotSupported
+// (nothing launched) if dg is not split or the pair does not qualify.
+hipError_t launch_gemm_bf16_pair_split(const GemmArgs& dg, const GemmArgs& wg, float* part, hipStream_t stream);
+
 }  // namespace mt

@@ -130,13 +130,15 @@ hipError_t dispatch(const GemmArgs& g, int batch, hipStream_t s) {
 }
 
 // Paired launch with tile config (BM, BN, WM, WN) for both problems.
+// Paired launch; problem 0 may be batched (batch0 entries, e.g. k slices).
 template <class P0, class P1>
-hipError_t run_pair(const GemmArgs& g0, const GemmArgs& g1, hipStream_t s) {
-  const int t0 = ((g0.M + P0::kBM - 1) / P0::kBM) * ((g0.N + P0::kBN - 1) / P0::kBN);
-  const int t1 = ((g1.M + P1::kBM - 1) / P1::kBM) * ((g1.N + P1::kBN - 1) / P1::kBN);
+hipError_t run_pair(const GemmArgs& g0, const GemmArgs& g1, hipStream_t s, int batch0 = 1) {
+  const int z0 = ((g0.M + P0::kBM - 1) / P0::kBM) * ((g0.N + P0::kBN - 1) / P0::kBN);
+  const int z1 = ((g1.M + P1::kBM - 1) / P1::kBM) * ((g1.N + P1::kBN - 1) / P1::kBN);
+  const int t0 = z0 * batch0, t1 = z1;
   const int first = g1.K > g0.K ? 1 : 0;  // deeper contraction first
   hipLaunchKernelGGL((gemm_dma_pair_kernel<P0, P1>), dim3(t0 + t1), dim3(P0::kThreads), 0, s, g0, g1, first,
-                     first ? t1 : t0);
+                     first ? t1 : t0, z0, z1);
   return hipGetLastError();
 }
 
@@ -149,6 +151,24 @@ double pair_cost(const TileCfg& c, const GemmArgs& g0, const GemmArgs& g1) {
   const double slots = (double)kNumCUs * c.per_cu;
   const double t = std::max((tiles(g0) * s0 + tiles(g1) * s1) / slots, std::max(s0, s1));
   return t * c.bm * c.bn * c.per_cu / c.eff;
+}
+
+// C = bf16(sum over `splits` fp32 slices of part, each [M, N] dense), C strided by ldc.
+__global__ __launch_bounds__(256) void split_sum_kernel(const float* __restrict__ part, bf16* __restrict__ C, int M,
+                                                        int N, int splits, int64_t ldc, int64_t total) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int cpr = N / 8;
+  const int m = (int)(i / cpr), n = (int)(i % cpr) * 8;
+  float acc[8];
+  load8(part + (int64_t)m * N + n, acc);
+  for (int z = 1; z < splits; ++z) {
+    float v[8];
+    load8(part + ((int64_t)z * M + m) * N + n, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += v[e];
+  }
+  store8(C + (int64_t)m * ldc + n, acc);
 }
 
 // dgrad (A k-contiguous, B n-contiguous) + wgrad (both token-strided, fp32 out).
@@ -171,6 +191,48 @@ hipError_t pair_dispatch_nt(const GemmArgs& g0, const GemmArgs& g1, hipStream_t 
 }
 
 }  // namespace
+
+int gemm_dgrad_splits(int64_t N, int64_t K) {
+  int best = 1;
+  for (int sp = 2; sp <= 4; sp *= 2) {
+    if (K / (sp / 2) <= 2 * N || K % (64 * sp) != 0) break;  // already shallow enough, or not divisible
+    best = sp;
+  }
+  return best;
+}
+
+hipError_t launch_gemm_bf16_pair_split(const GemmArgs& dg, const GemmArgs& wg, float* part, hipStream_t s) {
+  const int sp = gemm_dgrad_splits(dg.N, dg.K);
+  if (sp <= 1 || !part || dg.N % 8 || dg.causal != CAUSAL_NONE || dg.nseg != 1 || dg.zdiv != 1)
+    return hipErrorNotSupported;
+  for (const GemmArgs* g : {&dg, &wg})
+    if (g->causal != CAUSAL_NONE || g->nseg != 1 || g->M <= 0 || g->N <= 0) return hipErrorNotSupported;
+  if (!dma_ok(dg, true, false) || !dma_ok(wg, false, false)) return hipErrorNotSupported;
+  // dgrad as `sp` k slices: slice z contracts k in [z K/sp, (z + 1) K/sp) into part[z].
+  GemmArgs g0 = dg;
+  const int64_t ks = dg.K / sp;
+  g0.K = (int)ks;
+  g0.a_so = ks;             // A(m, k) at m lda + k
+  g0.b_so = ks * dg.ldb;    // B(n, k) at k ldb + n
+  g0.C = part;
+  g0.ldc = dg.N;
+  g0.c_so = (int64_t)dg.M * dg.N;
+  g0.a_si = g0.b_si = g0.c_si = 0;
+  g0.zdiv = 1;
+  g0.alpha = 1.0f;
+  hipError_t e;
+  if (pair_cost(kDmaT[0], g0, wg) <= pair_cost(kDmaT[1], g0, wg))
+    e = run_pair<DmaProblem<true, false, 256, 256, 64, 2, 4, EPI_STORE_F32>,
+                 DmaProblem<false, false, 256, 256, 64, 2, 4, EPI_STORE_F32>>(g0, wg, s, sp);
+  else
+    e = run_pair<DmaProblem<true, false, 128, 128, 64, 2, 2, EPI_STORE_F32>,
+                 DmaProblem<false, false, 128, 128, 64, 2, 2, EPI_STORE_F32>>(g0, wg, s, sp);
+  if (e != hipSuccess) return e;
+  const int64_t total = (int64_t)dg.M * (dg.N / 8);
+  hipLaunchKernelGGL(split_sum_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part,
+                     static_cast<bf16*>(dg.C), dg.M, dg.N, sp, dg.ldc, total);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm_bf16_pair(const GemmArgs& g0, bool a_k0, bool b_k0, int kind0, const GemmArgs& g1, bool a_k1,
                                  bool b_k1, int kind1, hipStream_t s) {

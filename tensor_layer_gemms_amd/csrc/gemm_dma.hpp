@@ -272,25 +272,26 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs g) {
 template <bool A_K, bool B_K, int BM, int BN, int BK, int WM, int WN, int KIND>
 struct DmaProblem {
   static constexpr int kBM = BM, kBN = BN, kThreads = 64 * WM * WN, kSmem = 2 * (BM + BN) * BK;
-  static __device__ __forceinline__ void tile(const GemmArgs& g, int bid, bf16* smem) {
-    gemm_dma_tile<A_K, B_K, BM, BN, BK, 2, WM, WN, KIND>(g, bid, 0, smem);
+  static __device__ __forceinline__ void tile(const GemmArgs& g, int bid, int z, bf16* smem) {
+    gemm_dma_tile<A_K, B_K, BM, BN, BK, 2, WM, WN, KIND>(g, bid, z, smem);
   }
 };
 
-// Two independent, unbatched problems in one launch. Blocks [0, tiles_first) run the
-// problem named by `first` (0 or 1), the remaining blocks the other one, so the second
-// problem's tiles fill the CUs the first one leaves idle.
+// Two independent problems in one launch; problem i has per_z[i] tiles per batch entry.
+// Blocks [0, tiles_first) run the problem named by `first` (0 or 1), the remaining
+// blocks the other one, so the second problem's tiles fill the CUs the first one leaves
+// idle.
 template <class P0, class P1>
 __global__ __launch_bounds__(P0::kThreads) void gemm_dma_pair_kernel(GemmArgs g0, GemmArgs g1, int first,
-                                                                      int tiles_first) {
+                                                                      int tiles_first, int per_z0, int per_z1) {
   static_assert(P0::kThreads == P1::kThreads, "paired problems share the work-group size");
   constexpr int SMEM = P0::kSmem > P1::kSmem ? P0::kSmem : P1::kSmem;
   __shared__ __attribute__((aligned(1024))) bf16 smem[SMEM];
   const int bid = blockIdx.x;
   const bool in_first = bid < tiles_first;
   const int local = in_first ? bid : bid - tiles_first;
-  if (in_first == (first == 0)) P0::tile(g0, local, smem);
-  else P1::tile(g1, local, smem);
+  if (in_first == (first == 0)) P0::tile(g0, local % per_z0, local / per_z0, smem);
+  else P1::tile(g1, local % per_z1, local / per_z1, smem);
 }
 
 }  // namespace mt

@@ -117,7 +117,20 @@ size_t carve_layer_fwd_ws(const Dims& d, void* base, LayerFwdWs* w) {
 struct LayerBwdWs {
   void *da, *dv2, *dx2, *dctx, *ds, *dqkv;
   float *dx2f, *D, *part;  // dx2f: fp32 copy of dX2 for the residual path
+  float* spart;            // k-slice partials of a split input gradient (bf16 path)
 };
+
+// fp32 partials of the largest split input gradient of the layer (0 if none splits).
+int64_t dgrad_split_floats(const Dims& d) {
+  if (!d.bf16) return 0;
+  const int64_t nk[4][2] = {{d.ft, d.h}, {d.h, d.ft}, {d.hs, d.h}, {d.h, d.qkv}};
+  int64_t n = 0;
+  for (const auto& p : nk) {
+    const int sp = gemm_dgrad_splits(p[0], p[1]);
+    if (sp > 1) n = std::max<int64_t>(n, sp * d.M * p[0]);
+  }
+  return n;
+}
 
 size_t colsum_floats(const Dims& d) {
   size_t n = colsum_partial_floats((int)d.M, (int)d.h, 1);
@@ -137,6 +150,8 @@ size_t carve_layer_bwd_ws(const Dims& d, void* base, LayerBwdWs* w) {
   w->dqkv = c.take(d.M * d.qkv * d.es);
   w->D = c.take<float>(d.B * d.at * d.seq * 4);
   w->part = c.take<float>(colsum_floats(d) * 4);
+  const int64_t sp = dgrad_split_floats(d);
+  w->spart = sp ? c.take<float>(sp * 4) : nullptr;
   return c.off;
 }
 
@@ -247,7 +262,12 @@ hipError_t gemm(const Dims& d, const GemmArgs& g, bool a_k, bool b_k, int kind, 
 // Input gradient dg (A k-contiguous, B n-contiguous; epilogue dkind) and weight
 // gradient wg (both operands token-strided, fp32 out) of one linear layer: one paired
 // launch where the bf16 path supports it, else the two one after the other.
-hipError_t gemm_dgrad_wgrad(const Dims& d, const GemmArgs& dg, int dkind, const GemmArgs& wg, hipStream_t s) {
+hipError_t gemm_dgrad_wgrad(const Dims& d, const GemmArgs& dg, int dkind, const GemmArgs& wg, hipStream_t s,
+                            float* spart = nullptr) {
+  if (d.bf16 && dkind == EPI_STORE && spart) {  // deep, narrow input gradient: k slices
+    const hipError_t e = launch_gemm_bf16_pair_split(dg, wg, spart, s);
+    if (e != hipErrorNotSupported) return e;
+  }
   if (d.bf16) {
     const hipError_t e = launch_gemm_bf16_pair(dg, true, false, dkind, wg, false, false, EPI_STORE_F32, s);
     if (e != hipErrorNotSupported) return e;
@@ -413,7 +433,7 @@ int layer_bwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, cons
   q.run("fc1_dgrad_wgrad", 2 * gflop(d.M, d.h, d.ft), 0, [&] {
     const GemmArgs dg = plain(ws.da, d.ft, w.w_fc1, d.h, ws.dv2, d.h, d.M, d.h, d.ft);
     const GemmArgs wg = plain(ws.da, d.ft, sv.v2, d.h, gr.w_fc1, d.h, d.ft, d.h, d.M);
-    return gemm_dgrad_wgrad(d, dg, EPI_STORE, wg, stream);
+    return gemm_dgrad_wgrad(d, dg, EPI_STORE, wg, stream, ws.spart);
   });
   // B3 dX2 = dOut + LN2-backward(AR(dV2)) (written as the GEMM operand and as an fp32
   // copy for the residual path); dgamma2, dbeta2; db_o = colsum(dX2)
@@ -433,7 +453,7 @@ int layer_bwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, cons
   q.run("out_proj_dgrad_wgrad", 2 * gflop(d.M, d.hs, d.h), 0, [&] {
     const GemmArgs dg = plain(ws.dx2, d.h, w.w_o, d.hs, ws.dctx, d.hs, d.M, d.hs, d.h);
     const GemmArgs wg = plain(ws.dx2, d.h, sv.ctx, d.hs, gr.w_o, d.hs, d.h, d.hs, d.M);
-    return gemm_dgrad_wgrad(d, dg, EPI_STORE, wg, stream);
+    return gemm_dgrad_wgrad(d, dg, EPI_STORE, wg, stream, ws.spart);
   });
   // B5/B6 attention: D = rowsum(dctx * ctx) = rowsum(P * dP); dS = P * (dctx V^T - D)
   q.run("attn_rowdot", 0, 2.0 * d.M * d.hs * es, [&] {
@@ -494,7 +514,7 @@ int layer_bwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, cons
   q.run("qkv_dgrad_wgrad", 2 * gflop(d.M, d.h, d.qkv), 0, [&] {
     const GemmArgs dg = plain(ws.dqkv, d.qkv, w.w_qkv, d.h, ws.dv2, d.h, d.M, d.h, d.qkv);
     const GemmArgs wg = plain(ws.dqkv, d.qkv, sv.u, d.h, gr.w_qkv, d.h, d.qkv, d.h, d.M);
-    return gemm_dgrad_wgrad(d, dg, EPI_STORE, wg, stream);
+    return gemm_dgrad_wgrad(d, dg, EPI_STORE, wg, stream, ws.spart);
   });
   // B8 dX = dX2 + LN1-backward(AR(dU)); dgamma1, dbeta1
   q.run("ln1_bwd", 0, Mh * (3 * es + 4), [&] {
