@@ -1,0 +1,551 @@
+// Fused causal attention kernels (see flash_attn.hpp).
+#include "flash_attn.hpp"
+
+#include "gemm_dma.hpp"
+
+namespace mt {
+
+namespace {
+
+constexpr int kFlashRows = 64;  // query rows per work-group (2 waves of 32)
+constexpr int kFlashKeys = 32;  // keys per streamed block
+// LDS ring depth: every row block of a head streams the same key blocks at about the same
+// pace, so each block's loads tend to miss in L2 together; three stages give them two
+// steps to arrive.
+constexpr int kStages = 3;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// LDS placement of 16-byte chunks in a [32 keys][D] tile.
+// K (read with ds_read_b128, 16 lanes on 16 consecutive keys at one chunk): spread the 16
+// rows over the 64 banks.
+template <int D>
+__device__ __forceinline__ int kswz(int row, int chunk) {
+  if constexpr (D == 128) return chunk ^ (row & 15);
+  else return chunk ^ ((row >> 1) & 7);
+}
+// V (read with ds_read_b64_tr_b16, a half-wave on 4 consecutive keys x 32 columns): put
+// the 4 rows in 4 different 64-byte bank groups.
+template <int D>
+__device__ __forceinline__ int vswz(int row, int chunk) {
+  if constexpr (D == 128) return chunk ^ ((row & 3) << 2);
+  else return chunk ^ (((row >> 1) & 1) << 2);
+}
+
+// DMA of one [32][D] tile whose rows are key rows kb.. of a head's column slice. `rsrc`
+// covers the sequence's rows (rows past it read zeros); row r of the tile is at byte
+// r * ld * 2 + chunk * 16 from the resource base. A wave instruction fills 1 KB of LDS:
+// lane L writes bytes [16 L, +16) of it = tile row q * RPI + L / CPR, stored chunk
+// L % CPR, which holds the logical chunk the swizzle maps there.
+template <int D, bool VTILE, int NW>
+__device__ __forceinline__ void dma_tile(bf16* lds, __amdgpu_buffer_rsrc_t rsrc, int64_t ld, int kb, int rows_left,
+                                         int wave, int lane) {
+  constexpr int CPR = D / 8, RPI = 64 / CPR, INSTR = 32 * D / 512;
+  static_assert(INSTR % NW == 0, "tile instructions split over the waves");
+#pragma unroll
+  for (int i = 0; i < INSTR / NW; ++i) {
+    const int q = wave + i * NW;
+    const int r = q * RPI + lane / CPR, p = lane % CPR;
+    const int c = VTILE ? vswz<D>(r, p) : kswz<D>(r, p);
+    const uint32_t off = r < rows_left ? (uint32_t)(((int64_t)(kb + r) * ld + c * 8) * 2) : 0xFFFFFFF0u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(lds + q * 512), 16, off, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t seq_rsrc(const bf16* base, int64_t ld, int seq) {
+  const uint64_t bytes = (uint64_t)seq * (uint64_t)ld * 2u;
+  const uint32_t n = bytes < 0xFFFFFFF0ull ? (uint32_t)bytes : 0xFFFFFFF0u;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base), (short)0, (int)n, 0x00020000);
+}
+
+// ---------------------------------------------------------------------------- forward
+// Work-group: 64 query rows (wave w: rows q0 + 32 w ..) of sequence b, head k. Lane l of a
+// wave owns query row (l & 31); the logit accumulator of a 32-key block holds keys
+// 8 q + 4 (l >> 5) + j in register 4 q + j (the operand-swapped MFMA layout).
+template <int D>
+__global__ __launch_bounds__(128) void flash_fwd_kernel(FlashArgs a) {
+  constexpr int KS = D / 16, NB = D / 32, TILE = kFlashKeys * D;
+  __shared__ __attribute__((aligned(1024))) bf16 smem[kStages * 3 * TILE];
+  dma_lds_escape(smem);
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 5, r32 = lane & 31;
+  const int nqb = (a.seq + kFlashRows - 1) / kFlashRows;
+  const int qb = nqb - 1 - (int)blockIdx.x;  // deepest row blocks first
+  const int z = blockIdx.y, b = z / a.heads, hd = z % a.heads;
+  const int row = qb * kFlashRows + wave * 32 + r32;  // this lane's query row
+  const bool row_ok = row < a.seq;
+
+  const bf16* qkv = static_cast<const bf16*>(a.qkv) + (int64_t)b * a.seq * a.ldq;
+  const bf16* qlo = static_cast<const bf16*>(a.qkv_lo) + (int64_t)b * a.seq * a.ldq;
+  const int cq = hd * D, ck = a.hs + hd * D, cv = 2 * a.hs + hd * D;
+
+  // Q_hi, Q_lo fragments of this lane's row for the whole head dim (A operand).
+  bf16x8 qh[KS], ql[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (row_ok) {
+      qh[ks] = *reinterpret_cast<const bf16x8*>(qkv + (int64_t)row * a.ldq + cq + 16 * ks + 8 * h);
+      ql[ks] = *reinterpret_cast<const bf16x8*>(qlo + (int64_t)row * a.ldq + cq + 16 * ks + 8 * h);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qh[ks][e] = ql[ks][e] = (bf16)0.f;
+    }
+  }
+
+  const __amdgpu_buffer_rsrc_t rk = seq_rsrc(qkv + ck, a.ldq, a.seq);
+  const __amdgpu_buffer_rsrc_t rkl = seq_rsrc(qlo + ck, a.ldq, a.seq);
+  const __amdgpu_buffer_rsrc_t rv = seq_rsrc(qkv + cv, a.ldq, a.seq);
+  const int kend = min(a.seq, (qb + 1) * kFlashRows);  // keys this row block can see
+  const int nsteps = (kend + kFlashKeys - 1) / kFlashKeys;
+  auto issue = [&](int t) {
+    bf16* st = smem + (t % kStages) * 3 * TILE;
+    const int kb = t * kFlashKeys, left = a.seq - kb;
+    dma_tile<D, false, 2>(st, rk, a.ldq, kb, left, wave, lane);
+    dma_tile<D, false, 2>(st + TILE, rkl, a.ldq, kb, left, wave, lane);
+    dma_tile<D, true, 2>(st + 2 * TILE, rv, a.ldq, kb, left, wave, lane);
+  };
+
+  // Per-lane LDS offsets. K fragment (B operand of S): key row r32, chunk 2 ks + h.
+  // V fragment (B operand of O, transposing read): 16-lane group g reads key rows
+  // K0 + ((l & 15) >> 2), columns 32 nb + 16 (g & 1) + 4 (l & 3).
+  const float scale2 = a.scale * kLog2e;  // logits in log2 units
+  f32x16 o[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[nb][r] = 0.f;
+  float m = -__builtin_inff(), l = 0.f;
+
+  // Per wave: 3 tiles of 32 D / 512 DMA instructions, over 2 waves.
+  constexpr int LOADS = 3 * (32 * D / 512) / 2;
+  issue(0);
+  if (nsteps > 1) issue(1);
+  for (int t = 0; t < nsteps; ++t) {
+    // this wave's loads of step t are done when at most those of step t + 1 are pending
+    if (t + 1 < nsteps) wait_vmcnt<LOADS>();
+    else wait_vmcnt<0>();
+    dma_barrier();
+    if (t + 2 < nsteps) issue(t + 2);  // into the stage read in step t - 1
+    const bf16* sK = smem + (t % kStages) * 3 * TILE;
+    const bf16* sKl = sK + TILE;
+    const bf16* sV = sK + 2 * TILE;
+
+    // Keys of this block vs this wave's rows r0..r0 + 31 (block and row starts are
+    // multiples of 32): all visible, the diagonal block, or none (nothing to do).
+    const int kb = t * kFlashKeys, r0 = qb * kFlashRows + wave * 32;
+    if (kb > r0) continue;
+    const bool diag = kb == r0;
+
+    // S block: 32 keys x this wave's 32 rows, three compensated segments.
+    f32x16 s;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int off = r32 * D + (kswz<D>(r32, 2 * ks + h) << 3);
+      const bf16x8 kh = *reinterpret_cast<const bf16x8*>(sK + off);
+      const bf16x8 kl = *reinterpret_cast<const bf16x8*>(sKl + off);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qh[ks], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, qh[ks], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, ql[ks], s, 0, 0, 0);
+    }
+
+    // Online softmax (row shared by lanes l and l ^ 32), in log2 units of the scaled
+    // logits. m is the maximum the exponentials are taken against; it is raised (and O,
+    // l rescaled) only when the block maximum exceeds it by more than 8, so the
+    // exponentials stay <= 2^8 and most blocks need no rescaling.
+    if (diag) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (kb + 8 * (r >> 2) + 4 * h + (r & 3) > row) s[r] = -__builtin_inff();
+    }
+    float mloc = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, s[r]);
+    const float mblk = fmaxf(mloc, __shfl_xor(mloc, 32)) * scale2;
+    if (__any(mblk > m + 8.f)) {
+      const float mnew = fmaxf(m, mblk);
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+      m = mnew;
+      l *= alpha;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[nb][r] *= alpha;
+    }
+    float lsum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], scale2, -m));
+      lsum += s[r];
+    }
+    l += lsum + __shfl_xor(lsum, 32);
+
+    // O += P V over the block's two 16-key slices.
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      bf16x8 p;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p[e] = (bf16)s[8 * sl + e];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int col = 32 * nb + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        s16x4 v2[2];
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+          const int krow = 16 * sl + 8 * rr + 4 * h + ((lane & 15) >> 2);
+          const bf16* pv = sV + krow * D + (vswz<D>(krow, col >> 3) << 3) + (col & 7);
+          v2[rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(pv));
+        }
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v2[0], v2[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p, o[nb], 0, 0, 0);
+      }
+    }
+  }
+
+  if (row_ok) {
+    const float inv = 1.f / l;
+    bf16* out = static_cast<bf16*>(a.ctx) + ((int64_t)b * a.seq + row) * a.ldc + hd * D;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float v[4] = {o[nb][4 * q] * inv, o[nb][4 * q + 1] * inv, o[nb][4 * q + 2] * inv, o[nb][4 * q + 3] * inv};
+        store4_bf16(out + 32 * nb + 8 * q + 4 * h, v);
+      }
+    if (h == 0) a.lse[(int64_t)z * a.seq + row] = m * kLn2 + logf(l);
+  }
+}
+
+// ---------------------------------------------------------------------------- backward
+// Head dim 128. Tiles [32 rows][128] that serve both row reads (ds_read_b128, 16 lanes on
+// 16 consecutive rows at one chunk) and transposing reads (a half-wave on 4 consecutive
+// rows x 4 chunks) use chunk ^ (4 (r & 3) | ((r >> 2) & 3)): 16 consecutive rows land on
+// 16 different 16-byte bank positions, and 4 consecutive rows in 4 different 64-byte
+// bank groups.
+__device__ __forceinline__ int dswz(int row, int chunk) { return chunk ^ (((row & 3) << 2) | ((row >> 2) & 3)); }
+
+constexpr int kBwdD = 128;
+
+// DMA of a [32][128] tile (dual swizzle) from rows r0.. of a column slice.
+__device__ __forceinline__ void dma_tile_dual(bf16* lds, __amdgpu_buffer_rsrc_t rsrc, int64_t ld, int r0,
+                                              int rows_left, int wave, int lane) {
+  constexpr int CPR = 16, RPI = 4, INSTR = 8;
+#pragma unroll
+  for (int i = 0; i < INSTR / 2; ++i) {
+    const int q = wave + i * 2;
+    const int r = q * RPI + lane / CPR, c = dswz(r, lane % CPR);
+    const uint32_t off = r < rows_left ? (uint32_t)(((int64_t)(r0 + r) * ld + c * 8) * 2) : 0xFFFFFFF0u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(lds + q * 512), 16, off, 0, 0, 0);
+  }
+}
+
+// Row read of a dual-swizzled tile: lane's row r32, 16-k step ks (B operand).
+__device__ __forceinline__ bf16x8 row_frag(const bf16* t, int r32, int ks, int h) {
+  return *reinterpret_cast<const bf16x8*>(t + r32 * kBwdD + (dswz(r32, 2 * ks + h) << 3));
+}
+// Transposing read of a dual-swizzled tile for output column block nb and 16-row slice
+// sl, matching the A operand taken from an accumulator (rows 16 sl + 4 h + 0..3 and
+// 16 sl + 8 + 4 h + 0..3 of the tile).
+__device__ __forceinline__ bf16x8 tr_frag(const bf16* t, int sl, int nb, int lane) {
+  const int h = lane >> 5;
+  const int col = 32 * nb + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  s16x4 v[2];
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    const int r = 16 * sl + 8 * rr + 4 * h + ((lane & 15) >> 2);
+    v[rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(t + r * kBwdD + (dswz(r, col >> 3) << 3) + (col & 7)));
+  }
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// bf16 operand of a 16-wide slice from accumulator registers 8 sl .. 8 sl + 7.
+__device__ __forceinline__ bf16x8 acc_operand(const float* v, int sl) {
+  bf16x8 p;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) p[e] = (bf16)v[8 * sl + e];
+  return p;
+}
+
+__device__ __forceinline__ void store_rows(bf16* out, const f32x16* acc, float scale, int h) {
+#pragma unroll
+  for (int nb = 0; nb < kBwdD / 32; ++nb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float v[4] = {acc[nb][4 * q] * scale, acc[nb][4 * q + 1] * scale, acc[nb][4 * q + 2] * scale,
+                    acc[nb][4 * q + 3] * scale};
+      store4_bf16(out + 32 * nb + 8 * q + 4 * h, v);
+    }
+}
+
+// dK and dV. Work-group: 64 keys (wave w: keys 64 kb + 32 w ..) of sequence b, head k;
+// streams the query blocks (32 queries) that see them. Lane l owns key (l & 31); the
+// accumulators of S^T and dP^T hold queries 8 q + 4 (l >> 5) + j in register 4 q + j.
+//   P^T = exp(S^T / sqrt(d) - L[q]) (0 above the diagonal), dV += P^T dO,
+//   dS^T = P^T * (dP^T - D[q]) with dP^T = V dO^T, dK += dS^T Q / sqrt(d).
+// Per stage: Q_hi, Q_lo, dO tiles, then 1 KB for L and 1 KB for D of the 32 queries (one
+// DMA instruction each, wave 0 and wave 1; the first 128 bytes carry the values).
+constexpr int kKvStage = 3 * 32 * kBwdD + 1024;
+constexpr int kQStage = 3 * 32 * kBwdD;
+
+__device__ __forceinline__ void flash_bwd_kv(const FlashArgs& a, int kblk, int z, bf16* smem) {
+  constexpr int D = kBwdD, KS = D / 16, NB = D / 32, TILE = 32 * D, STAGE = kKvStage;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 5, r32 = lane & 31;
+  const int b = z / a.heads, hd = z % a.heads;
+  const int key = kblk * 64 + wave * 32 + r32;
+  const bool key_ok = key < a.seq;
+
+  const bf16* qkv = static_cast<const bf16*>(a.qkv) + (int64_t)b * a.seq * a.ldq;
+  const bf16* qlo = static_cast<const bf16*>(a.qkv_lo) + (int64_t)b * a.seq * a.ldq;
+  const bf16* dO = static_cast<const bf16*>(a.dctx) + (int64_t)b * a.seq * a.ldc + hd * D;
+  const int cq = hd * D, ck = a.hs + hd * D, cv = 2 * a.hs + hd * D;
+
+  bf16x8 kh[KS], kl[KS], vv[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (key_ok) {
+      const int64_t o = (int64_t)key * a.ldq + 16 * ks + 8 * h;
+      kh[ks] = *reinterpret_cast<const bf16x8*>(qkv + o + ck);
+      kl[ks] = *reinterpret_cast<const bf16x8*>(qlo + o + ck);
+      vv[ks] = *reinterpret_cast<const bf16x8*>(qkv + o + cv);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kh[ks][e] = kl[ks][e] = vv[ks][e] = (bf16)0.f;
+    }
+  }
+  const __amdgpu_buffer_rsrc_t rq = seq_rsrc(qkv + cq, a.ldq, a.seq);
+  const __amdgpu_buffer_rsrc_t rql = seq_rsrc(qlo + cq, a.ldq, a.seq);
+  const __amdgpu_buffer_rsrc_t rdo = seq_rsrc(dO, a.ldc, a.seq);
+  // L and D rows of this (sequence, head): seq floats each; reads past them return 0.
+  const __amdgpu_buffer_rsrc_t rl =
+      __builtin_amdgcn_make_buffer_rsrc(a.lse + (int64_t)z * a.seq, (short)0, a.seq * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rd =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.D) + (int64_t)z * a.seq, (short)0, a.seq * 4, 0x00020000);
+  const int qb0 = (kblk * 64) / 32, nqb = (a.seq + 31) / 32;
+  const int nsteps = nqb - qb0;
+  auto issue = [&](int t) {
+    bf16* st = smem + (t % kStages) * STAGE;
+    const int r0 = (qb0 + t) * 32, left = a.seq - r0;
+    dma_tile_dual(st, rq, a.ldq, r0, left, wave, lane);
+    dma_tile_dual(st + TILE, rql, a.ldq, r0, left, wave, lane);
+    dma_tile_dual(st + 2 * TILE, rdo, a.ldc, r0, left, wave, lane);
+    // lanes 0..7 of one instruction fetch the 32 floats; the others read past the range
+    const uint32_t off = lane < 8 ? (uint32_t)((r0 + 4 * lane) * 4) : 0xFFFFFFF0u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(wave == 0 ? rl : rd, (lds_ptr_t)(st + 3 * TILE + wave * 512), 16, off, 0,
+                                             0, 0);
+  };
+
+  const float scale2 = a.scale * kLog2e;
+  f32x16 dv[NB], dk[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dv[nb][r] = dk[nb][r] = 0.f;
+
+  // Per wave: 3 tiles of 8 DMA instructions over 2 waves, plus one for L or D.
+  constexpr int LOADS = 3 * 8 / 2 + 1;
+  if (nsteps > 0) issue(0);
+  if (nsteps > 1) issue(1);
+  for (int t = 0; t < nsteps; ++t) {
+    if (t + 1 < nsteps) wait_vmcnt<LOADS>();
+    else wait_vmcnt<0>();
+    dma_barrier();
+    if (t + 2 < nsteps) issue(t + 2);
+    const bf16* sQ = smem + (t % kStages) * STAGE;
+    const bf16* sQl = sQ + TILE;
+    const bf16* sO = sQ + 2 * TILE;
+    const int q0 = (qb0 + t) * 32, k0 = kblk * 64 + wave * 32;
+    // Queries of this block vs this wave's keys (starts are multiples of 32): all see
+    // them, the diagonal block, or none.
+    const bool masked = q0 == k0 || q0 + 32 > a.seq;
+    if (q0 < k0) continue;
+    // L and D of this lane's 16 query columns (4 runs of 4 consecutive queries).
+    const float* sL = reinterpret_cast<const float*>(sQ + 3 * TILE);
+    float l2[16], dq[16];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const f32x4 lv = *reinterpret_cast<const f32x4*>(sL + 8 * qq + 4 * h);
+      const f32x4 dv4 = *reinterpret_cast<const f32x4*>(sL + 256 + 8 * qq + 4 * h);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        l2[4 * qq + j] = lv[j] * kLog2e;
+        dq[4 * qq + j] = dv4[j];
+      }
+    }
+    f32x16 st, dpt;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st[r] = dpt[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 qf = row_frag(sQ, r32, ks, h), qfl = row_frag(sQl, r32, ks, h), of = row_frag(sO, r32, ks, h);
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, kh[ks], st, 0, 0, 0);
+      dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(of, vv[ks], dpt, 0, 0, 0);
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, kl[ks], st, 0, 0, 0);
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qfl, kh[ks], st, 0, 0, 0);
+    }
+    float p[16], ds[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(st[r], scale2, -l2[r]));
+    if (masked) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int q = q0 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (key > q || q >= a.seq) p[r] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ds[r] = p[r] * (dpt[r] - dq[r]);
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      const bf16x8 pp = acc_operand(p, sl), dd = acc_operand(ds, sl);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        dv[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(sO, sl, nb, lane), pp, dv[nb], 0, 0, 0);
+        dk[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(sQ, sl, nb, lane), dd, dk[nb], 0, 0, 0);
+      }
+    }
+  }
+  if (key_ok) {
+    bf16* out = static_cast<bf16*>(a.dqkv) + ((int64_t)b * a.seq + key) * a.ldq;
+    store_rows(out + ck, dk, a.scale, h);
+    store_rows(out + cv, dv, 1.f, h);
+  }
+}
+
+// dQ. Work-group: 64 query rows of sequence b, head k; streams the key blocks (32 keys)
+// they see. Lane l owns query row (l & 31).
+//   P = exp(S / sqrt(d) - L), dS = P * (dO V^T - D), dQ += dS K / sqrt(d).
+__device__ __forceinline__ void flash_bwd_q(const FlashArgs& a, int qb, int z, bf16* smem) {
+  constexpr int D = kBwdD, KS = D / 16, NB = D / 32, TILE = 32 * D;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 5, r32 = lane & 31;
+  const int b = z / a.heads, hd = z % a.heads;
+  const int row = qb * kFlashRows + wave * 32 + r32;
+  const bool row_ok = row < a.seq;
+
+  const bf16* qkv = static_cast<const bf16*>(a.qkv) + (int64_t)b * a.seq * a.ldq;
+  const bf16* qlo = static_cast<const bf16*>(a.qkv_lo) + (int64_t)b * a.seq * a.ldq;
+  const bf16* dO = static_cast<const bf16*>(a.dctx) + (int64_t)b * a.seq * a.ldc + hd * D;
+  const int cq = hd * D, ck = a.hs + hd * D, cv = 2 * a.hs + hd * D;
+  const int rc = min(row, a.seq - 1);
+  const float l2 = a.lse[(int64_t)z * a.seq + rc] * kLog2e;
+  const float drow = a.D[(int64_t)z * a.seq + rc];
+
+  bf16x8 qh[KS], ql[KS], of[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (row_ok) {
+      const int64_t o = (int64_t)row * a.ldq + 16 * ks + 8 * h;
+      qh[ks] = *reinterpret_cast<const bf16x8*>(qkv + o + cq);
+      ql[ks] = *reinterpret_cast<const bf16x8*>(qlo + o + cq);
+      of[ks] = *reinterpret_cast<const bf16x8*>(dO + (int64_t)row * a.ldc + 16 * ks + 8 * h);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qh[ks][e] = ql[ks][e] = of[ks][e] = (bf16)0.f;
+    }
+  }
+  const __amdgpu_buffer_rsrc_t rk = seq_rsrc(qkv + ck, a.ldq, a.seq);
+  const __amdgpu_buffer_rsrc_t rkl = seq_rsrc(qlo + ck, a.ldq, a.seq);
+  const __amdgpu_buffer_rsrc_t rv = seq_rsrc(qkv + cv, a.ldq, a.seq);
+  const int kend = min(a.seq, (qb + 1) * kFlashRows);
+  const int nsteps = (kend + 31) / 32;
+  auto issue = [&](int t) {
+    bf16* st = smem + (t % kStages) * 3 * TILE;
+    const int r0 = t * 32, left = a.seq - r0;
+    dma_tile_dual(st, rk, a.ldq, r0, left, wave, lane);
+    dma_tile_dual(st + TILE, rkl, a.ldq, r0, left, wave, lane);
+    dma_tile_dual(st + 2 * TILE, rv, a.ldq, r0, left, wave, lane);
+  };
+
+  const float scale2 = a.scale * kLog2e;
+  f32x16 dq[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[nb][r] = 0.f;
+
+  constexpr int LOADS = 3 * 8 / 2;  // per wave: 3 tiles of 8 DMA instructions, over 2 waves
+  issue(0);
+  if (nsteps > 1) issue(1);
+  for (int t = 0; t < nsteps; ++t) {
+    if (t + 1 < nsteps) wait_vmcnt<LOADS>();
+    else wait_vmcnt<0>();
+    dma_barrier();
+    if (t + 2 < nsteps) issue(t + 2);
+    const bf16* sK = smem + (t % kStages) * 3 * TILE;
+    const bf16* sKl = sK + TILE;
+    const bf16* sV = sK + 2 * TILE;
+    // Keys of this block vs this wave's rows (starts are multiples of 32): all visible,
+    // the diagonal block, or none.
+    const int kb = t * 32, r0 = qb * kFlashRows + wave * 32;
+    if (kb > r0) continue;
+    f32x16 s, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 kf = row_frag(sK, r32, ks, h), kfl = row_frag(sKl, r32, ks, h), vf = row_frag(sV, r32, ks, h);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qh[ks], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, of[ks], dp, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfl, qh[ks], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, ql[ks], s, 0, 0, 0);
+    }
+    float ds[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ds[r] = __builtin_amdgcn_exp2f(fmaf(s[r], scale2, -l2));
+    if (kb == r0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (kb + 8 * (r >> 2) + 4 * h + (r & 3) > row) ds[r] = 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ds[r] *= dp[r] - drow;
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      const bf16x8 dd = acc_operand(ds, sl);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        dq[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(sK, sl, nb, lane), dd, dq[nb], 0, 0, 0);
+    }
+  }
+  if (row_ok) store_rows(static_cast<bf16*>(a.dqkv) + ((int64_t)b * a.seq + row) * a.ldq + cq, dq, a.scale, h);
+}
+
+// Both backward parts in one grid, each walking its deepest blocks first: blockIdx.x
+// interleaves them (even: key block x / 2 of dK, dV; odd: row block of dQ, deepest
+// first), so the grid's critical path is the longer of the two chains, not their sum.
+__global__ __launch_bounds__(128) void flash_bwd_kernel(FlashArgs a) {
+  constexpr int SMEM = kStages * (kKvStage > kQStage ? kKvStage : kQStage);
+  __shared__ __attribute__((aligned(1024))) bf16 smem[SMEM];
+  dma_lds_escape(smem);
+  const int x = (int)blockIdx.x, z = blockIdx.y;
+  const int nqb = (a.seq + kFlashRows - 1) / kFlashRows, nkb = (a.seq + 63) / 64;
+  if ((x & 1) == 0) {
+    if (x / 2 < nkb) flash_bwd_kv(a, x / 2, z, smem);
+  } else {
+    if (x / 2 < nqb) flash_bwd_q(a, nqb - 1 - x / 2, z, smem);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_flash_bwd(const FlashArgs& a, int d, hipStream_t s) {
+  if (a.seq <= 0 || a.batch <= 0 || a.heads <= 0) return hipSuccess;
+  if (d != kBwdD) return hipErrorInvalidValue;
+  const int nqb = (a.seq + kFlashRows - 1) / kFlashRows, nkb = (a.seq + 63) / 64;
+  const int n = 2 * (nqb > nkb ? nqb : nkb);
+  hipLaunchKernelGGL(flash_bwd_kernel, dim3(n, a.batch * a.heads), dim3(128), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_flash_fwd(const FlashArgs& a, int d, hipStream_t s) {
+  if (a.seq <= 0 || a.batch <= 0 || a.heads <= 0) return hipSuccess;
+  const dim3 grid((a.seq + kFlashRows - 1) / kFlashRows, a.batch * a.heads);
+  if (d == 128) hipLaunchKernelGGL(flash_fwd_kernel<128>, grid, dim3(128), 0, s, a);
+  else if (d == 64) hipLaunchKernelGGL(flash_fwd_kernel<64>, grid, dim3(128), 0, s, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace mt

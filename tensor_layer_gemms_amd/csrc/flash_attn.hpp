@@ -1,0 +1,43 @@
+// Fused causal attention of the layer shard's heads (bf16 path, head dim 64 or 128).
+//
+// Forward: a work-group owns 64 query rows of one (sequence, head) and streams the keys
+// in blocks of 32 through LDS (DMA loads, two stages). Per block it forms the logits
+// S = (Q_hi K_hi^T + Q_hi K_lo^T + Q_lo K_hi^T) / sqrt(d) on the matrix cores, applies the
+// causal mask, updates the running row maximum and exponential sum (online softmax) and
+// accumulates O += P V with P taken straight from the logit accumulators (rounded to
+// bf16 as the matrix-core operand). S and P never reach HBM. It writes ctx = O / l and
+// the row log-sum-exp L = m + ln(l), from which the backward recomputes
+// P = exp(S - L).
+//
+// Attention and its causal mask follow the layer definition of the "Megatron-LM" concept
+// report (compassingai.com), section 4.1 (the attention heads of a rank); the fused,
+// tiled form is the FlashAttention approach the same pages cite for long sequences.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mt {
+
+struct FlashArgs {
+  const void* qkv;     // [B seq, ldq] bf16: Q of head k at column k d, K at hs + k d, V at 2 hs + k d
+  const void* qkv_lo;  // same layout: rounding remainders of Q and K
+  void* ctx;           // [B seq, ldc] bf16: head k at column k d
+  float* lse;          // [B, heads, seq] fp32 natural-log row log-sum-exp
+  const void* dctx;    // backward: dL/dctx, layout of ctx
+  const float* D;      // backward: rowsum(dctx * ctx) [B, heads, seq]
+  void* dqkv;          // backward: layout of qkv (dQ, dK, dV of every head)
+  int64_t ldq, ldc;
+  int batch, heads, seq, hs;
+  float scale;         // 1 / sqrt(d)
+};
+
+// Head dims the fused kernels handle (forward and backward).
+inline bool flash_supported(int d) { return d == 128; }
+
+// Forward: ctx and lse from qkv, qkv_lo (d = 64 or 128).
+hipError_t launch_flash_fwd(const FlashArgs& a, int d, hipStream_t s);
+// Backward: dQ, dK, dV into dqkv from qkv, qkv_lo, dctx, lse and D (d = 128).
+hipError_t launch_flash_bwd(const FlashArgs& a, int d, hipStream_t s);
+
+}  // namespace mt

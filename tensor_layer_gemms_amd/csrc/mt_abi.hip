@@ -11,6 +11,7 @@
 #include <string>
 #include <vector>
 
+#include "flash_attn.hpp"
 #include "gemm.hpp"
 #include "mt.h"
 #include "rowwise.hpp"
@@ -24,6 +25,7 @@ constexpr float kLnEps = 1e-5f;  // LayerNorm epsilon (silent on the pages; comm
 struct Dims {
   int64_t M, h, heads, at, d, seq, B, tp, hs, qkv, ft;
   bool bf16;
+  bool flash;  // fused attention kernels (bf16 path, head dims they support)
   int64_t es;  // bytes per activation element
 };
 
@@ -52,6 +54,7 @@ int validate_shape(const mt_shape* s, Dims* out) {
   x.qkv = 3 * x.hs;
   x.ft = 4 * x.h / x.tp;
   x.bf16 = s->dtype == MT_BF16;
+  x.flash = x.bf16 && flash_supported((int)d);
   x.es = x.bf16 ? 2 : 4;
   *out = x;
   return MT_OK;
@@ -78,6 +81,9 @@ struct LayerSaved {
   float *mean1, *rstd1, *mean2, *rstd2;
   float* x2;  // residual stream X + O + b_o, fp32
   void *u, *qkv, *p, *ctx, *v2, *a, *z;
+  // fused attention (instead of P): row log-sum-exp [B, a_t, s] and the Q, K remainders
+  float* lse;
+  void* qkv_lo;
 };
 
 size_t carve_layer_saved(const Dims& d, void* base, LayerSaved* s) {
@@ -88,7 +94,9 @@ size_t carve_layer_saved(const Dims& d, void* base, LayerSaved* s) {
   s->rstd2 = c.take<float>(d.M * 4);
   s->u = c.take(d.M * d.h * d.es);
   s->qkv = c.take(d.M * d.qkv * d.es);
-  s->p = c.take(d.B * d.at * d.seq * d.seq * d.es);
+  s->p = d.flash ? nullptr : c.take(d.B * d.at * d.seq * d.seq * d.es);
+  s->lse = d.flash ? c.take<float>(d.B * d.at * d.seq * 4) : nullptr;
+  s->qkv_lo = d.flash ? c.take(d.M * d.qkv * 2) : nullptr;
   s->ctx = c.take(d.M * d.hs * d.es);
   s->x2 = c.take<float>(d.M * d.h * 4);
   s->v2 = c.take(d.M * d.h * d.es);
@@ -107,10 +115,11 @@ struct LayerFwdWs {
 size_t carve_layer_fwd_ws(const Dims& d, void* base, LayerFwdWs* w) {
   Carver c(base);
   const int64_t qkv_partials = d.bf16 ? d.M * (d.qkv + 2 * d.hs) : 0;
-  w->S = c.take<float>(std::max<int64_t>(d.B * d.at * d.seq * d.seq, qkv_partials) * 4);
+  const int64_t scores = d.flash ? 0 : d.B * d.at * d.seq * d.seq;
+  w->S = c.take<float>(std::max<int64_t>(scores, qkv_partials) * 4);
   w->o = c.take(d.M * d.h * d.es);
   w->u_lo = d.bf16 ? c.take(d.M * d.h * 2) : nullptr;
-  w->qkv_lo = d.bf16 ? c.take(d.M * d.qkv * 2) : nullptr;
+  w->qkv_lo = d.bf16 && !d.flash ? c.take(d.M * d.qkv * 2) : nullptr;  // saved with fused attention
   return c.off;
 }
 
@@ -146,7 +155,7 @@ size_t carve_layer_bwd_ws(const Dims& d, void* base, LayerBwdWs* w) {
   w->dx2 = c.take(d.M * d.h * d.es);
   w->dx2f = c.take<float>(d.M * d.h * 4);
   w->dctx = c.take(d.M * d.hs * d.es);
-  w->ds = c.take(d.B * d.at * d.seq * d.seq * d.es);
+  w->ds = d.flash ? nullptr : c.take(d.B * d.at * d.seq * d.seq * d.es);
   w->dqkv = c.take(d.M * d.qkv * d.es);
   w->D = c.take<float>(d.B * d.at * d.seq * 4);
   w->part = c.take<float>(colsum_floats(d) * 4);
@@ -291,6 +300,24 @@ struct Attn {
   }
 };
 
+// Arguments of the fused attention kernels for this shard.
+FlashArgs flash_args(const Dims& d, const void* qkv, const void* qkv_lo, void* ctx, float* lse, float scale) {
+  FlashArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.qkv = qkv;
+  a.qkv_lo = qkv_lo;
+  a.ctx = ctx;
+  a.lse = lse;
+  a.ldq = d.qkv;
+  a.ldc = d.hs;
+  a.batch = (int)d.B;
+  a.heads = (int)d.at;
+  a.seq = (int)d.seq;
+  a.hs = (int)d.hs;
+  a.scale = scale;
+  return a;
+}
+
 // ------------------------------------------------------------------------- forward
 int layer_fwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, void* out, const LayerSaved& sv,
                    const LayerFwdWs& ws, hipStream_t stream) {
@@ -301,6 +328,7 @@ int layer_fwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, void
   const float scale = 1.0f / std::sqrt((float)d.d);
   const int batch = (int)(d.B * d.at);
   Attn at{d};
+  void* qkv_lo = d.flash ? sv.qkv_lo : ws.qkv_lo;  // Q, K remainders (kept for the backward when fused)
 
   // F1 LayerNorm 1 (bf16 path: also the rounding remainder U_lo of U)
   q.run("ln1_fwd", 0, Mh * es * (bf ? 3 : 2), [&] {
@@ -324,7 +352,7 @@ int layer_fwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, void
     const GemmArgs glo = plain(ws.u_lo, d.h, w.w_qkv, d.h, lo, 2 * d.hs, d.M, 2 * d.hs, d.h);
     const hipError_t e = launch_gemm_bf16_pair(ghi, true, true, EPI_STORE_F32, glo, true, true, EPI_STORE_F32, stream);
     if (e == hipSuccess)
-      return launch_qkv_finish(hi, lo, w.b_qkv, sv.qkv, ws.qkv_lo, (int)d.M, (int)d.qkv, (int)(2 * d.hs), stream);
+      return launch_qkv_finish(hi, lo, w.b_qkv, sv.qkv, qkv_lo, (int)d.M, (int)d.qkv, (int)(2 * d.hs), stream);
     if (e != hipErrorNotSupported) return e;
     // Operands the paired launch cannot address: one GEMM with a second K segment for
     // the Q and K columns.
@@ -332,47 +360,57 @@ int layer_fwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, void
     g.seg_b[1] = w.w_qkv;
     g.nseg = 2;
     g.seg_n = (int)(2 * d.hs);
-    g.C2 = ws.qkv_lo;
+    g.C2 = qkv_lo;
     return gemm(d, g, true, true, EPI_BIAS_SPLIT, 1, stream);
   });
-  // F3 scores S = Q K^T / sqrt(d), causal tiles only, fp32 (bf16 path:
-  // Q_hi K_hi^T + Q_hi K_lo^T + Q_lo K_hi^T)
-  q.run("attn_scores", at.flops() * (bf ? 3 : 1), 0, [&] {
-    GemmArgs g = plain(sv.qkv, d.qkv, static_cast<const char*>(sv.qkv) + d.hs * d.es, d.qkv, ws.S, d.seq, d.seq,
-                       d.seq, d.d);
-    if (bf) {
-      const char* lo = static_cast<const char*>(ws.qkv_lo);
-      g.seg_a[1] = sv.qkv;
-      g.seg_b[1] = lo + d.hs * d.es;
-      g.seg_a[2] = lo;
-      g.seg_b[2] = static_cast<const char*>(sv.qkv) + d.hs * d.es;
-      g.nseg = 3;
-    }
-    at.head_operand(d.qkv, g.a_so, g.a_si);
-    at.head_operand(d.qkv, g.b_so, g.b_si);
-    g.c_so = d.at * d.seq * d.seq;
-    g.c_si = d.seq * d.seq;
-    g.zdiv = (int)d.at;
-    g.causal = CAUSAL_SKIP_UPPER;
-    g.alpha = scale;
-    return gemm(d, g, true, true, EPI_STORE_F32, batch, stream);
-  });
-  // F4 causal softmax -> P
-  q.run("softmax_fwd", 0, (double)batch * at.causal_pairs() * (4 + es), [&] {
-    return launch_softmax_causal(bf, ws.S, sv.p, batch, (int)d.seq, stream);
-  });
-  // F5 ctx = P V (k <= q), heads concatenated in columns
-  q.run("attn_ctx", at.flops(), 0, [&] {
-    GemmArgs g = plain(sv.p, d.seq, static_cast<const char*>(sv.qkv) + 2 * d.hs * d.es, d.qkv, sv.ctx, d.hs, d.seq,
-                       d.d, d.seq);
-    g.a_so = d.at * d.seq * d.seq;
-    g.a_si = d.seq * d.seq;
-    at.head_operand(d.qkv, g.b_so, g.b_si);
-    at.head_operand(d.hs, g.c_so, g.c_si);
-    g.zdiv = (int)d.at;
-    g.causal = CAUSAL_K_LE_M;
-    return gemm(d, g, true, false, EPI_STORE, batch, stream);
-  });
+  // F3-F5 causal attention. Fused (bf16, supported head dim): one kernel streams the keys
+  // through LDS with an online softmax and keeps S and P on chip; it saves the row
+  // log-sum-exp for the backward.
+  if (d.flash) {
+    q.run("attn_fwd", 2 * at.flops(), 0, [&] {
+      FlashArgs fa = flash_args(d, sv.qkv, qkv_lo, sv.ctx, sv.lse, scale);
+      return launch_flash_fwd(fa, (int)d.d, stream);
+    });
+  } else {
+    // F3 scores S = Q K^T / sqrt(d), causal tiles only, fp32 (bf16 path:
+    // Q_hi K_hi^T + Q_hi K_lo^T + Q_lo K_hi^T)
+    q.run("attn_scores", at.flops() * (bf ? 3 : 1), 0, [&] {
+      GemmArgs g = plain(sv.qkv, d.qkv, static_cast<const char*>(sv.qkv) + d.hs * d.es, d.qkv, ws.S, d.seq, d.seq,
+                         d.seq, d.d);
+      if (bf) {
+        const char* lo = static_cast<const char*>(qkv_lo);
+        g.seg_a[1] = sv.qkv;
+        g.seg_b[1] = lo + d.hs * d.es;
+        g.seg_a[2] = lo;
+        g.seg_b[2] = static_cast<const char*>(sv.qkv) + d.hs * d.es;
+        g.nseg = 3;
+      }
+      at.head_operand(d.qkv, g.a_so, g.a_si);
+      at.head_operand(d.qkv, g.b_so, g.b_si);
+      g.c_so = d.at * d.seq * d.seq;
+      g.c_si = d.seq * d.seq;
+      g.zdiv = (int)d.at;
+      g.causal = CAUSAL_SKIP_UPPER;
+      g.alpha = scale;
+      return gemm(d, g, true, true, EPI_STORE_F32, batch, stream);
+    });
+    // F4 causal softmax -> P
+    q.run("softmax_fwd", 0, (double)batch * at.causal_pairs() * (4 + es), [&] {
+      return launch_softmax_causal(bf, ws.S, sv.p, batch, (int)d.seq, stream);
+    });
+    // F5 ctx = P V (k <= q), heads concatenated in columns
+    q.run("attn_ctx", at.flops(), 0, [&] {
+      GemmArgs g = plain(sv.p, d.seq, static_cast<const char*>(sv.qkv) + 2 * d.hs * d.es, d.qkv, sv.ctx, d.hs, d.seq,
+                         d.d, d.seq);
+      g.a_so = d.at * d.seq * d.seq;
+      g.a_si = d.seq * d.seq;
+      at.head_operand(d.qkv, g.b_so, g.b_si);
+      at.head_operand(d.hs, g.c_so, g.c_si);
+      g.zdiv = (int)d.at;
+      g.causal = CAUSAL_K_LE_M;
+      return gemm(d, g, true, false, EPI_STORE, batch, stream);
+    });
+  }
   // F6 row-parallel out-projection: partial sum O_i (the all-reduce input)
   q.run("out_proj_fwd", gflop(d.M, d.h, d.hs), 0, [&] {
     GemmArgs g = plain(sv.ctx, d.hs, w.w_o, d.hs, ws.o, d.h, d.M, d.h, d.hs);
@@ -459,53 +497,65 @@ int layer_bwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, cons
   q.run("attn_rowdot", 0, 2.0 * d.M * d.hs * es, [&] {
     return launch_attn_rowdot(bf, ws.dctx, sv.ctx, ws.D, (int)d.B, (int)d.seq, (int)d.at, (int)d.d, stream);
   });
-  const char* qkv = static_cast<const char*>(sv.qkv);
-  char* dqkv = static_cast<char*>(ws.dqkv);
-  q.run("attn_dscores", at.flops(), 0, [&] {
-    GemmArgs g = plain(ws.dctx, d.hs, qkv + 2 * d.hs * d.es, d.qkv, ws.ds, d.seq, d.seq, d.seq, d.d);
-    at.head_operand(d.hs, g.a_so, g.a_si);
-    at.head_operand(d.qkv, g.b_so, g.b_si);
-    g.c_so = d.at * d.seq * d.seq;
-    g.c_si = d.seq * d.seq;
-    g.aux = sv.p;
-    g.vec = ws.D;
-    g.vec_bs = d.seq;
-    g.zdiv = (int)d.at;
-    g.causal = CAUSAL_SKIP_UPPER;
-    return gemm(d, g, true, true, EPI_DSOFTMAX, batch, stream);
-  });
-  q.run("attn_dv", at.flops(), 0, [&] {  // dV = P^T dctx (q >= j)
-    GemmArgs g = plain(sv.p, d.seq, ws.dctx, d.hs, dqkv + 2 * d.hs * d.es, d.qkv, d.seq, d.d, d.seq);
-    g.a_so = d.at * d.seq * d.seq;
-    g.a_si = d.seq * d.seq;
-    at.head_operand(d.hs, g.b_so, g.b_si);
-    at.head_operand(d.qkv, g.c_so, g.c_si);
-    g.zdiv = (int)d.at;
-    g.causal = CAUSAL_K_GE_M;
-    return gemm(d, g, false, false, EPI_STORE, batch, stream);
-  });
-  q.run("attn_dq", at.flops(), 0, [&] {  // dQ = dS K / sqrt(d) (j <= q)
-    GemmArgs g = plain(ws.ds, d.seq, qkv + d.hs * d.es, d.qkv, dqkv, d.qkv, d.seq, d.d, d.seq);
-    g.a_so = d.at * d.seq * d.seq;
-    g.a_si = d.seq * d.seq;
-    at.head_operand(d.qkv, g.b_so, g.b_si);
-    at.head_operand(d.qkv, g.c_so, g.c_si);
-    g.zdiv = (int)d.at;
-    g.causal = CAUSAL_K_LE_M;
-    g.alpha = scale;
-    return gemm(d, g, true, false, EPI_STORE, batch, stream);
-  });
-  q.run("attn_dk", at.flops(), 0, [&] {  // dK = dS^T Q / sqrt(d) (q >= j)
-    GemmArgs g = plain(ws.ds, d.seq, qkv, d.qkv, dqkv + d.hs * d.es, d.qkv, d.seq, d.d, d.seq);
-    g.a_so = d.at * d.seq * d.seq;
-    g.a_si = d.seq * d.seq;
-    at.head_operand(d.qkv, g.b_so, g.b_si);
-    at.head_operand(d.qkv, g.c_so, g.c_si);
-    g.zdiv = (int)d.at;
-    g.causal = CAUSAL_K_GE_M;
-    g.alpha = scale;
-    return gemm(d, g, false, false, EPI_STORE, batch, stream);
-  });
+  if (d.flash) {
+    // B5/B6 fused: P recomputed from Q, K and the saved log-sum-exp; dK, dV per key block
+    // and dQ per query block, each summed in one work-group (no atomics).
+    q.run("attn_bwd", 4 * at.flops(), 0, [&] {
+      FlashArgs fa = flash_args(d, sv.qkv, sv.qkv_lo, nullptr, sv.lse, scale);
+      fa.dctx = ws.dctx;
+      fa.D = ws.D;
+      fa.dqkv = ws.dqkv;
+      return launch_flash_bwd(fa, (int)d.d, stream);
+    });
+  } else {
+    const char* qkv = static_cast<const char*>(sv.qkv);
+    char* dqkv = static_cast<char*>(ws.dqkv);
+    q.run("attn_dscores", at.flops(), 0, [&] {
+      GemmArgs g = plain(ws.dctx, d.hs, qkv + 2 * d.hs * d.es, d.qkv, ws.ds, d.seq, d.seq, d.seq, d.d);
+      at.head_operand(d.hs, g.a_so, g.a_si);
+      at.head_operand(d.qkv, g.b_so, g.b_si);
+      g.c_so = d.at * d.seq * d.seq;
+      g.c_si = d.seq * d.seq;
+      g.aux = sv.p;
+      g.vec = ws.D;
+      g.vec_bs = d.seq;
+      g.zdiv = (int)d.at;
+      g.causal = CAUSAL_SKIP_UPPER;
+      return gemm(d, g, true, true, EPI_DSOFTMAX, batch, stream);
+    });
+    q.run("attn_dv", at.flops(), 0, [&] {  // dV = P^T dctx (q >= j)
+      GemmArgs g = plain(sv.p, d.seq, ws.dctx, d.hs, dqkv + 2 * d.hs * d.es, d.qkv, d.seq, d.d, d.seq);
+      g.a_so = d.at * d.seq * d.seq;
+      g.a_si = d.seq * d.seq;
+      at.head_operand(d.hs, g.b_so, g.b_si);
+      at.head_operand(d.qkv, g.c_so, g.c_si);
+      g.zdiv = (int)d.at;
+      g.causal = CAUSAL_K_GE_M;
+      return gemm(d, g, false, false, EPI_STORE, batch, stream);
+    });
+    q.run("attn_dq", at.flops(), 0, [&] {  // dQ = dS K / sqrt(d) (j <= q)
+      GemmArgs g = plain(ws.ds, d.seq, qkv + d.hs * d.es, d.qkv, dqkv, d.qkv, d.seq, d.d, d.seq);
+      g.a_so = d.at * d.seq * d.seq;
+      g.a_si = d.seq * d.seq;
+      at.head_operand(d.qkv, g.b_so, g.b_si);
+      at.head_operand(d.qkv, g.c_so, g.c_si);
+      g.zdiv = (int)d.at;
+      g.causal = CAUSAL_K_LE_M;
+      g.alpha = scale;
+      return gemm(d, g, true, false, EPI_STORE, batch, stream);
+    });
+    q.run("attn_dk", at.flops(), 0, [&] {  // dK = dS^T Q / sqrt(d) (q >= j)
+      GemmArgs g = plain(ws.ds, d.seq, qkv, d.qkv, dqkv + d.hs * d.es, d.qkv, d.seq, d.d, d.seq);
+      g.a_so = d.at * d.seq * d.seq;
+      g.a_si = d.seq * d.seq;
+      at.head_operand(d.qkv, g.b_so, g.b_si);
+      at.head_operand(d.qkv, g.c_so, g.c_si);
+      g.zdiv = (int)d.at;
+      g.causal = CAUSAL_K_GE_M;
+      g.alpha = scale;
+      return gemm(d, g, false, false, EPI_STORE, batch, stream);
+    });
+  }
   // B7 QKV: db_qkv, dW_qkv = dQKV^T U, dU = dQKV W_qkv (partial)
   q.run("db_qkv", 0, d.M * d.qkv * es, [&] {
     return launch_colsum(bf, 0, ws.dqkv, false, nullptr, false, nullptr, nullptr, gr.b_qkv, nullptr, ws.part, M,
