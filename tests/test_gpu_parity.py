@@ -81,6 +81,8 @@ def test_mlp_shards_sum_to_unsharded_block(dtype, tp):
     (320, 5, 136, 3, 1, 0),    # several tiles, ragged token and feature tails
     (640, 4, 264, 1, 2, 1),    # head dim 160, shard 1 of 2, ragged seq
     (512, 8, 520, 2, 2, 0),    # seq spanning three causal chunks
+    (512, 4, 200, 2, 2, 1),    # head dim 128 (fused attention): ragged query and key blocks
+    (1024, 8, 72, 3, 1, 0),    # head dim 128, short sequences, 3 sequences per micro-batch
 ])
 def test_layer_bf16_multi_tile(h, heads, seq, mb, tp, shard):
     shape = si.LayerShape(h=h, heads=heads, seq=seq, micro_batch=mb, tp=tp, shard=shard)
