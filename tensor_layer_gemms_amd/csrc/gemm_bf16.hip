@@ -113,6 +113,8 @@ bool dma_ok(const GemmArgs& g, bool a_k, bool b_k) {
   auto a16 = [](const void* p) { return ((uintptr_t)p & 15u) == 0; };
   if (g.M % 8 || g.N % 8 || g.K % 8 || g.lda % 8 || g.ldb % 8) return false;
   if (g.a_so % 8 || g.a_si % 8 || g.b_so % 8 || g.b_si % 8) return false;
+  // the staged epilogue writes 16-byte row chunks of C and C2
+  if (g.ldc % 8 || g.c_so % 8 || g.c_si % 8 || g.seg_n % 8 || !a16(g.C) || !a16(g.C2)) return false;
   for (int s = 0; s < g.nseg; ++s)
     if (!a16(g.seg_a[s]) || !a16(g.seg_b[s])) return false;
   const uint64_t lim = 0xFFFFFFF0ull;

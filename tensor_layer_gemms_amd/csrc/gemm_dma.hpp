@@ -142,6 +142,108 @@ struct FragReader {
   }
 };
 
+// LDS placement of the 16-byte chunks of a staged bf16 output tile [BM][BN]: chunk c of
+// row r sits at c ^ f(r), so the 16 consecutive rows that one accumulator write covers
+// fall in 16 different 16-byte bank groups (row pitch 0 mod 256 bytes for BN = 128, 256;
+// 128 mod 256 for BN = 192).
+template <int BN>
+__device__ __forceinline__ int epi_swz(int row, int chunk) {
+  static_assert(BN == 128 || BN == 192 || BN == 256, "staged tile widths");
+  if constexpr (BN == 192) return chunk ^ ((row >> 1) & 7);
+  else return chunk ^ (row & 15);
+}
+
+// Epilogue through LDS for bf16 outputs: the element-wise epilogue runs on the
+// accumulators, the values go to LDS (free once the last k-step has been read), and the
+// work-group then writes whole row segments with 16-byte stores, so every output cache
+// line is written at once instead of in 16-byte pieces from 32 rows per store.
+// One-output epilogues stage the whole tile in one round. Two-output epilogues (bias +
+// GeLU: a and GeLU(a); the bias split: hi and remainder) stage both outputs of one
+// 32-row accumulator block per wave at a time, TM rounds, so no value outlives its
+// round. Requires ldc, the batch strides and seg_n to be multiples of 8 and C, C2 to be
+// 16-byte aligned (checked on the host).
+template <int BM, int BN, int TM, int TN, int WM, int WN, int KIND>
+__device__ __forceinline__ void epi_staged(const GemmArgs& g, f32x16 (&acc)[TM][TN], bf16* smem, int m0, int n0,
+                                           int wm0, int wn0, int64_t coff, int64_t voff) {
+  constexpr bool TWO = KIND == EPI_BIAS_GELU || KIND == EPI_BIAS_SPLIT;
+  constexpr int NT = 64 * WM * WN, CPR = BN / 8;
+  constexpr int ROUNDS = TWO ? TM : 1, TR = TM / ROUNDS;  // accumulator blocks per round
+  constexpr int RROWS = BM / ROUNDS;                      // staged tile rows per round
+  constexpr int REGION = RROWS * BN;                      // elements per staged output
+  static_assert(RROWS * CPR % NT == 0, "drain splits evenly");
+  const int tid = threadIdx.x, lane = tid & 63, wr = wm0 / (BM / WM);
+  bf16* s0 = smem;
+  bf16* s1 = smem + REGION;
+  auto put = [&](bf16* region, int rho, int c, const float* v) {  // 4 values, staged row rho, columns c..c+3
+    store4_bf16(region + rho * BN + (epi_swz<BN>(rho, c >> 3) << 3) + (c & 7), v);
+  };
+  auto drain = [&](const bf16* region, void* dst, int round, int ncols) {
+#pragma unroll 2
+    for (int it = 0; it < RROWS * CPR / NT; ++it) {
+      const int id = it * NT + tid, rho = id / CPR, c = id % CPR;
+      const int r = (rho / (32 * TR)) * (BM / WM) + round * TR * 32 + rho % (32 * TR);
+      const int m = m0 + r, n = n0 + 8 * c;
+      const u32x4 w = *reinterpret_cast<const u32x4*>(region + rho * BN + (epi_swz<BN>(rho, c) << 3));
+      if (m < g.M && n < ncols) *reinterpret_cast<u32x4*>(static_cast<bf16*>(dst) + coff + (int64_t)m * g.ldc + n) = w;
+    }
+  };
+
+#pragma unroll
+  for (int round = 0; round < ROUNDS; ++round) {
+    dma_barrier();  // the operand stages, or the previous round, have been read
+#pragma unroll
+    for (int ii = 0; ii < TR; ++ii) {
+      const int i = round * TR + ii;
+      const int rho = (wr * TR + ii) * 32 + (lane & 31);
+      const int m = m0 + wm0 + i * 32 + (lane & 31);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = wn0 + j * 32 + q * 8 + (lane >> 5) * 4, n = n0 + c;
+          const bool ok = m < g.M && n < g.N;
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
+          if constexpr (KIND == EPI_STORE) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] *= g.alpha;
+          } else if constexpr (KIND == EPI_BIAS || KIND == EPI_BIAS_GELU || KIND == EPI_BIAS_SPLIT) {
+            float b[4] = {0.f, 0.f, 0.f, 0.f};
+            if (ok) load4_bf16(static_cast<const bf16*>(g.vec) + n, b);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] += b[e];
+          } else if constexpr (KIND == EPI_DGELU) {
+            float a[4] = {0.f, 0.f, 0.f, 0.f};
+            if (ok) load4_bf16(static_cast<const bf16*>(g.aux) + coff + (int64_t)m * g.ldc + n, a);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] *= gelu_grad_f(a[e]);
+          } else if constexpr (KIND == EPI_DSOFTMAX) {
+            float p[4] = {0.f, 0.f, 0.f, 0.f};
+            float d = 0.f;
+            if (ok) {
+              load4_bf16(static_cast<const bf16*>(g.aux) + coff + (int64_t)m * g.ldc + n, p);
+              d = static_cast<const float*>(g.vec)[voff + m];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = p[e] * (g.alpha * v[e] - d);
+          }
+          put(s0, rho, c, v);
+          if constexpr (TWO) {
+            float w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = KIND == EPI_BIAS_GELU ? gelu_f(v[e]) : v[e] - (float)(bf16)v[e];
+            put(s1, rho, c, w);
+          }
+        }
+      }
+    }
+    dma_barrier();
+    drain(s0, g.C, round, g.N);
+    if constexpr (TWO) drain(s1, g.C2, round, KIND == EPI_BIAS_SPLIT ? min(g.N, g.seg_n) : g.N);
+  }
+}
+
 // One output tile: bid = tile index of the problem, z = batch index, smem = the
 // launch's LDS ring (at least NS (BM + BN) BK elements).
 template <bool A_K, bool B_K, int BM, int BN, int BK, int NS, int WM, int WN, int KIND>
@@ -247,18 +349,23 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs& g, int bid, int z,
 
   const int64_t coff = zo * g.c_so + zi * g.c_si;
   const int64_t voff = (int64_t)z * g.vec_bs;
+  if constexpr (KIND == EPI_STORE_F32) {
+    // fp32 tiles do not fit the LDS ring; each lane stores its 16-byte row pieces.
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int m = m0 + wm0 + i * 32 + (lane & 31);
+    for (int i = 0; i < TM; ++i) {
+      const int m = m0 + wm0 + i * 32 + (lane & 31);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
+      for (int j = 0; j < TN; ++j) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn0 + j * 32 + q * 8 + (lane >> 5) * 4;
-        float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-        if (m < g.M && n < g.N) epi_store4<KIND>(g, coff, voff, m, n, v);
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + wn0 + j * 32 + q * 8 + (lane >> 5) * 4;
+          float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          if (m < g.M && n < g.N) epi_store4<KIND>(g, coff, voff, m, n, v);
+        }
       }
     }
+  } else {
+    epi_staged<BM, BN, TM, TN, WM, WN, KIND>(g, acc, smem, m0, n0, wm0, wn0, coff, voff);
   }
 }
 
