@@ -252,6 +252,9 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs& g, int bid, int z,
   constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
   constexpr int STAGE = (BM + BN) * BK;  // bf16 elements per stage
   static_assert(TM >= 1 && TN >= 1 && BM % (WM * 32) == 0 && BN % (WN * 32) == 0, "wave tile of 32x32 blocks");
+  static_assert(KIND == EPI_STORE_F32 ||
+                    ((KIND == EPI_BIAS_GELU || KIND == EPI_BIAS_SPLIT) ? 2 * (BM / TM) * BN : BM * BN) <= NS * STAGE,
+                "the staged epilogue fits the LDS ring");
 
   dma_lds_escape(smem);
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
