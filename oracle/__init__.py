@@ -13,8 +13,10 @@ gradient; the pages' tensor-parallel invariant (sum over shards of
 f(X A_i) B_i equals f(X A) B) forward and backward; brute-force per-element
 attention loops; closed forms of LayerNorm, GeLU, the causal first query, a zero
 query projection and a zeroed residual branch; and torch's fp64 CPU functional ops
-with autograd as an independent library cross-check. No function is parity unpinned.
+with autograd as an independent library cross-check. adamw_step (oracle/adamw.py) is
+pinned in tests/test_oracle_adamw.py. No function is parity unpinned.
 """
+from .adamw import adamw_step  # noqa: F401
 from .layer import (  # noqa: F401
     EPS,
     attention_bwd,

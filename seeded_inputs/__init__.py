@@ -298,3 +298,35 @@ def model_flops(shape: LayerShape, causal: bool = True) -> float:
     pairs = s * (s + 1) / 2 if causal else s * s
     attn = 2 * 2 * B * (h // t) * pairs
     return 3.0 * (gemm + attn)
+
+
+# ------------------------------------------------------------------ optimizer step
+PURPOSE_ADAM = 4
+
+# Hyperparameters of the AdamW step workload. beta1, beta2 and the peak learning rate
+# are the typical 175B settings listed on the oreateai.com Megatron-LM analysis
+# ("In-Depth Analysis of Distributed Training Frameworks for Large Models ...
+# Megatron-LM"), section 3.1; eps and the weight decay are not given there (1e-8 and
+# 0.1 are the common GPT values); step 1000 is an arbitrary mid-training step.
+ADAM_HPARAMS = dict(lr=6e-5, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=1000, grad_scale=1.0)
+
+
+def shard_param_count(shape: LayerShape) -> int:
+    """Parameters one tensor-parallel rank owns for one layer (every tensor of
+    mt_layer_weights, the replicated LayerNorm and row-parallel biases included)."""
+    h, t = shape.h, shape.tp
+    ht, ft = h // t, 4 * h // t
+    return (3 * ht * h + 3 * ht) + (h * ht + h) + (ft * h + ft) + (h * ft + h) + 4 * h
+
+
+def adam_case(n: int, seed: int = 0):
+    """fp32 master parameters, gradient and Adam moments for n parameters: p ~ N(0,
+    0.02) like the weights, g ~ N(0, 1e-3), m ~ N(0, 3e-4) and v = (N(0, 1e-3))^2 +
+    1e-10 (a second moment of gradients of that size). Each array from its own keyed
+    stream."""
+    key = lambda tid: keyed_rng(seed, PURPOSE_ADAM, 0, 0, tid)  # noqa: E731
+    p = key(0).standard_normal(n, dtype=np.float32) * np.float32(WEIGHT_STD)
+    g = key(1).standard_normal(n, dtype=np.float32) * np.float32(1e-3)
+    m = key(2).standard_normal(n, dtype=np.float32) * np.float32(3e-4)
+    v = np.square(key(3).standard_normal(n, dtype=np.float32) * np.float32(1e-3)) + np.float32(1e-10)
+    return p, g, m, v
