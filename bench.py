@@ -8,7 +8,9 @@ shard 0 of tp=8 (h=12288, 12 of 96 heads of 128, seq 2048, micro-batch 1, bf16).
 Reported (one JSON line): model TFLOP/s = 3 x (forward GEMM + causal attention FLOPs)
 per step / step time, its fraction of the MI355X dense bf16 MFMA peak, the roofline
 of the dominant kernel (timed live with HIP events on the library's stream around
-that kernel's launches inside the timed steps), and the fp64 oracle timed on the host.
+that kernel's launches inside the timed steps), the fp64 oracle timed on the host, and
+(outside the timed steps) the fused AdamW step over the shard's parameters against HBM
+bandwidth.
 """
 from __future__ import annotations
 
@@ -67,6 +69,7 @@ def parse():
     ap.add_argument("--dominant", default="fc1_fwd",
                     help="label of the kernel launch whose roofline is reported")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-optimizer", action="store_true", help="skip the fused AdamW step measurement")
     ap.add_argument("--breakdown", action="store_true", help="also print a per-launch time breakdown (stderr)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes three times (counter calibration)")
@@ -82,6 +85,34 @@ def copy_probe(nbytes: int) -> None:
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes": nbytes}), flush=True)
+
+
+def optimizer_step(mt, si, torch, shape, stream, warmup: int = 2, iters: int = 10):
+    """Fused AdamW step over the shard's parameters in one flat fp32 buffer (with the
+    bf16 copy): average launch time from HIP events on the library's stream, against
+    HBM bandwidth (30 bytes per parameter: read p, g, m, v; write p, m, v, bf16 p)."""
+    n = si.shard_param_count(shape)
+    print(f"[bench] AdamW step over {n} parameters", file=sys.stderr, flush=True)
+    bufs = [torch.from_numpy(a).cuda() for a in si.adam_case(n, seed=0)]
+    q = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    hp = si.ADAM_HPARAMS
+    for _ in range(warmup):
+        mt.adamw_step(*bufs, q, stream=stream, **hp)
+    torch.cuda.synchronize()
+    mt.timing_reset()
+    mt.timing_enable(True, "adamw")
+    for _ in range(iters):
+        mt.adamw_step(*bufs, q, stream=stream, **hp)
+    torch.cuda.synchronize()
+    mt.timing_enable(False)
+    recs = [r for r in mt.timing_records() if r[0] == "adamw"]
+    mt.timing_reset()
+    avg_ms = sum(r[1] for r in recs) / len(recs)
+    nbytes = recs[0][3]
+    gbs = nbytes / (avg_ms * 1e-3) / 1e9
+    return {"kernel": "adamw", "params": n, "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "avg_ms": round(avg_ms, 4),
+            "launches": len(recs), "bytes_per_launch": int(nbytes)}
 
 
 def cpu_baseline(case, shape, min_seconds: float = 10.0, max_steps: int = 5):
@@ -201,6 +232,8 @@ def main():
                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic, "kernel": args.dominant,
                     "avg_ms": round(avg_ms, 4), "launches": len(recs), "gflop_per_launch": round(kflops / 1e9, 2)}
 
+    optim = None if args.no_optimizer else optimizer_step(mt, si, torch, shape, stream)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on the host (one step)", file=sys.stderr, flush=True)
@@ -227,6 +260,7 @@ def main():
         "wall_s_timed": round(wall, 3),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "optimizer_step": optim,
     }
     print(json.dumps(line), flush=True)
 

@@ -124,6 +124,23 @@ int mt_mlp_bwd(const mt_shape *shape, const void *x, const void *w_fc1, const vo
                size_t saved_bytes, const void *dy, void *dx_partial, float *dw_fc1, float *db_fc1, float *dw_fc2,
                void *workspace, size_t workspace_bytes, void *stream);
 
+/* Fused AdamW step over n fp32 master parameters, one pass (the oreateai.com
+ * Megatron-LM analysis, "In-Depth Analysis of Distributed Training Frameworks for Large
+ * Models ... Megatron-LM", section 2.2: the fused optimizer step; section 3.1: beta1 0.9,
+ * beta2 0.95). Per parameter, with g = grad_scale * grad, t = step (1-based):
+ *   m = beta1 m + (1 - beta1) g;  v = beta2 v + (1 - beta2) g^2
+ *   p = p - lr weight_decay p - lr (m / (1 - beta1^t)) / (sqrt(v / (1 - beta2^t)) + eps)
+ * param, exp_avg (m) and exp_avg_sq (v) are updated in place; grad is read; param_bf16
+ * (may be NULL) receives bf16(p) rounded to nearest even, the weights the next forward
+ * multiplies with. All are device pointers, caller-owned, 16-byte aligned; a layer's
+ * tensors can share one flat buffer when each starts at a multiple of 4 elements.
+ * Arithmetic in fp32 (bias corrections in double on the host). n == 0 is a no-op.
+ * Returns MT_ERR_INVALID_ARG for n < 0, step < 1, a beta outside [0, 1) or a null or
+ * misaligned pointer, before launching anything; MT_ERR_HIP if the launch fails. */
+int mt_adamw_step(int64_t n, float *param, const float *grad, float *exp_avg, float *exp_avg_sq, void *param_bf16,
+                  float lr, float beta1, float beta2, float eps, float weight_decay, float grad_scale, int32_t step,
+                  void *stream);
+
 /* Static text of a status code. */
 const char *mt_status_string(int status);
 

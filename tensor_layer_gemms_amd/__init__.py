@@ -5,8 +5,8 @@ C ABI of include/mt.h. torch tensors provide device memory and the stream; nothi
 here computes. If the library has not been built, loading fails loudly (build it with
 ``python -m tensor_layer_gemms_amd.build``).
 
-Names follow include/mt.h: layer_fwd / layer_bwd / mlp_fwd / mlp_bwd and the
-*_bytes queries; Shape, LayerWeights and LayerGrads mirror the C structs.
+Names follow include/mt.h: layer_fwd / layer_bwd / mlp_fwd / mlp_bwd, adamw_step and
+the *_bytes queries; Shape, LayerWeights and LayerGrads mirror the C structs.
 """
 from __future__ import annotations
 
@@ -51,6 +51,8 @@ _SIGS = {
     "mt_mlp_workspace_bytes": (_SZ, [ctypes.POINTER(Shape)]),
     "mt_mlp_fwd": (_I, [ctypes.POINTER(Shape), _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP, _SZ, _VP]),
     "mt_mlp_bwd": (_I, [ctypes.POINTER(Shape), _VP, _VP, _VP, _VP, _SZ, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "mt_adamw_step": (_I, [ctypes.c_int64, _VP, _VP, _VP, _VP, _VP, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                           ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_int32, _VP]),
     "mt_status_string": (ctypes.c_char_p, [_I]),
     "mt_timing_enable": (_I, [_I, ctypes.c_char_p]),
     "mt_timing_reset": (_I, []),
@@ -237,3 +239,20 @@ def timing_records() -> List[Tuple[str, float, float, float]]:
         _check("mt_timing_get", lib().mt_timing_get(i, buf, 64, ctypes.byref(ms), ctypes.byref(fl), ctypes.byref(by)))
         out.append((buf.value.decode(), ms.value, fl.value, by.value))
     return out
+
+
+def adamw_step(param, grad, exp_avg, exp_avg_sq, param_bf16=None, *, lr: float, beta1: float, beta2: float,
+               eps: float, weight_decay: float, step: int, grad_scale: float = 1.0, stream=None) -> None:
+    """mt_adamw_step: one fused AdamW step over flat fp32 tensors of equal size
+    (param, exp_avg, exp_avg_sq updated in place; param_bf16 optional bf16 output)."""
+    import torch
+    n = param.numel() if not isinstance(param, int) else None
+    if n is None:
+        raise ValueError("param: a device tensor is required (its size is the step's length)")
+    for name, t in (("param", param), ("grad", grad), ("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq)):
+        _expect(name, t, n, torch.float32)
+    if param_bf16 is not None:
+        _expect("param_bf16", param_bf16, n, torch.bfloat16)
+    _check("mt_adamw_step", lib().mt_adamw_step(n, _ptr(param), _ptr(grad), _ptr(exp_avg), _ptr(exp_avg_sq),
+                                                _ptr(param_bf16), lr, beta1, beta2, eps, weight_decay, grad_scale,
+                                                int(step), _stream(stream)))

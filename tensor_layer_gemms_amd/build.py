@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmt.so")
-SOURCES = ["gemm_bf16.hip", "gemm_f32.hip", "rowwise.hip", "flash_attn.hip", "mt_abi.hip"]
+SOURCES = ["gemm_bf16.hip", "gemm_f32.hip", "rowwise.hip", "flash_attn.hip", "adamw.hip", "mt_abi.hip"]
 ARCH = "gfx950"
 # -packed-fp32-ops off: packed fp32 VALU forms stay out of the generated code.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

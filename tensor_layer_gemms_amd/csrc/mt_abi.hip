@@ -11,6 +11,7 @@
 #include <string>
 #include <vector>
 
+#include "adamw.hpp"
 #include "flash_attn.hpp"
 #include "gemm.hpp"
 #include "mt.h"
@@ -740,6 +741,39 @@ int mt_mlp_bwd(const mt_shape* shape, const void* x, const void* w_fc1, const vo
   carve_mlp_ws(d, workspace, &ws);
   return mlp_bwd_impl(d, x, w_fc1, w_fc2, sv, dy, dx_partial, dw_fc1, db_fc1, dw_fc2, ws,
                       static_cast<hipStream_t>(stream));
+}
+
+int mt_adamw_step(int64_t n, float* param, const float* grad, float* exp_avg, float* exp_avg_sq, void* param_bf16,
+                  float lr, float beta1, float beta2, float eps, float weight_decay, float grad_scale, int32_t step,
+                  void* stream) {
+  if (n < 0 || step < 1 || !(beta1 >= 0.f && beta1 < 1.f) || !(beta2 >= 0.f && beta2 < 1.f))
+    return MT_ERR_INVALID_ARG;
+  if (n == 0) return MT_OK;
+  if (!aligned16(param) || !aligned16(grad) || !aligned16(exp_avg) || !aligned16(exp_avg_sq) ||
+      (param_bf16 && !aligned16(param_bf16)))
+    return MT_ERR_INVALID_ARG;
+  AdamwArgs a;
+  a.p = param;
+  a.g = grad;
+  a.m = exp_avg;
+  a.v = exp_avg_sq;
+  a.p16 = param_bf16;
+  a.n = n;
+  a.grad_scale = grad_scale;
+  a.beta1 = beta1;
+  a.one_minus_beta1 = (float)(1.0 - (double)beta1);
+  a.beta2 = beta2;
+  a.one_minus_beta2 = (float)(1.0 - (double)beta2);
+  a.lr_wd = (float)((double)lr * (double)weight_decay);
+  // bias corrections of the zero-initialised moments, in double on the host
+  a.step_size = (float)((double)lr / (1.0 - std::pow((double)beta1, (double)step)));
+  a.inv_sqrt_bc2 = (float)(1.0 / std::sqrt(1.0 - std::pow((double)beta2, (double)step)));
+  a.eps = eps;
+  const double bytes = (double)n * (28.0 + (param_bf16 ? 2.0 : 0.0));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  Seq q(s);
+  q.run("adamw", 0.0, bytes, [&] { return launch_adamw(a, s); });
+  return q.status();
 }
 
 const char* mt_status_string(int status) {
