@@ -33,23 +33,54 @@ __device__ __forceinline__ int vswz(int row, int chunk) {
 }
 
 // DMA of one [32][D] tile whose rows are key rows kb.. of a head's column slice. `rsrc`
-// covers the sequence's rows (rows past it read zeros); row r of the tile is at byte
-// r * ld * 2 + chunk * 16 from the resource base. A wave instruction fills 1 KB of LDS:
-// lane L writes bytes [16 L, +16) of it = tile row q * RPI + L / CPR, stored chunk
-// L % CPR, which holds the logical chunk the swizzle maps there.
+// covers the sequence's rows, so rows past it read zeros (the byte offset of row kb + r
+// is at least the resource size once kb + r >= seq; the host keeps that size below
+// 4 GiB). A wave instruction fills 1 KB of LDS: lane L writes bytes [16 L, +16) of it =
+// tile row q * RPI + L / CPR, stored chunk L % CPR, which holds the logical chunk the
+// swizzle maps there. The lane's byte offset within the tile is the same for every key
+// block, so it is computed once (TileOffsets) and each block adds kb * ld * 2.
 template <int D, bool VTILE, int NW>
-__device__ __forceinline__ void dma_tile(bf16* lds, __amdgpu_buffer_rsrc_t rsrc, int64_t ld, int kb, int rows_left,
-                                         int wave, int lane) {
-  constexpr int CPR = D / 8, RPI = 64 / CPR, INSTR = 32 * D / 512;
+struct TileOffsets {
+  static constexpr int CPR = D / 8, RPI = 64 / CPR, INSTR = 32 * D / 512, PER = INSTR / NW;
   static_assert(INSTR % NW == 0, "tile instructions split over the waves");
+  uint32_t off[PER];
+  __device__ __forceinline__ void init(int64_t ld, int wave, int lane) {
 #pragma unroll
-  for (int i = 0; i < INSTR / NW; ++i) {
-    const int q = wave + i * NW;
-    const int r = q * RPI + lane / CPR, p = lane % CPR;
-    const int c = VTILE ? vswz<D>(r, p) : kswz<D>(r, p);
-    const uint32_t off = r < rows_left ? (uint32_t)(((int64_t)(kb + r) * ld + c * 8) * 2) : 0xFFFFFFF0u;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(lds + q * 512), 16, off, 0, 0, 0);
+    for (int i = 0; i < PER; ++i) {
+      const int q = wave + i * NW;
+      const int r = q * RPI + lane / CPR, p = lane % CPR;
+      const int c = VTILE ? vswz<D>(r, p) : kswz<D>(r, p);
+      off[i] = (uint32_t)(((int64_t)r * ld + c * 8) * 2);
+    }
   }
+};
+
+template <int D, bool VTILE, int NW>
+__device__ __forceinline__ void dma_tile(bf16* lds, __amdgpu_buffer_rsrc_t rsrc, const TileOffsets<D, VTILE, NW>& o,
+                                         uint32_t row_bytes, int wave) {
+#pragma unroll
+  for (int i = 0; i < TileOffsets<D, VTILE, NW>::PER; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(lds + (wave + i * NW) * 512), 16, o.off[i] + row_bytes, 0,
+                                             0, 0);
+}
+
+// Work-groups are handed to the 8 XCDs round-robin by linear id. Maps a grid of
+// `per_z` blocks per (sequence, head) to (z, block) so that each XCD gets a contiguous
+// run of the (z, block) list: one to two heads per XCD, whose K/V (or Q/dO) panels then
+// stay in that XCD's L2, instead of every XCD streaming every head. Within a run the
+// blocks keep their order (the deepest first).
+__device__ __forceinline__ void xcd_block(int per_z, int& z, int& blk) {
+  constexpr int NXCD = 8;
+  const int total = (int)(gridDim.x * gridDim.y);
+  const int lin = (int)(blockIdx.x + gridDim.x * blockIdx.y);
+  int logical = lin;
+  if (total >= NXCD) {
+    const int per = (total + NXCD - 1) / NXCD, rem = total % NXCD;
+    const int xcd = lin % NXCD, local = lin / NXCD;
+    logical = (rem == 0 || xcd < rem) ? xcd * per + local : rem * per + (xcd - rem) * (per - 1) + local;
+  }
+  z = logical / per_z;
+  blk = logical % per_z;
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t seq_rsrc(const bf16* base, int64_t ld, int seq) {
@@ -59,20 +90,28 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t seq_rsrc(const bf16* base, int
 }
 
 // ---------------------------------------------------------------------------- forward
-// Work-group: 64 query rows (wave w: rows q0 + 32 w ..) of sequence b, head k. Lane l of a
-// wave owns query row (l & 31); the logit accumulator of a 32-key block holds keys
+// Work-group: 64 query rows of sequence b, head k, and 4 waves in two pairs. Both pairs
+// own the same rows (wave w: rows q0 + 32 (w & 1) ..) and split the row block's keys:
+// pair 0 streams the first half of its key blocks, pair 1 the second half, each through
+// its own three-stage LDS ring, so the longest chain of dependent key steps (the deepest
+// row block walks every key of the sequence) is halved. At the end pair 1 hands its
+// running (O, m, l) to pair 0 through LDS and pair 0 merges and writes. Lane l of a wave
+// owns query row (l & 31); the logit accumulator of a 32-key block holds keys
 // 8 q + 4 (l >> 5) + j in register 4 q + j (the operand-swapped MFMA layout).
 template <int D>
-__global__ __launch_bounds__(128) void flash_fwd_kernel(FlashArgs a) {
-  constexpr int KS = D / 16, NB = D / 32, TILE = kFlashKeys * D;
-  __shared__ __attribute__((aligned(1024))) bf16 smem[kStages * 3 * TILE];
+__global__ __launch_bounds__(256) void flash_fwd_kernel(FlashArgs a) {
+  constexpr int KS = D / 16, NB = D / 32, TILE = kFlashKeys * D, RING = kStages * 3 * TILE;
+  __shared__ __attribute__((aligned(1024))) bf16 smem[2 * RING];
   dma_lds_escape(smem);
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int pair = wave >> 1, wv = wave & 1;  // key half, and the 32-row half of the block
   const int h = lane >> 5, r32 = lane & 31;
   const int nqb = (a.seq + kFlashRows - 1) / kFlashRows;
-  const int qb = nqb - 1 - (int)blockIdx.x;  // deepest row blocks first
-  const int z = blockIdx.y, b = z / a.heads, hd = z % a.heads;
-  const int row = qb * kFlashRows + wave * 32 + r32;  // this lane's query row
+  int z, qbi;
+  xcd_block(nqb, z, qbi);
+  const int qb = nqb - 1 - qbi;  // deepest row blocks first
+  const int b = z / a.heads, hd = z % a.heads;
+  const int row = qb * kFlashRows + wv * 32 + r32;  // this lane's query row
   const bool row_ok = row < a.seq;
 
   const bf16* qkv = static_cast<const bf16*>(a.qkv) + (int64_t)b * a.seq * a.ldq;
@@ -97,12 +136,19 @@ __global__ __launch_bounds__(128) void flash_fwd_kernel(FlashArgs a) {
   const __amdgpu_buffer_rsrc_t rv = seq_rsrc(qkv + cv, a.ldq, a.seq);
   const int kend = min(a.seq, (qb + 1) * kFlashRows);  // keys this row block can see
   const int nsteps = (kend + kFlashKeys - 1) / kFlashKeys;
-  auto issue = [&](int t) {
-    bf16* st = smem + (t % kStages) * 3 * TILE;
-    const int kb = t * kFlashKeys, left = a.seq - kb;
-    dma_tile<D, false, 2>(st, rk, a.ldq, kb, left, wave, lane);
-    dma_tile<D, false, 2>(st + TILE, rkl, a.ldq, kb, left, wave, lane);
-    dma_tile<D, true, 2>(st + 2 * TILE, rv, a.ldq, kb, left, wave, lane);
+  const int half = (nsteps + 1) / 2;                    // pair 0: blocks [0, half)
+  const int tb = pair ? half : 0, cnt = pair ? nsteps - half : half;
+  bf16* ring = smem + pair * RING;
+  TileOffsets<D, false, 2> ok;
+  TileOffsets<D, true, 2> ov;
+  ok.init(a.ldq, wv, lane);
+  ov.init(a.ldq, wv, lane);
+  auto issue = [&](int j) {  // key block tb + j into stage j % kStages of this pair's ring
+    bf16* st = ring + (j % kStages) * 3 * TILE;
+    const uint32_t rb = (uint32_t)((tb + j) * kFlashKeys) * (uint32_t)a.ldq * 2u;
+    dma_tile(st, rk, ok, rb, wv);
+    dma_tile(st + TILE, rkl, ok, rb, wv);
+    dma_tile(st + 2 * TILE, rv, ov, rb, wv);
   };
 
   // Per-lane LDS offsets. K fragment (B operand of S): key row r32, chunk 2 ks + h.
@@ -116,24 +162,26 @@ __global__ __launch_bounds__(128) void flash_fwd_kernel(FlashArgs a) {
     for (int r = 0; r < 16; ++r) o[nb][r] = 0.f;
   float m = -__builtin_inff(), l = 0.f;
 
-  // Per wave: 3 tiles of 32 D / 512 DMA instructions, over 2 waves.
+  // Per wave: 3 tiles of 32 D / 512 DMA instructions, over the pair's 2 waves. Both
+  // pairs pass the same number of work-group barriers (half iterations; pair 1 has at
+  // most one block fewer and idles through the last).
   constexpr int LOADS = 3 * (32 * D / 512) / 2;
-  issue(0);
-  if (nsteps > 1) issue(1);
-  for (int t = 0; t < nsteps; ++t) {
-    // this wave's loads of step t are done when at most those of step t + 1 are pending
-    if (t + 1 < nsteps) wait_vmcnt<LOADS>();
+  if (cnt > 0) issue(0);
+  if (cnt > 1) issue(1);
+  for (int j = 0; j < half; ++j) {
+    // this wave's loads of block j are done when at most those of block j + 1 are pending
+    if (j + 1 < cnt) wait_vmcnt<LOADS>();
     else wait_vmcnt<0>();
     dma_barrier();
-    if (t + 2 < nsteps) issue(t + 2);  // into the stage read in step t - 1
-    const bf16* sK = smem + (t % kStages) * 3 * TILE;
+    if (j + 2 < cnt) issue(j + 2);  // into the stage read in step j - 1
+    const bf16* sK = ring + (j % kStages) * 3 * TILE;
     const bf16* sKl = sK + TILE;
     const bf16* sV = sK + 2 * TILE;
 
     // Keys of this block vs this wave's rows r0..r0 + 31 (block and row starts are
     // multiples of 32): all visible, the diagonal block, or none (nothing to do).
-    const int kb = t * kFlashKeys, r0 = qb * kFlashRows + wave * 32;
-    if (kb > r0) continue;
+    const int kb = (tb + j) * kFlashKeys, r0 = qb * kFlashRows + wv * 32;
+    if (j >= cnt || kb > r0) continue;
     const bool diag = kb == r0;
 
     // S block: 32 keys x this wave's 32 rows, three compensated segments.
@@ -203,6 +251,33 @@ __global__ __launch_bounds__(128) void flash_fwd_kernel(FlashArgs a) {
     }
   }
 
+  // Merge the pairs: pair 1 parks (O, m, l) in LDS as [value][wave-in-pair, lane] floats
+  // (consecutive lanes on consecutive words); pair 0 combines them with its own:
+  // M = max(m0, m1), O = O0 2^(m0 - M) + O1 2^(m1 - M), l likewise (a pair that saw no
+  // key of a row has m = -inf, l = 0, O = 0 and contributes nothing).
+  constexpr int NV = NB * 16 + 2;
+  float* park = reinterpret_cast<float*>(smem);
+  const int slot = wv * 64 + lane;
+  dma_barrier();  // both rings are done with
+  if (pair == 1) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) park[(nb * 16 + r) * 128 + slot] = o[nb][r];
+    park[(NV - 2) * 128 + slot] = m;
+    park[(NV - 1) * 128 + slot] = l;
+  }
+  dma_barrier();
+  if (pair == 1) return;
+  const float m1 = park[(NV - 2) * 128 + slot], l1 = park[(NV - 1) * 128 + slot];
+  const float mm = fmaxf(m, m1);
+  const float w0 = __builtin_amdgcn_exp2f(m - mm), w1 = __builtin_amdgcn_exp2f(m1 - mm);
+  l = l * w0 + l1 * w1;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[nb][r] = o[nb][r] * w0 + park[(nb * 16 + r) * 128 + slot] * w1;
+
   if (row_ok) {
     const float inv = 1.f / l;
     bf16* out = static_cast<bf16*>(a.ctx) + ((int64_t)b * a.seq + row) * a.ldc + hd * D;
@@ -213,7 +288,7 @@ __global__ __launch_bounds__(128) void flash_fwd_kernel(FlashArgs a) {
         float v[4] = {o[nb][4 * q] * inv, o[nb][4 * q + 1] * inv, o[nb][4 * q + 2] * inv, o[nb][4 * q + 3] * inv};
         store4_bf16(out + 32 * nb + 8 * q + 4 * h, v);
       }
-    if (h == 0) a.lse[(int64_t)z * a.seq + row] = m * kLn2 + logf(l);
+    if (h == 0) a.lse[(int64_t)z * a.seq + row] = mm * kLn2 + logf(l);
   }
 }
 
@@ -227,17 +302,28 @@ __device__ __forceinline__ int dswz(int row, int chunk) { return chunk ^ (((row 
 
 constexpr int kBwdD = 128;
 
-// DMA of a [32][128] tile (dual swizzle) from rows r0.. of a column slice.
-__device__ __forceinline__ void dma_tile_dual(bf16* lds, __amdgpu_buffer_rsrc_t rsrc, int64_t ld, int r0,
-                                              int rows_left, int wave, int lane) {
-  constexpr int CPR = 16, RPI = 4, INSTR = 8;
+// DMA of a [32][128] tile (dual swizzle) from rows r0.. of a column slice; rows past the
+// sequence read zeros through the resource's range (as for dma_tile). The lane's byte
+// offsets within the tile are computed once per leading dimension (DualOffsets).
+struct DualOffsets {
+  uint32_t off[4];
+  __device__ __forceinline__ void init(int64_t ld, int wave, int lane) {
+    constexpr int CPR = 16, RPI = 4;
 #pragma unroll
-  for (int i = 0; i < INSTR / 2; ++i) {
-    const int q = wave + i * 2;
-    const int r = q * RPI + lane / CPR, c = dswz(r, lane % CPR);
-    const uint32_t off = r < rows_left ? (uint32_t)(((int64_t)(r0 + r) * ld + c * 8) * 2) : 0xFFFFFFF0u;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(lds + q * 512), 16, off, 0, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      const int q = wave + i * 2;
+      const int r = q * RPI + lane / CPR, c = dswz(r, lane % CPR);
+      off[i] = (uint32_t)(((int64_t)r * ld + c * 8) * 2);
+    }
   }
+};
+
+__device__ __forceinline__ void dma_tile_dual(bf16* lds, __amdgpu_buffer_rsrc_t rsrc, const DualOffsets& o,
+                                              uint32_t row_bytes, int wave) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(lds + (wave + i * 2) * 512), 16, o.off[i] + row_bytes, 0,
+                                             0, 0);
 }
 
 // Row read of a dual-swizzled tile: lane's row r32, 16-k step ks (B operand).
@@ -324,16 +410,20 @@ __device__ __forceinline__ void flash_bwd_kv(const FlashArgs& a, int kblk, int z
       __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.D) + (int64_t)z * a.seq, (short)0, a.seq * 4, 0x00020000);
   const int qb0 = (kblk * 64) / 32, nqb = (a.seq + 31) / 32;
   const int nsteps = nqb - qb0;
+  DualOffsets oq, oo;
+  oq.init(a.ldq, wave, lane);
+  oo.init(a.ldc, wave, lane);
+  // lanes 0..7 of one instruction fetch the 32 floats; the others read past the range
+  // (2^31 plus a row offset below 2^20 stays past it)
+  const uint32_t lane_ld = lane < 8 ? 16u * lane : 0x80000000u;
   auto issue = [&](int t) {
     bf16* st = smem + (t % kStages) * STAGE;
-    const int r0 = (qb0 + t) * 32, left = a.seq - r0;
-    dma_tile_dual(st, rq, a.ldq, r0, left, wave, lane);
-    dma_tile_dual(st + TILE, rql, a.ldq, r0, left, wave, lane);
-    dma_tile_dual(st + 2 * TILE, rdo, a.ldc, r0, left, wave, lane);
-    // lanes 0..7 of one instruction fetch the 32 floats; the others read past the range
-    const uint32_t off = lane < 8 ? (uint32_t)((r0 + 4 * lane) * 4) : 0xFFFFFFF0u;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(wave == 0 ? rl : rd, (lds_ptr_t)(st + 3 * TILE + wave * 512), 16, off, 0,
-                                             0, 0);
+    const uint32_t r0 = (uint32_t)((qb0 + t) * 32);
+    dma_tile_dual(st, rq, oq, r0 * (uint32_t)a.ldq * 2u, wave);
+    dma_tile_dual(st + TILE, rql, oq, r0 * (uint32_t)a.ldq * 2u, wave);
+    dma_tile_dual(st + 2 * TILE, rdo, oo, r0 * (uint32_t)a.ldc * 2u, wave);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(wave == 0 ? rl : rd, (lds_ptr_t)(st + 3 * TILE + wave * 512), 16,
+                                             lane_ld + r0 * 4u, 0, 0, 0);
   };
 
   const float scale2 = a.scale * kLog2e;
@@ -450,12 +540,14 @@ __device__ __forceinline__ void flash_bwd_q(const FlashArgs& a, int qb, int z, b
   const __amdgpu_buffer_rsrc_t rv = seq_rsrc(qkv + cv, a.ldq, a.seq);
   const int kend = min(a.seq, (qb + 1) * kFlashRows);
   const int nsteps = (kend + 31) / 32;
+  DualOffsets ok;
+  ok.init(a.ldq, wave, lane);
   auto issue = [&](int t) {
     bf16* st = smem + (t % kStages) * 3 * TILE;
-    const int r0 = t * 32, left = a.seq - r0;
-    dma_tile_dual(st, rk, a.ldq, r0, left, wave, lane);
-    dma_tile_dual(st + TILE, rkl, a.ldq, r0, left, wave, lane);
-    dma_tile_dual(st + 2 * TILE, rv, a.ldq, r0, left, wave, lane);
+    const uint32_t rb = (uint32_t)(t * 32) * (uint32_t)a.ldq * 2u;
+    dma_tile_dual(st, rk, ok, rb, wave);
+    dma_tile_dual(st + TILE, rkl, ok, rb, wave);
+    dma_tile_dual(st + 2 * TILE, rv, ok, rb, wave);
   };
 
   const float scale2 = a.scale * kLog2e;
@@ -519,7 +611,8 @@ __global__ __launch_bounds__(128) void flash_bwd_kernel(FlashArgs a) {
   constexpr int SMEM = kStages * (kKvStage > kQStage ? kKvStage : kQStage);
   __shared__ __attribute__((aligned(1024))) bf16 smem[SMEM];
   dma_lds_escape(smem);
-  const int x = (int)blockIdx.x, z = blockIdx.y;
+  int z, x;
+  xcd_block((int)gridDim.x, z, x);
   const int nqb = (a.seq + kFlashRows - 1) / kFlashRows, nkb = (a.seq + 63) / 64;
   if ((x & 1) == 0) {
     if (x / 2 < nkb) flash_bwd_kv(a, x / 2, z, smem);
@@ -530,8 +623,17 @@ __global__ __launch_bounds__(128) void flash_bwd_kernel(FlashArgs a) {
 
 }  // namespace
 
+// The kernels address a sequence's rows with 32-bit byte offsets and rely on the buffer
+// range check for the rows of a last partial block past the sequence: the rows up to one
+// block beyond it must span < 4 GiB in every column slice.
+static bool flash_extents_ok(const FlashArgs& a) {
+  const uint64_t lim = 0xFFFFFFF0ull, rows = (uint64_t)a.seq + 64u;
+  return rows * (uint64_t)a.ldq * 2u < lim && rows * (uint64_t)a.ldc * 2u < lim && rows * 4u < (1ull << 20);
+}
+
 hipError_t launch_flash_bwd(const FlashArgs& a, int d, hipStream_t s) {
   if (a.seq <= 0 || a.batch <= 0 || a.heads <= 0) return hipSuccess;
+  if (!flash_extents_ok(a)) return hipErrorInvalidValue;
   if (d != kBwdD) return hipErrorInvalidValue;
   const int nqb = (a.seq + kFlashRows - 1) / kFlashRows, nkb = (a.seq + 63) / 64;
   const int n = 2 * (nqb > nkb ? nqb : nkb);
@@ -541,9 +643,10 @@ hipError_t launch_flash_bwd(const FlashArgs& a, int d, hipStream_t s) {
 
 hipError_t launch_flash_fwd(const FlashArgs& a, int d, hipStream_t s) {
   if (a.seq <= 0 || a.batch <= 0 || a.heads <= 0) return hipSuccess;
+  if (!flash_extents_ok(a)) return hipErrorInvalidValue;
   const dim3 grid((a.seq + kFlashRows - 1) / kFlashRows, a.batch * a.heads);
-  if (d == 128) hipLaunchKernelGGL(flash_fwd_kernel<128>, grid, dim3(128), 0, s, a);
-  else if (d == 64) hipLaunchKernelGGL(flash_fwd_kernel<64>, grid, dim3(128), 0, s, a);
+  if (d == 128) hipLaunchKernelGGL(flash_fwd_kernel<128>, grid, dim3(256), 0, s, a);
+  else if (d == 64) hipLaunchKernelGGL(flash_fwd_kernel<64>, grid, dim3(256), 0, s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
