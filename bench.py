@@ -87,6 +87,42 @@ def copy_probe(nbytes: int) -> None:
     print(json.dumps({"copy_probe_bytes": nbytes}), flush=True)
 
 
+def recompute_report(shape, ms_per_step: float, saved_bytes: int):
+    """Hardware vs model FLOPs of the fused-attention path, and the activation bytes it
+    does not store. The backward recomputes the attention probabilities P = exp(S - L)
+    from Q, K and the saved row log-sum-exp instead of keeping P (selective
+    recomputation of the attention core); the logits are formed in three compensated
+    segments (Q_hi K_hi + Q_hi K_lo + Q_lo K_hi) and the QKV forward adds U_lo W_qk^T.
+    Counted per head product over the s (s + 1) / 2 causal (query, key) pairs, as the
+    model FLOPs are: forward 3 logit segments + P V; backward, key-block part 3 logit
+    segments + dP + dV + dK, row-block part 3 logit segments + dP + dQ."""
+    if shape.dtype != "bf16" or shape.head_dim != 128:
+        return None
+    B, s, at, d = shape.micro_batch, shape.seq, shape.heads_per_shard, shape.head_dim
+    M, h, t = shape.tokens, shape.h, shape.tp
+    unit = 2.0 * B * at * d * s * (s + 1) / 2  # one causal head product
+    model = si_model_flops(shape)
+    attn_model = 6 * unit
+    attn_hw = (3 + 1) * unit + (3 + 3) * unit + (3 + 2) * unit
+    qkv_comp = 2.0 * M * (2 * h // t) * h
+    hw = model - attn_model + attn_hw + qkv_comp
+    p_bytes = B * at * s * s * 2  # bf16 probabilities a materialised backward would keep
+    return {"model_gflop": round(model / 1e9, 1), "hardware_gflop": round(hw / 1e9, 1),
+            "hardware_tflops": round(hw / (ms_per_step * 1e-3) / 1e12, 1),
+            # the backward's logits recomputed in both parts (all three segments)
+            "bwd_logit_recompute_gflop": round(6 * unit / 1e9, 1),
+            # dP formed in both backward parts (one extra head product)
+            "bwd_dp_duplicate_gflop": round(unit / 1e9, 1),
+            # forward: the two extra logit segments and U_lo W_qk^T
+            "fwd_compensation_gflop": round((2 * unit + qkv_comp) / 1e9, 1),
+            "p_bytes_not_stored": int(p_bytes), "saved_store_bytes": int(saved_bytes)}
+
+
+def si_model_flops(shape) -> float:
+    import seeded_inputs as si
+    return si.model_flops(shape, causal=True)
+
+
 def optimizer_step(mt, si, torch, shape, stream, warmup: int = 2, iters: int = 10):
     """Fused AdamW step over the shard's parameters in one flat fp32 buffer (with the
     bf16 copy): average launch time from HIP events on the library's stream, against
@@ -261,6 +297,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "optimizer_step": optim,
+        "recompute": recompute_report(shape, ms_per_step, mt.layer_saved_bytes(sh)) if L == 1 else None,
     }
     print(json.dumps(line), flush=True)
 
