@@ -146,6 +146,7 @@ size_t colsum_floats(const Dims& d) {
   size_t n = colsum_partial_floats((int)d.M, (int)d.h, 1);
   n = std::max(n, colsum_partial_floats((int)d.M, (int)d.ft, 0));
   n = std::max(n, colsum_partial_floats((int)d.M, (int)d.qkv, 0));
+  if (ln_bwd_sums_supported((int)d.h)) n = std::max(n, ln_bwd_sums_partial_floats((int)d.M, (int)d.h, 3));
   return n;
 }
 
@@ -475,19 +476,28 @@ int layer_bwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, cons
     return gemm_dgrad_wgrad(d, dg, EPI_STORE, wg, stream, ws.spart);
   });
   // B3 dX2 = dOut + LN2-backward(AR(dV2)) (written as the GEMM operand and as an fp32
-  // copy for the residual path); dgamma2, dbeta2; db_o = colsum(dX2)
-  q.run("ln2_bwd", 0, Mh * (3 * es + 8), [&] {
-    return launch_ln_bwd(bf, ws.dv2, sv.x2, true, w.ln2_g, sv.mean2, sv.rstd2, dout, false, ws.dx2, ws.dx2f, M,
-                         (int)d.h, stream);
-  });
-  q.run("ln2_param_grads", 0, Mh * (es + 4), [&] {
-    return launch_colsum(bf, 1, ws.dv2, false, sv.x2, true, sv.mean2, sv.rstd2, gr.ln2_g, gr.ln2_b, ws.part, M,
-                         (int)d.h, stream);
-  });
-  q.run("db_o", 0, Mh * 4, [&] {
-    return launch_colsum(bf, 0, ws.dx2f, true, nullptr, false, nullptr, nullptr, gr.b_o, nullptr, ws.part, M,
-                         (int)d.h, stream);
-  });
+  // copy for the residual path); dgamma2, dbeta2; db_o = colsum(dX2) — in one pass over
+  // the rows where the fused kernel covers h, else as separate column sums
+  const bool ln_sums = ln_bwd_sums_supported((int)d.h);
+  if (ln_sums) {
+    q.run("ln2_bwd", 0, Mh * (3 * es + 8), [&] {
+      return launch_ln_bwd_sums(bf, ws.dv2, sv.x2, true, w.ln2_g, sv.mean2, sv.rstd2, dout, false, ws.dx2, ws.dx2f,
+                                ws.part, gr.ln2_g, gr.ln2_b, gr.b_o, M, (int)d.h, stream);
+    });
+  } else {
+    q.run("ln2_bwd", 0, Mh * (3 * es + 8), [&] {
+      return launch_ln_bwd(bf, ws.dv2, sv.x2, true, w.ln2_g, sv.mean2, sv.rstd2, dout, false, ws.dx2, ws.dx2f, M,
+                           (int)d.h, stream);
+    });
+    q.run("ln2_param_grads", 0, Mh * (es + 4), [&] {
+      return launch_colsum(bf, 1, ws.dv2, false, sv.x2, true, sv.mean2, sv.rstd2, gr.ln2_g, gr.ln2_b, ws.part, M,
+                           (int)d.h, stream);
+    });
+    q.run("db_o", 0, Mh * 4, [&] {
+      return launch_colsum(bf, 0, ws.dx2f, true, nullptr, false, nullptr, nullptr, gr.b_o, nullptr, ws.part, M,
+                           (int)d.h, stream);
+    });
+  }
   // B4 out-projection: dW_o = dX2^T ctx, dctx = dX2 W_o
   q.run("out_proj_dgrad_wgrad", 2 * gflop(d.M, d.hs, d.h), 0, [&] {
     const GemmArgs dg = plain(ws.dx2, d.h, w.w_o, d.hs, ws.dctx, d.hs, d.M, d.hs, d.h);
@@ -568,14 +578,21 @@ int layer_bwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, cons
     return gemm_dgrad_wgrad(d, dg, EPI_STORE, wg, stream, ws.spart);
   });
   // B8 dX = dX2 + LN1-backward(AR(dU)); dgamma1, dbeta1
-  q.run("ln1_bwd", 0, Mh * (3 * es + 4), [&] {
-    return launch_ln_bwd(bf, ws.dv2, x, false, w.ln1_g, sv.mean1, sv.rstd1, ws.dx2f, true, dx, nullptr, M, (int)d.h,
-                         stream);
-  });
-  q.run("ln1_param_grads", 0, 2 * Mh * es, [&] {
-    return launch_colsum(bf, 1, ws.dv2, false, x, false, sv.mean1, sv.rstd1, gr.ln1_g, gr.ln1_b, ws.part, M,
-                         (int)d.h, stream);
-  });
+  if (ln_sums) {
+    q.run("ln1_bwd", 0, Mh * (3 * es + 4), [&] {
+      return launch_ln_bwd_sums(bf, ws.dv2, x, false, w.ln1_g, sv.mean1, sv.rstd1, ws.dx2f, true, dx, nullptr,
+                                ws.part, gr.ln1_g, gr.ln1_b, nullptr, M, (int)d.h, stream);
+    });
+  } else {
+    q.run("ln1_bwd", 0, Mh * (3 * es + 4), [&] {
+      return launch_ln_bwd(bf, ws.dv2, x, false, w.ln1_g, sv.mean1, sv.rstd1, ws.dx2f, true, dx, nullptr, M,
+                           (int)d.h, stream);
+    });
+    q.run("ln1_param_grads", 0, 2 * Mh * es, [&] {
+      return launch_colsum(bf, 1, ws.dv2, false, x, false, sv.mean1, sv.rstd1, gr.ln1_g, gr.ln1_b, ws.part, M,
+                           (int)d.h, stream);
+    });
+  }
   return q.status();
 }
 

@@ -137,6 +137,84 @@ __global__ __launch_bounds__(kLnThreads) void ln_bwd_kernel(const T* __restrict_
   }
 }
 
+// LayerNorm backward fused with its column reductions. A block walks `rpb` consecutive
+// rows (the row math is ln_bwd_kernel's) and keeps, per thread and column, the sums
+// over its rows of dy * xhat (d gamma), dy (d beta) and, with NS = 3, dx (the bias
+// gradient of the sublayer whose output dx is); it writes them as one partial row per
+// sum and block, which colsum_final_kernel adds in a fixed order. The rows' inputs are
+// read once, where separate column-sum launches would read dy, x and dx again.
+template <typename T, typename TX, typename TR, int CPT, int NS>
+__global__ __launch_bounds__(kLnThreads) void ln_bwd_sums_kernel(const T* __restrict__ dy, const TX* __restrict__ x,
+                                                                 const T* __restrict__ gamma,
+                                                                 const float* __restrict__ mean,
+                                                                 const float* __restrict__ rstd,
+                                                                 const TR* __restrict__ resid, T* __restrict__ dx,
+                                                                 float* __restrict__ dxf, float* __restrict__ part,
+                                                                 int rows, int h, int rpb) {
+  constexpr int NW = kLnThreads / 64;
+  __shared__ float red[2 * NW];
+  const int nch = h / 8;
+  const int r0 = blockIdx.x * rpb, r1 = min(rows, r0 + rpb);
+  float acc[NS][CPT][8];
+#pragma unroll
+  for (int k = 0; k < NS; ++k)
+#pragma unroll
+    for (int c = 0; c < CPT; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[k][c][e] = 0.f;
+  for (int row = r0; row < r1; ++row) {
+    const float mu = mean[row], rs = rstd[row];
+    float g[CPT][8], xh[CPT][8], rv[CPT][8];
+    float s[2] = {0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ch = threadIdx.x + c * kLnThreads;
+      if (ch < nch) {
+        const int64_t off = (int64_t)row * h + (int64_t)ch * 8;
+        float gv[8];
+        load8(dy + off, g[c]);
+        load8(x + off, xh[c]);
+        load8(resid + off, rv[c]);
+        load8(gamma + ch * 8, gv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          xh[c][e] = (xh[c][e] - mu) * rs;
+          acc[0][c][e] += g[c][e] * xh[c][e];
+          acc[1][c][e] += g[c][e];
+          g[c][e] *= gv[e];
+          s[0] += g[c][e];
+          s[1] += g[c][e] * xh[c][e];
+        }
+      }
+    }
+    block_sum<2, NW>(s, red);
+    const float mg = s[0] / (float)h, mgx = s[1] / (float)h;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ch = threadIdx.x + c * kLnThreads;
+      if (ch < nch) {
+        const int64_t off = (int64_t)row * h + (int64_t)ch * 8;
+        float out[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) out[e] = rv[c][e] + rs * (g[c][e] - mg - xh[c][e] * mgx);
+        store8(dx + off, out);
+        if (dxf) store8(dxf + off, out);
+        if constexpr (NS == 3) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[2][c][e] += out[e];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < NS; ++k)
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ch = threadIdx.x + c * kLnThreads;
+      if (ch < nch) store8(part + ((int64_t)k * gridDim.x + blockIdx.x) * h + (int64_t)ch * 8, acc[k][c]);
+    }
+}
+
 // ------------------------------------------------------------------ column sums
 // Stage 1: block (64 column chunks of 8 x 4 row lanes) sums a slab of rows per column.
 template <typename TA, typename TX, int MODE>
@@ -193,17 +271,19 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(const TA* __restric
   }
 }
 
-// Stage 2: sum the row-slab partials. Block: 64 columns x 4 slab groups; group g sums
-// slabs g, g + 4, ... in four interleaved chains (independent loads in flight), then the
-// groups are added in a fixed order. The order depends on the geometry only.
+// Stage 2: sum the row-slab partials of `nsum` (1 to 3) column sums, partial k of slab b
+// at part[(k nrb + b) cols + c]. Block: 64 columns x 4 slab groups; group g sums slabs
+// g, g + 4, ... in four interleaved chains (independent loads in flight), then the groups
+// are added in a fixed order. The order depends on the geometry only.
 __global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restrict__ part, float* __restrict__ out0,
-                                                           float* __restrict__ out1, int nrb, int cols, int mode) {
-  __shared__ float red[2][4][64];
+                                                           float* __restrict__ out1, float* __restrict__ out2,
+                                                           int nrb, int cols, int nsum) {
+  __shared__ float red[3][4][64];
   const int lane = threadIdx.x & 63, grp = threadIdx.x >> 6;
   const int c = blockIdx.x * 64 + lane;
-  float s[2] = {0.f, 0.f};
+  float s[3] = {0.f, 0.f, 0.f};
   if (c < cols) {
-    for (int k = 0; k < (mode == 1 ? 2 : 1); ++k) {
+    for (int k = 0; k < nsum; ++k) {
       const float* p = part + (int64_t)k * nrb * cols + c;
       float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
       int b = grp;
@@ -217,12 +297,13 @@ __global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restri
       s[k] = (a0 + a1) + (a2 + a3);
     }
   }
-  red[0][grp][lane] = s[0];
-  red[1][grp][lane] = s[1];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) red[k][grp][lane] = s[k];
   __syncthreads();
   if (grp == 0 && c < cols) {
-    out0[c] = (red[0][0][lane] + red[0][1][lane]) + (red[0][2][lane] + red[0][3][lane]);
-    if (mode == 1) out1[c] = (red[1][0][lane] + red[1][1][lane]) + (red[1][2][lane] + red[1][3][lane]);
+    float* outs[3] = {out0, out1, out2};
+    for (int k = 0; k < nsum; ++k)
+      outs[k][c] = (red[k][0][lane] + red[k][1][lane]) + (red[k][2][lane] + red[k][3][lane]);
   }
 }
 
@@ -425,6 +506,56 @@ hipError_t ln_bwd_dispatch(const void* dy, const void* x, bool x_f32, const void
   return ln_bwd_t<T, T, T>(dy, x, gamma, mean, rstd, resid, dx, dxf, rows, h, s);
 }
 
+// Rows per block of the fused LayerNorm backward: about 256 blocks (one per CU).
+int ln_sums_rpb(int rows) { return rows <= 256 ? 1 : (rows + 255) / 256; }
+
+template <typename T, typename TX, typename TR, int CPT>
+hipError_t ln_bwd_sums_launch(const void* dy, const void* x, const void* gamma, const float* mean, const float* rstd,
+                              const void* resid, void* dx, float* dxf, float* part, float* dgamma, float* dbeta,
+                              float* dsum, int rows, int h, hipStream_t s) {
+  const int rpb = ln_sums_rpb(rows), nblk = (rows + rpb - 1) / rpb;
+  if (dsum)
+    hipLaunchKernelGGL((ln_bwd_sums_kernel<T, TX, TR, CPT, 3>), dim3(nblk), dim3(kLnThreads), 0, s, (const T*)dy,
+                       (const TX*)x, (const T*)gamma, mean, rstd, (const TR*)resid, (T*)dx, dxf, part, rows, h, rpb);
+  else
+    hipLaunchKernelGGL((ln_bwd_sums_kernel<T, TX, TR, CPT, 2>), dim3(nblk), dim3(kLnThreads), 0, s, (const T*)dy,
+                       (const TX*)x, (const T*)gamma, mean, rstd, (const TR*)resid, (T*)dx, dxf, part, rows, h, rpb);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(colsum_final_kernel, dim3((h + 63) / 64), dim3(256), 0, s, part, dgamma, dbeta, dsum, nblk, h,
+                     dsum ? 3 : 2);
+  return hipGetLastError();
+}
+
+template <typename T, typename TX, typename TR>
+hipError_t ln_bwd_sums_t(const void* dy, const void* x, const void* gamma, const float* mean, const float* rstd,
+                         const void* resid, void* dx, float* dxf, float* part, float* dgamma, float* dbeta, float* dsum,
+                         int rows, int h, hipStream_t s) {
+  const int need = (h / 8 + kLnThreads - 1) / kLnThreads;
+  switch (need) {
+    case 1: return ln_bwd_sums_launch<T, TX, TR, 1>(dy, x, gamma, mean, rstd, resid, dx, dxf, part, dgamma, dbeta, dsum, rows, h, s);
+    case 2: return ln_bwd_sums_launch<T, TX, TR, 2>(dy, x, gamma, mean, rstd, resid, dx, dxf, part, dgamma, dbeta, dsum, rows, h, s);
+    case 3: return ln_bwd_sums_launch<T, TX, TR, 3>(dy, x, gamma, mean, rstd, resid, dx, dxf, part, dgamma, dbeta, dsum, rows, h, s);
+    case 4: return ln_bwd_sums_launch<T, TX, TR, 4>(dy, x, gamma, mean, rstd, resid, dx, dxf, part, dgamma, dbeta, dsum, rows, h, s);
+    default: return hipErrorNotSupported;
+  }
+}
+
+template <typename T>
+hipError_t ln_bwd_sums_dispatch(const void* dy, const void* x, bool x_f32, const void* gamma, const float* mean,
+                                const float* rstd, const void* resid, bool resid_f32, void* dx, float* dxf,
+                                float* part, float* dgamma, float* dbeta, float* dsum, int rows, int h,
+                                hipStream_t s) {
+  if (x_f32 && !resid_f32)
+    return ln_bwd_sums_t<T, float, T>(dy, x, gamma, mean, rstd, resid, dx, dxf, part, dgamma, dbeta, dsum, rows, h, s);
+  if (!x_f32 && resid_f32)
+    return ln_bwd_sums_t<T, T, float>(dy, x, gamma, mean, rstd, resid, dx, dxf, part, dgamma, dbeta, dsum, rows, h, s);
+  if (x_f32 && resid_f32)
+    return ln_bwd_sums_t<T, float, float>(dy, x, gamma, mean, rstd, resid, dx, dxf, part, dgamma, dbeta, dsum, rows,
+                                          h, s);
+  return ln_bwd_sums_t<T, T, T>(dy, x, gamma, mean, rstd, resid, dx, dxf, part, dgamma, dbeta, dsum, rows, h, s);
+}
+
 template <typename TA, typename TX>
 hipError_t colsum_t(int mode, const void* a, const void* x, const float* mean, const float* rstd, float* out0,
                     float* out1, float* partial, int rows, int cols, hipStream_t s) {
@@ -438,8 +569,8 @@ hipError_t colsum_t(int mode, const void* a, const void* x, const float* mean, c
                        (const TX*)x, mean, rstd, partial, rows, cols, rpb, nrb);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(colsum_final_kernel, dim3((cols + 63) / 64), dim3(256), 0, s, partial, out0, out1, nrb, cols,
-                     mode);
+  hipLaunchKernelGGL(colsum_final_kernel, dim3((cols + 63) / 64), dim3(256), 0, s, partial, out0, out1, nullptr, nrb,
+                     cols, mode == 1 ? 2 : 1);
   return hipGetLastError();
 }
 
@@ -481,6 +612,25 @@ hipError_t launch_ln_bwd(bool is_bf16, const void* dy, const void* x, bool x_f32
   if (rows <= 0) return hipSuccess;
   return is_bf16 ? ln_bwd_dispatch<bf16>(dy, x, x_f32, gamma, mean, rstd, resid, resid_f32, dx, dx_f32, rows, h, s)
                  : ln_bwd_dispatch<float>(dy, x, x_f32, gamma, mean, rstd, resid, resid_f32, dx, dx_f32, rows, h, s);
+}
+
+bool ln_bwd_sums_supported(int h) { return h % 8 == 0 && (h / 8 + kLnThreads - 1) / kLnThreads <= 4; }
+
+size_t ln_bwd_sums_partial_floats(int rows, int h, int nsum) {
+  const int rpb = ln_sums_rpb(rows);
+  return (size_t)nsum * ((rows + rpb - 1) / rpb) * h;
+}
+
+hipError_t launch_ln_bwd_sums(bool is_bf16, const void* dy, const void* x, bool x_f32, const void* gamma,
+                              const float* mean, const float* rstd, const void* resid, bool resid_f32, void* dx,
+                              float* dx_f32, float* part, float* dgamma, float* dbeta, float* dsum, int rows, int h,
+                              hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (!ln_bwd_sums_supported(h)) return hipErrorNotSupported;
+  return is_bf16 ? ln_bwd_sums_dispatch<bf16>(dy, x, x_f32, gamma, mean, rstd, resid, resid_f32, dx, dx_f32, part,
+                                              dgamma, dbeta, dsum, rows, h, s)
+                 : ln_bwd_sums_dispatch<float>(dy, x, x_f32, gamma, mean, rstd, resid, resid_f32, dx, dx_f32, part,
+                                               dgamma, dbeta, dsum, rows, h, s);
 }
 
 size_t colsum_partial_floats(int rows, int cols, int mode) {
