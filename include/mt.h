@@ -38,7 +38,7 @@
  *   - Precision of the bf16 path: the residual stream X2 = X + O + b_o and its
  *     gradient dX2 are kept in fp32 inside the call; everything stored between kernels
  *     as a GEMM operand (U, QKV, P, ctx, V2, A, Z, dA, dctx, dS, dQKV, partials) is bf16.
- *   - Attention of the bf16 path with head dim 128 is fused: the logits and
+ *   - Attention of the bf16 path with head dim 64 or 128 is fused: the logits and
  *     probabilities stay on chip, the saved store keeps each row's log-sum-exp (fp32)
  *     and the Q, K rounding remainders instead of P, and the backward recomputes P.
  *     Other head dims, and the fp32 path, store P and the gradients of the logits.

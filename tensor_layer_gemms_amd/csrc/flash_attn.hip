@@ -293,46 +293,54 @@ __global__ __launch_bounds__(256) void flash_fwd_kernel(FlashArgs a) {
 }
 
 // ---------------------------------------------------------------------------- backward
-// Head dim 128. Tiles [32 rows][128] that serve both row reads (ds_read_b128, 16 lanes on
-// 16 consecutive rows at one chunk) and transposing reads (a half-wave on 4 consecutive
-// rows x 4 chunks) use chunk ^ (4 (r & 3) | ((r >> 2) & 3)): 16 consecutive rows land on
-// 16 different 16-byte bank positions, and 4 consecutive rows in 4 different 64-byte
-// bank groups.
-__device__ __forceinline__ int dswz(int row, int chunk) { return chunk ^ (((row & 3) << 2) | ((row >> 2) & 3)); }
+// Head dim D = 64 or 128. Tiles [32 rows][D] that serve both row reads (ds_read_b128, 16
+// lanes on 16 consecutive rows at one chunk) and transposing reads (a half-wave on 4
+// consecutive rows x 4 chunks) XOR the chunk index so that 16 consecutive rows land on 16
+// different 16-byte bank positions and 4 consecutive rows in 4 different 64-byte bank
+// groups: D = 128 (256-byte rows) chunk ^ (4 (r & 3) | ((r >> 2) & 3)); D = 64 (128-byte
+// rows, two per bank window) chunk ^ (4 ((r >> 1) & 1) | ((r >> 2) & 3)).
+template <int D>
+__device__ __forceinline__ int dswz(int row, int chunk) {
+  static_assert(D == 64 || D == 128, "backward head dims");
+  if constexpr (D == 128) return chunk ^ (((row & 3) << 2) | ((row >> 2) & 3));
+  else return chunk ^ ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+}
 
-constexpr int kBwdD = 128;
-
-// DMA of a [32][128] tile (dual swizzle) from rows r0.. of a column slice; rows past the
+// DMA of a [32][D] tile (dual swizzle) from rows r0.. of a column slice; rows past the
 // sequence read zeros through the resource's range (as for dma_tile). The lane's byte
 // offsets within the tile are computed once per leading dimension (DualOffsets).
+template <int D>
 struct DualOffsets {
-  uint32_t off[4];
+  static constexpr int CPR = D / 8, RPI = 64 / CPR, PER = 32 * D / 512 / 2;  // per wave, 2 waves
+  uint32_t off[PER];
   __device__ __forceinline__ void init(int64_t ld, int wave, int lane) {
-    constexpr int CPR = 16, RPI = 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < PER; ++i) {
       const int q = wave + i * 2;
-      const int r = q * RPI + lane / CPR, c = dswz(r, lane % CPR);
+      const int r = q * RPI + lane / CPR, c = dswz<D>(r, lane % CPR);
       off[i] = (uint32_t)(((int64_t)r * ld + c * 8) * 2);
     }
   }
 };
 
-__device__ __forceinline__ void dma_tile_dual(bf16* lds, __amdgpu_buffer_rsrc_t rsrc, const DualOffsets& o,
+template <int PER>
+__device__ __forceinline__ void dma_tile_dual(bf16* lds, __amdgpu_buffer_rsrc_t rsrc, const uint32_t (&off)[PER],
                                               uint32_t row_bytes, int wave) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(lds + (wave + i * 2) * 512), 16, o.off[i] + row_bytes, 0,
-                                             0, 0);
+  for (int i = 0; i < PER; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(lds + (wave + i * 2) * 512), 16, off[i] + row_bytes, 0, 0,
+                                             0);
 }
 
 // Row read of a dual-swizzled tile: lane's row r32, 16-k step ks (B operand).
+template <int D>
 __device__ __forceinline__ bf16x8 row_frag(const bf16* t, int r32, int ks, int h) {
-  return *reinterpret_cast<const bf16x8*>(t + r32 * kBwdD + (dswz(r32, 2 * ks + h) << 3));
+  return *reinterpret_cast<const bf16x8*>(t + r32 * D + (dswz<D>(r32, 2 * ks + h) << 3));
 }
 // Transposing read of a dual-swizzled tile for output column block nb and 16-row slice
 // sl, matching the A operand taken from an accumulator (rows 16 sl + 4 h + 0..3 and
 // 16 sl + 8 + 4 h + 0..3 of the tile).
+template <int D>
 __device__ __forceinline__ bf16x8 tr_frag(const bf16* t, int sl, int nb, int lane) {
   const int h = lane >> 5;
   const int col = 32 * nb + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
@@ -340,7 +348,7 @@ __device__ __forceinline__ bf16x8 tr_frag(const bf16* t, int sl, int nb, int lan
 #pragma unroll
   for (int rr = 0; rr < 2; ++rr) {
     const int r = 16 * sl + 8 * rr + 4 * h + ((lane & 15) >> 2);
-    v[rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(t + r * kBwdD + (dswz(r, col >> 3) << 3) + (col & 7)));
+    v[rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(t + r * D + (dswz<D>(r, col >> 3) << 3) + (col & 7)));
   }
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
 }
@@ -353,9 +361,10 @@ __device__ __forceinline__ bf16x8 acc_operand(const float* v, int sl) {
   return p;
 }
 
+template <int D>
 __device__ __forceinline__ void store_rows(bf16* out, const f32x16* acc, float scale, int h) {
 #pragma unroll
-  for (int nb = 0; nb < kBwdD / 32; ++nb)
+  for (int nb = 0; nb < D / 32; ++nb)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       float v[4] = {acc[nb][4 * q] * scale, acc[nb][4 * q + 1] * scale, acc[nb][4 * q + 2] * scale,
@@ -371,11 +380,14 @@ __device__ __forceinline__ void store_rows(bf16* out, const f32x16* acc, float s
 //   dS^T = P^T * (dP^T - D[q]) with dP^T = V dO^T, dK += dS^T Q / sqrt(d).
 // Per stage: Q_hi, Q_lo, dO tiles, then 1 KB for L and 1 KB for D of the 32 queries (one
 // DMA instruction each, wave 0 and wave 1; the first 128 bytes carry the values).
-constexpr int kKvStage = 3 * 32 * kBwdD + 1024;
-constexpr int kQStage = 3 * 32 * kBwdD;
+template <int D>
+constexpr int kv_stage() { return 3 * 32 * D + 1024; }
+template <int D>
+constexpr int q_stage() { return 3 * 32 * D; }
 
+template <int D>
 __device__ __forceinline__ void flash_bwd_kv(const FlashArgs& a, int kblk, int z, bf16* smem) {
-  constexpr int D = kBwdD, KS = D / 16, NB = D / 32, TILE = 32 * D, STAGE = kKvStage;
+  constexpr int KS = D / 16, NB = D / 32, TILE = 32 * D, STAGE = kv_stage<D>();
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5, r32 = lane & 31;
   const int b = z / a.heads, hd = z % a.heads;
@@ -410,7 +422,7 @@ __device__ __forceinline__ void flash_bwd_kv(const FlashArgs& a, int kblk, int z
       __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.D) + (int64_t)z * a.seq, (short)0, a.seq * 4, 0x00020000);
   const int qb0 = (kblk * 64) / 32, nqb = (a.seq + 31) / 32;
   const int nsteps = nqb - qb0;
-  DualOffsets oq, oo;
+  DualOffsets<D> oq, oo;
   oq.init(a.ldq, wave, lane);
   oo.init(a.ldc, wave, lane);
   // lanes 0..7 of one instruction fetch the 32 floats; the others read past the range
@@ -419,9 +431,9 @@ __device__ __forceinline__ void flash_bwd_kv(const FlashArgs& a, int kblk, int z
   auto issue = [&](int t) {
     bf16* st = smem + (t % kStages) * STAGE;
     const uint32_t r0 = (uint32_t)((qb0 + t) * 32);
-    dma_tile_dual(st, rq, oq, r0 * (uint32_t)a.ldq * 2u, wave);
-    dma_tile_dual(st + TILE, rql, oq, r0 * (uint32_t)a.ldq * 2u, wave);
-    dma_tile_dual(st + 2 * TILE, rdo, oo, r0 * (uint32_t)a.ldc * 2u, wave);
+    dma_tile_dual(st, rq, oq.off, r0 * (uint32_t)a.ldq * 2u, wave);
+    dma_tile_dual(st + TILE, rql, oq.off, r0 * (uint32_t)a.ldq * 2u, wave);
+    dma_tile_dual(st + 2 * TILE, rdo, oo.off, r0 * (uint32_t)a.ldc * 2u, wave);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(wave == 0 ? rl : rd, (lds_ptr_t)(st + 3 * TILE + wave * 512), 16,
                                              lane_ld + r0 * 4u, 0, 0, 0);
   };
@@ -433,8 +445,8 @@ __device__ __forceinline__ void flash_bwd_kv(const FlashArgs& a, int kblk, int z
 #pragma unroll
     for (int r = 0; r < 16; ++r) dv[nb][r] = dk[nb][r] = 0.f;
 
-  // Per wave: 3 tiles of 8 DMA instructions over 2 waves, plus one for L or D.
-  constexpr int LOADS = 3 * 8 / 2 + 1;
+  // Per wave: 3 tiles of 32 D / 512 DMA instructions over 2 waves, plus one for L or D.
+  constexpr int LOADS = 3 * DualOffsets<D>::PER + 1;
   if (nsteps > 0) issue(0);
   if (nsteps > 1) issue(1);
   for (int t = 0; t < nsteps; ++t) {
@@ -468,7 +480,7 @@ __device__ __forceinline__ void flash_bwd_kv(const FlashArgs& a, int kblk, int z
     for (int r = 0; r < 16; ++r) st[r] = dpt[r] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 qf = row_frag(sQ, r32, ks, h), qfl = row_frag(sQl, r32, ks, h), of = row_frag(sO, r32, ks, h);
+      const bf16x8 qf = row_frag<D>(sQ, r32, ks, h), qfl = row_frag<D>(sQl, r32, ks, h), of = row_frag<D>(sO, r32, ks, h);
       st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, kh[ks], st, 0, 0, 0);
       dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(of, vv[ks], dpt, 0, 0, 0);
       st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, kl[ks], st, 0, 0, 0);
@@ -491,23 +503,24 @@ __device__ __forceinline__ void flash_bwd_kv(const FlashArgs& a, int kblk, int z
       const bf16x8 pp = acc_operand(p, sl), dd = acc_operand(ds, sl);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        dv[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(sO, sl, nb, lane), pp, dv[nb], 0, 0, 0);
-        dk[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(sQ, sl, nb, lane), dd, dk[nb], 0, 0, 0);
+        dv[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(sO, sl, nb, lane), pp, dv[nb], 0, 0, 0);
+        dk[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(sQ, sl, nb, lane), dd, dk[nb], 0, 0, 0);
       }
     }
   }
   if (key_ok) {
     bf16* out = static_cast<bf16*>(a.dqkv) + ((int64_t)b * a.seq + key) * a.ldq;
-    store_rows(out + ck, dk, a.scale, h);
-    store_rows(out + cv, dv, 1.f, h);
+    store_rows<D>(out + ck, dk, a.scale, h);
+    store_rows<D>(out + cv, dv, 1.f, h);
   }
 }
 
 // dQ. Work-group: 64 query rows of sequence b, head k; streams the key blocks (32 keys)
 // they see. Lane l owns query row (l & 31).
 //   P = exp(S / sqrt(d) - L), dS = P * (dO V^T - D), dQ += dS K / sqrt(d).
+template <int D>
 __device__ __forceinline__ void flash_bwd_q(const FlashArgs& a, int qb, int z, bf16* smem) {
-  constexpr int D = kBwdD, KS = D / 16, NB = D / 32, TILE = 32 * D;
+  constexpr int KS = D / 16, NB = D / 32, TILE = 32 * D;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5, r32 = lane & 31;
   const int b = z / a.heads, hd = z % a.heads;
@@ -540,14 +553,19 @@ __device__ __forceinline__ void flash_bwd_q(const FlashArgs& a, int qb, int z, b
   const __amdgpu_buffer_rsrc_t rv = seq_rsrc(qkv + cv, a.ldq, a.seq);
   const int kend = min(a.seq, (qb + 1) * kFlashRows);
   const int nsteps = (kend + 31) / 32;
-  DualOffsets ok;
-  ok.init(a.ldq, wave, lane);
+  DualOffsets<D> koff;
+  koff.init(a.ldq, wave, lane);
   auto issue = [&](int t) {
     bf16* st = smem + (t % kStages) * 3 * TILE;
     const uint32_t rb = (uint32_t)(t * 32) * (uint32_t)a.ldq * 2u;
-    dma_tile_dual(st, rk, ok, rb, wave);
-    dma_tile_dual(st + TILE, rkl, ok, rb, wave);
-    dma_tile_dual(st + 2 * TILE, rv, ok, rb, wave);
+#pragma unroll
+    for (int i = 0; i < DualOffsets<D>::PER; ++i) {  // K_hi, K_lo and V tiles of key block t
+      const int q = (wave + i * 2) * 512;
+      const uint32_t off = koff.off[i] + rb;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(st + q), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rkl, (lds_ptr_t)(st + TILE + q), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(st + 2 * TILE + q), 16, off, 0, 0, 0);
+    }
   };
 
   const float scale2 = a.scale * kLog2e;
@@ -557,7 +575,7 @@ __device__ __forceinline__ void flash_bwd_q(const FlashArgs& a, int qb, int z, b
 #pragma unroll
     for (int r = 0; r < 16; ++r) dq[nb][r] = 0.f;
 
-  constexpr int LOADS = 3 * 8 / 2;  // per wave: 3 tiles of 8 DMA instructions, over 2 waves
+  constexpr int LOADS = 3 * DualOffsets<D>::PER;  // per wave: 3 tiles, over 2 waves
   issue(0);
   if (nsteps > 1) issue(1);
   for (int t = 0; t < nsteps; ++t) {
@@ -577,7 +595,7 @@ __device__ __forceinline__ void flash_bwd_q(const FlashArgs& a, int qb, int z, b
     for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 kf = row_frag(sK, r32, ks, h), kfl = row_frag(sKl, r32, ks, h), vf = row_frag(sV, r32, ks, h);
+      const bf16x8 kf = row_frag<D>(sK, r32, ks, h), kfl = row_frag<D>(sKl, r32, ks, h), vf = row_frag<D>(sV, r32, ks, h);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qh[ks], s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, of[ks], dp, 0, 0, 0);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfl, qh[ks], s, 0, 0, 0);
@@ -598,26 +616,27 @@ __device__ __forceinline__ void flash_bwd_q(const FlashArgs& a, int qb, int z, b
       const bf16x8 dd = acc_operand(ds, sl);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
-        dq[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(sK, sl, nb, lane), dd, dq[nb], 0, 0, 0);
+        dq[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(sK, sl, nb, lane), dd, dq[nb], 0, 0, 0);
     }
   }
-  if (row_ok) store_rows(static_cast<bf16*>(a.dqkv) + ((int64_t)b * a.seq + row) * a.ldq + cq, dq, a.scale, h);
+  if (row_ok) store_rows<D>(static_cast<bf16*>(a.dqkv) + ((int64_t)b * a.seq + row) * a.ldq + cq, dq, a.scale, h);
 }
 
 // Both backward parts in one grid, each walking its deepest blocks first: blockIdx.x
 // interleaves them (even: key block x / 2 of dK, dV; odd: row block of dQ, deepest
 // first), so the grid's critical path is the longer of the two chains, not their sum.
+template <int D>
 __global__ __launch_bounds__(128) void flash_bwd_kernel(FlashArgs a) {
-  constexpr int SMEM = kStages * (kKvStage > kQStage ? kKvStage : kQStage);
+  constexpr int SMEM = kStages * (kv_stage<D>() > q_stage<D>() ? kv_stage<D>() : q_stage<D>());
   __shared__ __attribute__((aligned(1024))) bf16 smem[SMEM];
   dma_lds_escape(smem);
   int z, x;
   xcd_block((int)gridDim.x, z, x);
   const int nqb = (a.seq + kFlashRows - 1) / kFlashRows, nkb = (a.seq + 63) / 64;
   if ((x & 1) == 0) {
-    if (x / 2 < nkb) flash_bwd_kv(a, x / 2, z, smem);
+    if (x / 2 < nkb) flash_bwd_kv<D>(a, x / 2, z, smem);
   } else {
-    if (x / 2 < nqb) flash_bwd_q(a, nqb - 1 - x / 2, z, smem);
+    if (x / 2 < nqb) flash_bwd_q<D>(a, nqb - 1 - x / 2, z, smem);
   }
 }
 
@@ -634,10 +653,11 @@ static bool flash_extents_ok(const FlashArgs& a) {
 hipError_t launch_flash_bwd(const FlashArgs& a, int d, hipStream_t s) {
   if (a.seq <= 0 || a.batch <= 0 || a.heads <= 0) return hipSuccess;
   if (!flash_extents_ok(a)) return hipErrorInvalidValue;
-  if (d != kBwdD) return hipErrorInvalidValue;
   const int nqb = (a.seq + kFlashRows - 1) / kFlashRows, nkb = (a.seq + 63) / 64;
   const int n = 2 * (nqb > nkb ? nqb : nkb);
-  hipLaunchKernelGGL(flash_bwd_kernel, dim3(n, a.batch * a.heads), dim3(128), 0, s, a);
+  if (d == 128) hipLaunchKernelGGL(flash_bwd_kernel<128>, dim3(n, a.batch * a.heads), dim3(128), 0, s, a);
+  else if (d == 64) hipLaunchKernelGGL(flash_bwd_kernel<64>, dim3(n, a.batch * a.heads), dim3(128), 0, s, a);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -33,11 +33,11 @@ struct FlashArgs {
 };
 
 // Head dims the fused kernels handle (forward and backward).
-inline bool flash_supported(int d) { return d == 128; }
+inline bool flash_supported(int d) { return d == 64 || d == 128; }
 
 // Forward: ctx and lse from qkv, qkv_lo (d = 64 or 128).
 hipError_t launch_flash_fwd(const FlashArgs& a, int d, hipStream_t s);
-// Backward: dQ, dK, dV into dqkv from qkv, qkv_lo, dctx, lse and D (d = 128).
+// Backward: dQ, dK, dV into dqkv from qkv, qkv_lo, dctx, lse and D (d = 64 or 128).
 hipError_t launch_flash_bwd(const FlashArgs& a, int d, hipStream_t s);
 
 }  // namespace mt

@@ -44,13 +44,21 @@ def _shape(**kw):
 
 
 def test_buffer_queries_consistent(lib):
-    s = _shape()
-    M, h, f, a, seq = 4096, 1024, 4096, 16, 1024
+    s = _shape()  # head dim 64: fused attention
+    M, h, f, a, seq, B = 4096, 1024, 4096, 16, 1024, 4
     saved = mt.layer_saved_bytes(s)
-    # U, QKV, P, ctx, V2, A, Z in bf16, the fp32 residual X2, four fp32 row statistics
-    need = 2 * (M * h * 2 + M * 3 * h + 4 * a * seq * seq + M * h + 2 * M * f) + 4 * M * h + 16 * M
+    # U, QKV, the Q/K rounding remainders (QKV layout), ctx, V2, A, Z in bf16, the fp32
+    # residual X2, four fp32 row statistics and the fp32 row log-sum-exp (no P)
+    need = 2 * (M * h + 2 * M * 3 * h + M * h + M * h + 2 * M * f) + 4 * M * h + 16 * M + 4 * B * a * seq
     assert need <= saved <= need + 64 * 256
-    assert mt.layer_workspace_bytes(s) >= 4 * 4 * a * seq * seq  # fp32 scores
+    assert mt.layer_workspace_bytes(s) >= 4 * M * (3 * h + 2 * h)  # fp32 QKV partials
+    # head dim 160 keeps the materialised attention: P (bf16) in the saved store, fp32
+    # scores in the workspace
+    s160 = _shape(h=640, heads=4, seq=256, micro_batch=2)
+    M1, h1, f1, a1, q1 = 512, 640, 2560, 4, 256
+    need160 = 2 * (M1 * h1 * 2 + M1 * 3 * h1 + 2 * a1 * q1 * q1 + M1 * h1 + 2 * M1 * f1) + 4 * M1 * h1 + 16 * M1
+    assert need160 <= mt.layer_saved_bytes(s160) <= need160 + 64 * 256
+    assert mt.layer_workspace_bytes(s160) >= 4 * 2 * a1 * q1 * q1
     assert mt.mlp_saved_bytes(s) == 2 * 2 * M * f
     s8 = _shape(h=12288, heads=96, seq=2048, micro_batch=1, tp=8)
     s8b = _shape(h=12288, heads=96, seq=2048, micro_batch=1, tp=8, shard=7)
