@@ -7,7 +7,7 @@ namespace mt {
 
 namespace {
 
-constexpr int kFlashRows = 64;  // query rows per work-group (2 waves of 32)
+constexpr int kFlashRows = 64;  // query rows per work-group (waves of 32 rows)
 constexpr int kFlashKeys = 32;  // keys per streamed block
 // LDS ring depth: every row block of a head streams the same key blocks at about the same
 // pace, so each block's loads tend to miss in L2 together; three stages give them two

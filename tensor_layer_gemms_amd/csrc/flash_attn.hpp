@@ -1,13 +1,14 @@
 // Fused causal attention of the layer shard's heads (bf16 path, head dim 64 or 128).
 //
-// Forward: a work-group owns 64 query rows of one (sequence, head) and streams the keys
-// in blocks of 32 through LDS (DMA loads, two stages). Per block it forms the logits
-// S = (Q_hi K_hi^T + Q_hi K_lo^T + Q_lo K_hi^T) / sqrt(d) on the matrix cores, applies the
-// causal mask, updates the running row maximum and exponential sum (online softmax) and
-// accumulates O += P V with P taken straight from the logit accumulators (rounded to
-// bf16 as the matrix-core operand). S and P never reach HBM. It writes ctx = O / l and
-// the row log-sum-exp L = m + ln(l), from which the backward recomputes
-// P = exp(S - L).
+// Forward: a work-group owns 64 query rows of one (sequence, head); two pairs of waves
+// stream the two halves of the visible keys in blocks of 32 through their own LDS rings
+// (DMA loads, three stages) and merge their partial results at the end. Per block the
+// logits S = (Q_hi K_hi^T + Q_hi K_lo^T + Q_lo K_hi^T) / sqrt(d) are formed on the matrix
+// cores, the causal mask is applied, the running row maximum and exponential sum are
+// updated (online softmax) and O += P V is accumulated with P taken straight from the
+// logit accumulators (rounded to bf16 as the matrix-core operand). S and P never reach
+// HBM. The forward writes ctx = O / l and the row log-sum-exp L = m + ln(l), from which
+// the backward recomputes P = exp(S - L).
 //
 // Attention and its causal mask follow the layer definition of the "Megatron-LM" concept
 // report (compassingai.com), section 4.1 (the attention heads of a rank); the fused,
