@@ -70,6 +70,8 @@ def parse():
                     help="label of the kernel launch whose roofline is reported")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-optimizer", action="store_true", help="skip the fused AdamW step measurement")
+    ap.add_argument("--qk-pairs", action="store_true",
+                    help="run the MT_BF16_QK mode (attention logits from hi + lo pairs of Q and K)")
     ap.add_argument("--breakdown", action="store_true", help="also print a per-launch time breakdown (stderr)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes three times (counter calibration)")
@@ -91,30 +93,32 @@ def recompute_report(shape, ms_per_step: float, saved_bytes: int):
     """Hardware vs model FLOPs of the fused-attention path, and the activation bytes it
     does not store. The backward recomputes the attention probabilities P = exp(S - L)
     from Q, K and the saved row log-sum-exp instead of keeping P (selective
-    recomputation of the attention core); the logits are formed in three compensated
-    segments (Q_hi K_hi + Q_hi K_lo + Q_lo K_hi) and the QKV forward adds U_lo W_qk^T.
-    Counted per head product over the s (s + 1) / 2 causal (query, key) pairs, as the
-    model FLOPs are: forward 3 logit segments + P V; backward, key-block part 3 logit
-    segments + dP + dV + dK, row-block part 3 logit segments + dP + dQ."""
-    if shape.dtype != "bf16" or shape.head_dim != 128:
+    recomputation of the attention core). In the MT_BF16_QK mode the logits are formed
+    in three segments (Q_hi K_hi + Q_hi K_lo + Q_lo K_hi) and the QKV forward adds
+    U_lo W_qk^T. Counted per head product over the s (s + 1) / 2 causal (query, key)
+    pairs, as the model FLOPs are: forward n logit segments + P V; backward, key-block
+    part n logit segments + dP + dV + dK, row-block part n logit segments + dP + dQ,
+    with n = 3 (MT_BF16_QK) or 1."""
+    if shape.dtype != "bf16" or shape.head_dim not in (64, 128):
         return None
     B, s, at, d = shape.micro_batch, shape.seq, shape.heads_per_shard, shape.head_dim
     M, h, t = shape.tokens, shape.h, shape.tp
+    nseg = 3 if shape.qk_pairs else 1
     unit = 2.0 * B * at * d * s * (s + 1) / 2  # one causal head product
     model = si_model_flops(shape)
     attn_model = 6 * unit
-    attn_hw = (3 + 1) * unit + (3 + 3) * unit + (3 + 2) * unit
-    qkv_comp = 2.0 * M * (2 * h // t) * h
+    attn_hw = (nseg + 1) * unit + (nseg + 3) * unit + (nseg + 2) * unit
+    qkv_comp = 2.0 * M * (2 * h // t) * h if shape.qk_pairs else 0.0
     hw = model - attn_model + attn_hw + qkv_comp
     p_bytes = B * at * s * s * 2  # bf16 probabilities a materialised backward would keep
     return {"model_gflop": round(model / 1e9, 1), "hardware_gflop": round(hw / 1e9, 1),
             "hardware_tflops": round(hw / (ms_per_step * 1e-3) / 1e12, 1),
-            # the backward's logits recomputed in both parts (all three segments)
-            "bwd_logit_recompute_gflop": round(6 * unit / 1e9, 1),
+            # the backward's logits recomputed in both parts (every segment)
+            "bwd_logit_recompute_gflop": round(2 * nseg * unit / 1e9, 1),
             # dP formed in both backward parts (one extra head product)
             "bwd_dp_duplicate_gflop": round(unit / 1e9, 1),
-            # forward: the two extra logit segments and U_lo W_qk^T
-            "fwd_compensation_gflop": round((2 * unit + qkv_comp) / 1e9, 1),
+            # forward (MT_BF16_QK): the two extra logit segments and U_lo W_qk^T
+            "fwd_compensation_gflop": round(((nseg - 1) * unit + qkv_comp) / 1e9, 1),
             "p_bytes_not_stored": int(p_bytes), "saved_store_bytes": int(saved_bytes)}
 
 
@@ -197,11 +201,14 @@ def main():
         build()
     mt.lib()
     w = si.WORKLOADS[args.workload]
-    shape = w.shape
+    shape = w.shape.replace(qk_pairs=True) if args.qk_pairs else w.shape
+    if shape.qk_pairs and shape.dtype != "bf16":
+        sys.exit("bench.py: --qk-pairs applies to bf16 workloads only")
     print(f"[bench] generating seeded inputs for {args.workload}", file=sys.stderr, flush=True)
     case = si.workload_case(args.workload)
     dev = lambda a: torch.from_numpy(a).cuda().to(torch.bfloat16 if shape.dtype == "bf16" else torch.float32)  # noqa
-    sh = mt.make_shape(shape.h, shape.heads, shape.seq, shape.micro_batch, shape.tp, shape.shard, shape.dtype)
+    mode = "bf16qk" if shape.qk_pairs else shape.dtype
+    sh = mt.make_shape(shape.h, shape.heads, shape.seq, shape.micro_batch, shape.tp, shape.shard, mode)
     L = w.layers
     weights = [{k: dev(v) for k, v in p.items()} for p in case.layers]
     grads = [{k: torch.empty(v.shape, dtype=torch.float32, device="cuda") for k, v in p.items()} for p in case.layers]
@@ -289,6 +296,7 @@ def main():
         "config": {"workload": args.workload, "h": shape.h, "heads": shape.heads, "heads_per_shard":
                    shape.heads_per_shard, "head_dim": shape.head_dim, "seq": shape.seq,
                    "micro_batch": shape.micro_batch, "tp": shape.tp, "shard": shape.shard, "layers": L,
+                   "mode": mode,
                    "gflop_per_step_causal": round(flops_step / 1e9, 1),
                    "gflop_per_step_dense": round(dense_step / 1e9, 1)},
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),

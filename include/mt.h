@@ -29,7 +29,9 @@
  *     is enqueued asynchronously on it; faults inside kernels surface at the caller's
  *     next synchronisation.
  *   - Activations and weights have the shape's dtype (MT_BF16: bfloat16 storage with
- *     fp32 accumulation and fp32 LayerNorm/softmax/GeLU math; MT_FP32: fp32 throughout).
+ *     fp32 accumulation and fp32 LayerNorm/softmax/GeLU math; MT_FP32: fp32 throughout;
+ *     MT_BF16_QK: as MT_BF16, with the attention logits formed from Q and K carried as
+ *     bf16 hi + lo pairs, see below).
  *     Parameter gradients are always fp32 and are overwritten (not accumulated).
  *   - Every argument is validated before anything is launched; on error nothing is
  *     launched and the status says why (mt_status_string).
@@ -38,10 +40,19 @@
  *   - Precision of the bf16 path: the residual stream X2 = X + O + b_o and its
  *     gradient dX2 are kept in fp32 inside the call; everything stored between kernels
  *     as a GEMM operand (U, QKV, P, ctx, V2, A, Z, dA, dctx, dS, dQKV, partials) is bf16.
- *   - Attention of the bf16 path with head dim 64 or 128 is fused: the logits and
+ *   - MT_BF16_QK: the softmax's exponent magnifies errors of the logits Q K^T / sqrt(d)
+ *     by their own size, and with bf16 Q and K (8 significant bits) a shard whose logits
+ *     reach the tens can miss the 2e-2 normwise bar on the attention gradients. In this
+ *     mode LayerNorm 1 also writes the rounding remainder U_lo of U, the Q and K
+ *     columns of the projection take (U + U_lo) W^T and are stored as hi + lo bf16
+ *     pairs, and the logits are Q_hi K_hi^T + Q_hi K_lo^T + Q_lo K_hi^T (Q and K to
+ *     about 16 bits). Cost: one more GEMM over the Q and K columns, two more logit
+ *     products, and the remainders in the saved store and workspace.
+ *   - Attention of the bf16 paths with head dim 64 or 128 is fused: the logits and
  *     probabilities stay on chip, the saved store keeps each row's log-sum-exp (fp32)
- *     and the Q, K rounding remainders instead of P, and the backward recomputes P.
- *     Other head dims, and the fp32 path, store P and the gradients of the logits.
+ *     (and under MT_BF16_QK the Q, K remainders) instead of P, and the backward
+ *     recomputes P. Other head dims, and the fp32 path, store P and the gradients of
+ *     the logits.
  */
 #ifndef MT_H_
 #define MT_H_
@@ -61,7 +72,7 @@ typedef enum {
   MT_ERR_WORKSPACE = 4    /* saved / workspace buffer smaller than the *_bytes query */
 } mt_status;
 
-typedef enum { MT_BF16 = 0, MT_FP32 = 1 } mt_dtype;
+typedef enum { MT_BF16 = 0, MT_FP32 = 1, MT_BF16_QK = 2 } mt_dtype;
 
 /* One TP shard of one layer. h and heads are the GLOBAL (unsharded) sizes; the shard
  * owns heads/tp heads and 4h/tp FFN columns. */

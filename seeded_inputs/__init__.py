@@ -51,6 +51,8 @@ class LayerShape:
     tp: int = 1
     shard: int = 0
     dtype: str = "bf16"  # "bf16" or "fp32"
+    # bf16 only: the attention logits from hi + lo bf16 pairs of Q and K (MT_BF16_QK)
+    qk_pairs: bool = False
 
     @property
     def tokens(self) -> int:

@@ -18,7 +18,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmt.so")
 
 MT_OK, MT_ERR_INVALID_ARG, MT_ERR_UNSUPPORTED, MT_ERR_HIP, MT_ERR_WORKSPACE = range(5)
-MT_BF16, MT_FP32 = 0, 1
+MT_BF16, MT_FP32, MT_BF16_QK = 0, 1, 2
+_DTYPES = {"bf16": MT_BF16, "fp32": MT_FP32, "bf16qk": MT_BF16_QK}
 
 WEIGHT_NAMES = ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_o", "b_o",
                 "ln2_g", "ln2_b", "w_fc1", "b_fc1", "w_fc2", "b_fc2")
@@ -97,7 +98,11 @@ def _check(fn: str, status: int) -> None:
 
 def make_shape(h: int, heads: int, seq: int, micro_batch: int, tp: int = 1, shard: int = 0,
                dtype: str = "bf16") -> Shape:
-    return Shape(h, heads, seq, micro_batch, tp, shard, MT_BF16 if dtype == "bf16" else MT_FP32)
+    """dtype: "bf16" (MT_BF16), "fp32" (MT_FP32) or "bf16qk" (MT_BF16_QK: bf16 with the
+    attention logits formed from hi + lo pairs of Q and K)."""
+    if dtype not in _DTYPES:
+        raise ValueError(f"dtype {dtype!r}: expected one of {sorted(_DTYPES)}")
+    return Shape(h, heads, seq, micro_batch, tp, shard, _DTYPES[dtype])
 
 
 def _ptr(t) -> int:
@@ -173,7 +178,7 @@ def _expect(name: str, t, numel: int, dtype=None) -> None:
 
 def _act_dtype(shape: Shape):
     import torch
-    return torch.bfloat16 if shape.dtype == MT_BF16 else torch.float32
+    return torch.float32 if shape.dtype == MT_FP32 else torch.bfloat16
 
 
 def check_layer_tensors(shape: Shape, weights: Dict[str, object], grads: Optional[Dict[str, object]] = None,

@@ -38,7 +38,8 @@ __device__ __forceinline__ int vswz(int row, int chunk) {
 // 4 GiB). A wave instruction fills 1 KB of LDS: lane L writes bytes [16 L, +16) of it =
 // tile row q * RPI + L / CPR, stored chunk L % CPR, which holds the logical chunk the
 // swizzle maps there. The lane's byte offset within the tile is the same for every key
-// block, so it is computed once (TileOffsets) and each block adds kb * ld * 2.
+// block, so it is computed once (TileOffsets) and each block adds kb * ld * 2 (the
+// kernels issue the loads themselves).
 template <int D, bool VTILE, int NW>
 struct TileOffsets {
   static constexpr int CPR = D / 8, RPI = 64 / CPR, INSTR = 32 * D / 512, PER = INSTR / NW;
@@ -55,13 +56,11 @@ struct TileOffsets {
   }
 };
 
-template <int D, bool VTILE, int NW>
-__device__ __forceinline__ void dma_tile(bf16* lds, __amdgpu_buffer_rsrc_t rsrc, const TileOffsets<D, VTILE, NW>& o,
-                                         uint32_t row_bytes, int wave) {
-#pragma unroll
-  for (int i = 0; i < TileOffsets<D, VTILE, NW>::PER; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(lds + (wave + i * NW) * 512), 16, o.off[i] + row_bytes, 0,
-                                             0, 0);
+// One 16-byte LDS-DMA load per lane into dst (the wave's 512-element slot of a tile).
+// The kernels' loader lambdas call this instead of the builtin: a lambda is compiled for
+// the host too, and there the target builtin would drop the kernel's host stub.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, bf16* dst, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 16, off, 0, 0, 0);
 }
 
 // Work-groups are handed to the 8 XCDs round-robin by linear id. Maps a grid of
@@ -98,7 +97,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t seq_rsrc(const bf16* base, int
 // running (O, m, l) to pair 0 through LDS and pair 0 merges and writes. Lane l of a wave
 // owns query row (l & 31); the logit accumulator of a 32-key block holds keys
 // 8 q + 4 (l >> 5) + j in register 4 q + j (the operand-swapped MFMA layout).
-template <int D>
+// COMP: the logits take the compensated form Q_hi K_hi^T + Q_hi K_lo^T + Q_lo K_hi^T
+// (a.qkv_lo holds the remainders); otherwise Q K^T with the bf16 Q and K.
+template <int D, bool COMP>
 __global__ __launch_bounds__(256) void flash_fwd_kernel(FlashArgs a) {
   constexpr int KS = D / 16, NB = D / 32, TILE = kFlashKeys * D, RING = kStages * 3 * TILE;
   __shared__ __attribute__((aligned(1024))) bf16 smem[2 * RING];
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(256) void flash_fwd_kernel(FlashArgs a) {
   for (int ks = 0; ks < KS; ++ks) {
     if (row_ok) {
       qh[ks] = *reinterpret_cast<const bf16x8*>(qkv + (int64_t)row * a.ldq + cq + 16 * ks + 8 * h);
-      ql[ks] = *reinterpret_cast<const bf16x8*>(qlo + (int64_t)row * a.ldq + cq + 16 * ks + 8 * h);
+      if constexpr (COMP) ql[ks] = *reinterpret_cast<const bf16x8*>(qlo + (int64_t)row * a.ldq + cq + 16 * ks + 8 * h);
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) qh[ks][e] = ql[ks][e] = (bf16)0.f;
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(256) void flash_fwd_kernel(FlashArgs a) {
   }
 
   const __amdgpu_buffer_rsrc_t rk = seq_rsrc(qkv + ck, a.ldq, a.seq);
-  const __amdgpu_buffer_rsrc_t rkl = seq_rsrc(qlo + ck, a.ldq, a.seq);
+  const __amdgpu_buffer_rsrc_t rkl = seq_rsrc(COMP ? qlo + ck : qkv + ck, a.ldq, a.seq);
   const __amdgpu_buffer_rsrc_t rv = seq_rsrc(qkv + cv, a.ldq, a.seq);
   const int kend = min(a.seq, (qb + 1) * kFlashRows);  // keys this row block can see
   const int nsteps = (kend + kFlashKeys - 1) / kFlashKeys;
@@ -146,9 +147,13 @@ __global__ __launch_bounds__(256) void flash_fwd_kernel(FlashArgs a) {
   auto issue = [&](int j) {  // key block tb + j into stage j % kStages of this pair's ring
     bf16* st = ring + (j % kStages) * 3 * TILE;
     const uint32_t rb = (uint32_t)((tb + j) * kFlashKeys) * (uint32_t)a.ldq * 2u;
-    dma_tile(st, rk, ok, rb, wv);
-    dma_tile(st + TILE, rkl, ok, rb, wv);
-    dma_tile(st + 2 * TILE, rv, ov, rb, wv);
+#pragma unroll
+    for (int i = 0; i < TileOffsets<D, false, 2>::PER; ++i) {  // K_hi, K_lo and V tiles of key block tb + j
+      const int q = (wv + i * 2) * 512;
+      lds_dma16(rk, st + q, ok.off[i] + rb);
+      if (COMP) lds_dma16(rkl, st + TILE + q, ok.off[i] + rb);
+      lds_dma16(rv, st + 2 * TILE + q, ov.off[i] + rb);
+    }
   };
 
   // Per-lane LDS offsets. K fragment (B operand of S): key row r32, chunk 2 ks + h.
@@ -162,10 +167,10 @@ __global__ __launch_bounds__(256) void flash_fwd_kernel(FlashArgs a) {
     for (int r = 0; r < 16; ++r) o[nb][r] = 0.f;
   float m = -__builtin_inff(), l = 0.f;
 
-  // Per wave: 3 tiles of 32 D / 512 DMA instructions, over the pair's 2 waves. Both
-  // pairs pass the same number of work-group barriers (half iterations; pair 1 has at
-  // most one block fewer and idles through the last).
-  constexpr int LOADS = 3 * (32 * D / 512) / 2;
+  // Per wave: 3 tiles (2 without the K remainders) of 32 D / 512 DMA instructions, over
+  // the pair's 2 waves. Both pairs pass the same number of work-group barriers (half
+  // iterations; pair 1 has at most one block fewer and idles through the last).
+  constexpr int LOADS = (COMP ? 3 : 2) * (32 * D / 512) / 2;
   if (cnt > 0) issue(0);
   if (cnt > 1) issue(1);
   for (int j = 0; j < half; ++j) {
@@ -184,7 +189,7 @@ __global__ __launch_bounds__(256) void flash_fwd_kernel(FlashArgs a) {
     if (j >= cnt || kb > r0) continue;
     const bool diag = kb == r0;
 
-    // S block: 32 keys x this wave's 32 rows, three compensated segments.
+    // S block: 32 keys x this wave's 32 rows (three segments when compensated).
     f32x16 s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
@@ -192,10 +197,12 @@ __global__ __launch_bounds__(256) void flash_fwd_kernel(FlashArgs a) {
     for (int ks = 0; ks < KS; ++ks) {
       const int off = r32 * D + (kswz<D>(r32, 2 * ks + h) << 3);
       const bf16x8 kh = *reinterpret_cast<const bf16x8*>(sK + off);
-      const bf16x8 kl = *reinterpret_cast<const bf16x8*>(sKl + off);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qh[ks], s, 0, 0, 0);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, qh[ks], s, 0, 0, 0);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, ql[ks], s, 0, 0, 0);
+      if constexpr (COMP) {
+        const bf16x8 kl = *reinterpret_cast<const bf16x8*>(sKl + off);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, qh[ks], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, ql[ks], s, 0, 0, 0);
+      }
     }
 
     // Online softmax (row shared by lanes l and l ^ 32), in log2 units of the scaled
@@ -306,9 +313,9 @@ __device__ __forceinline__ int dswz(int row, int chunk) {
   else return chunk ^ ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
 }
 
-// DMA of a [32][D] tile (dual swizzle) from rows r0.. of a column slice; rows past the
-// sequence read zeros through the resource's range (as for dma_tile). The lane's byte
-// offsets within the tile are computed once per leading dimension (DualOffsets).
+// Per-lane byte offsets of the DMA loads of a [32][D] tile (dual swizzle) relative to the
+// tile's first row, computed once per leading dimension; a block adds its row offset, and
+// rows past the sequence read zeros through the resource's range (as for dma_tile).
 template <int D>
 struct DualOffsets {
   static constexpr int CPR = D / 8, RPI = 64 / CPR, PER = 32 * D / 512 / 2;  // per wave, 2 waves
@@ -322,15 +329,6 @@ struct DualOffsets {
     }
   }
 };
-
-template <int PER>
-__device__ __forceinline__ void dma_tile_dual(bf16* lds, __amdgpu_buffer_rsrc_t rsrc, const uint32_t (&off)[PER],
-                                              uint32_t row_bytes, int wave) {
-#pragma unroll
-  for (int i = 0; i < PER; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(lds + (wave + i * 2) * 512), 16, off[i] + row_bytes, 0, 0,
-                                             0);
-}
 
 // Row read of a dual-swizzled tile: lane's row r32, 16-k step ks (B operand).
 template <int D>
@@ -385,7 +383,7 @@ constexpr int kv_stage() { return 3 * 32 * D + 1024; }
 template <int D>
 constexpr int q_stage() { return 3 * 32 * D; }
 
-template <int D>
+template <int D, bool COMP>
 __device__ __forceinline__ void flash_bwd_kv(const FlashArgs& a, int kblk, int z, bf16* smem) {
   constexpr int KS = D / 16, NB = D / 32, TILE = 32 * D, STAGE = kv_stage<D>();
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -405,7 +403,7 @@ __device__ __forceinline__ void flash_bwd_kv(const FlashArgs& a, int kblk, int z
     if (key_ok) {
       const int64_t o = (int64_t)key * a.ldq + 16 * ks + 8 * h;
       kh[ks] = *reinterpret_cast<const bf16x8*>(qkv + o + ck);
-      kl[ks] = *reinterpret_cast<const bf16x8*>(qlo + o + ck);
+      if constexpr (COMP) kl[ks] = *reinterpret_cast<const bf16x8*>(qlo + o + ck);
       vv[ks] = *reinterpret_cast<const bf16x8*>(qkv + o + cv);
     } else {
 #pragma unroll
@@ -413,7 +411,7 @@ __device__ __forceinline__ void flash_bwd_kv(const FlashArgs& a, int kblk, int z
     }
   }
   const __amdgpu_buffer_rsrc_t rq = seq_rsrc(qkv + cq, a.ldq, a.seq);
-  const __amdgpu_buffer_rsrc_t rql = seq_rsrc(qlo + cq, a.ldq, a.seq);
+  const __amdgpu_buffer_rsrc_t rql = seq_rsrc(COMP ? qlo + cq : qkv + cq, a.ldq, a.seq);
   const __amdgpu_buffer_rsrc_t rdo = seq_rsrc(dO, a.ldc, a.seq);
   // L and D rows of this (sequence, head): seq floats each; reads past them return 0.
   const __amdgpu_buffer_rsrc_t rl =
@@ -431,11 +429,15 @@ __device__ __forceinline__ void flash_bwd_kv(const FlashArgs& a, int kblk, int z
   auto issue = [&](int t) {
     bf16* st = smem + (t % kStages) * STAGE;
     const uint32_t r0 = (uint32_t)((qb0 + t) * 32);
-    dma_tile_dual(st, rq, oq.off, r0 * (uint32_t)a.ldq * 2u, wave);
-    dma_tile_dual(st + TILE, rql, oq.off, r0 * (uint32_t)a.ldq * 2u, wave);
-    dma_tile_dual(st + 2 * TILE, rdo, oo.off, r0 * (uint32_t)a.ldc * 2u, wave);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(wave == 0 ? rl : rd, (lds_ptr_t)(st + 3 * TILE + wave * 512), 16,
-                                             lane_ld + r0 * 4u, 0, 0, 0);
+    const uint32_t rbq = r0 * (uint32_t)a.ldq * 2u, rbo = r0 * (uint32_t)a.ldc * 2u;
+#pragma unroll
+    for (int i = 0; i < DualOffsets<D>::PER; ++i) {  // Q_hi, Q_lo and dO tiles of query block qb0 + t
+      const int q = (wave + i * 2) * 512;
+      lds_dma16(rq, st + q, oq.off[i] + rbq);
+      if (COMP) lds_dma16(rql, st + TILE + q, oq.off[i] + rbq);
+      lds_dma16(rdo, st + 2 * TILE + q, oo.off[i] + rbo);
+    }
+    lds_dma16(wave == 0 ? rl : rd, st + 3 * TILE + wave * 512, lane_ld + r0 * 4u);
   };
 
   const float scale2 = a.scale * kLog2e;
@@ -446,7 +448,7 @@ __device__ __forceinline__ void flash_bwd_kv(const FlashArgs& a, int kblk, int z
     for (int r = 0; r < 16; ++r) dv[nb][r] = dk[nb][r] = 0.f;
 
   // Per wave: 3 tiles of 32 D / 512 DMA instructions over 2 waves, plus one for L or D.
-  constexpr int LOADS = 3 * DualOffsets<D>::PER + 1;
+  constexpr int LOADS = (COMP ? 3 : 2) * DualOffsets<D>::PER + 1;
   if (nsteps > 0) issue(0);
   if (nsteps > 1) issue(1);
   for (int t = 0; t < nsteps; ++t) {
@@ -480,11 +482,14 @@ __device__ __forceinline__ void flash_bwd_kv(const FlashArgs& a, int kblk, int z
     for (int r = 0; r < 16; ++r) st[r] = dpt[r] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 qf = row_frag<D>(sQ, r32, ks, h), qfl = row_frag<D>(sQl, r32, ks, h), of = row_frag<D>(sO, r32, ks, h);
+      const bf16x8 qf = row_frag<D>(sQ, r32, ks, h), of = row_frag<D>(sO, r32, ks, h);
       st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, kh[ks], st, 0, 0, 0);
       dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(of, vv[ks], dpt, 0, 0, 0);
-      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, kl[ks], st, 0, 0, 0);
-      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qfl, kh[ks], st, 0, 0, 0);
+      if constexpr (COMP) {
+        const bf16x8 qfl = row_frag<D>(sQl, r32, ks, h);
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, kl[ks], st, 0, 0, 0);
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qfl, kh[ks], st, 0, 0, 0);
+      }
     }
     float p[16], ds[16];
 #pragma unroll
@@ -518,7 +523,7 @@ __device__ __forceinline__ void flash_bwd_kv(const FlashArgs& a, int kblk, int z
 // dQ. Work-group: 64 query rows of sequence b, head k; streams the key blocks (32 keys)
 // they see. Lane l owns query row (l & 31).
 //   P = exp(S / sqrt(d) - L), dS = P * (dO V^T - D), dQ += dS K / sqrt(d).
-template <int D>
+template <int D, bool COMP>
 __device__ __forceinline__ void flash_bwd_q(const FlashArgs& a, int qb, int z, bf16* smem) {
   constexpr int KS = D / 16, NB = D / 32, TILE = 32 * D;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -541,7 +546,7 @@ __device__ __forceinline__ void flash_bwd_q(const FlashArgs& a, int qb, int z, b
     if (row_ok) {
       const int64_t o = (int64_t)row * a.ldq + 16 * ks + 8 * h;
       qh[ks] = *reinterpret_cast<const bf16x8*>(qkv + o + cq);
-      ql[ks] = *reinterpret_cast<const bf16x8*>(qlo + o + cq);
+      if constexpr (COMP) ql[ks] = *reinterpret_cast<const bf16x8*>(qlo + o + cq);
       of[ks] = *reinterpret_cast<const bf16x8*>(dO + (int64_t)row * a.ldc + 16 * ks + 8 * h);
     } else {
 #pragma unroll
@@ -549,7 +554,7 @@ __device__ __forceinline__ void flash_bwd_q(const FlashArgs& a, int qb, int z, b
     }
   }
   const __amdgpu_buffer_rsrc_t rk = seq_rsrc(qkv + ck, a.ldq, a.seq);
-  const __amdgpu_buffer_rsrc_t rkl = seq_rsrc(qlo + ck, a.ldq, a.seq);
+  const __amdgpu_buffer_rsrc_t rkl = seq_rsrc(COMP ? qlo + ck : qkv + ck, a.ldq, a.seq);
   const __amdgpu_buffer_rsrc_t rv = seq_rsrc(qkv + cv, a.ldq, a.seq);
   const int kend = min(a.seq, (qb + 1) * kFlashRows);
   const int nsteps = (kend + 31) / 32;
@@ -562,9 +567,9 @@ __device__ __forceinline__ void flash_bwd_q(const FlashArgs& a, int qb, int z, b
     for (int i = 0; i < DualOffsets<D>::PER; ++i) {  // K_hi, K_lo and V tiles of key block t
       const int q = (wave + i * 2) * 512;
       const uint32_t off = koff.off[i] + rb;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(st + q), 16, off, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rkl, (lds_ptr_t)(st + TILE + q), 16, off, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(st + 2 * TILE + q), 16, off, 0, 0, 0);
+      lds_dma16(rk, st + q, off);
+      if (COMP) lds_dma16(rkl, st + TILE + q, off);
+      lds_dma16(rv, st + 2 * TILE + q, off);
     }
   };
 
@@ -575,7 +580,7 @@ __device__ __forceinline__ void flash_bwd_q(const FlashArgs& a, int qb, int z, b
 #pragma unroll
     for (int r = 0; r < 16; ++r) dq[nb][r] = 0.f;
 
-  constexpr int LOADS = 3 * DualOffsets<D>::PER;  // per wave: 3 tiles, over 2 waves
+  constexpr int LOADS = (COMP ? 3 : 2) * DualOffsets<D>::PER;  // per wave: 3 tiles (2), over 2 waves
   issue(0);
   if (nsteps > 1) issue(1);
   for (int t = 0; t < nsteps; ++t) {
@@ -595,11 +600,14 @@ __device__ __forceinline__ void flash_bwd_q(const FlashArgs& a, int qb, int z, b
     for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 kf = row_frag<D>(sK, r32, ks, h), kfl = row_frag<D>(sKl, r32, ks, h), vf = row_frag<D>(sV, r32, ks, h);
+      const bf16x8 kf = row_frag<D>(sK, r32, ks, h), vf = row_frag<D>(sV, r32, ks, h);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qh[ks], s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, of[ks], dp, 0, 0, 0);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfl, qh[ks], s, 0, 0, 0);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, ql[ks], s, 0, 0, 0);
+      if constexpr (COMP) {
+        const bf16x8 kfl = row_frag<D>(sKl, r32, ks, h);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfl, qh[ks], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, ql[ks], s, 0, 0, 0);
+      }
     }
     float ds[16];
 #pragma unroll
@@ -625,7 +633,7 @@ __device__ __forceinline__ void flash_bwd_q(const FlashArgs& a, int qb, int z, b
 // Both backward parts in one grid, each walking its deepest blocks first: blockIdx.x
 // interleaves them (even: key block x / 2 of dK, dV; odd: row block of dQ, deepest
 // first), so the grid's critical path is the longer of the two chains, not their sum.
-template <int D>
+template <int D, bool COMP>
 __global__ __launch_bounds__(128) void flash_bwd_kernel(FlashArgs a) {
   constexpr int SMEM = kStages * (kv_stage<D>() > q_stage<D>() ? kv_stage<D>() : q_stage<D>());
   __shared__ __attribute__((aligned(1024))) bf16 smem[SMEM];
@@ -634,9 +642,9 @@ __global__ __launch_bounds__(128) void flash_bwd_kernel(FlashArgs a) {
   xcd_block((int)gridDim.x, z, x);
   const int nqb = (a.seq + kFlashRows - 1) / kFlashRows, nkb = (a.seq + 63) / 64;
   if ((x & 1) == 0) {
-    if (x / 2 < nkb) flash_bwd_kv<D>(a, x / 2, z, smem);
+    if (x / 2 < nkb) flash_bwd_kv<D, COMP>(a, x / 2, z, smem);
   } else {
-    if (x / 2 < nqb) flash_bwd_q<D>(a, nqb - 1 - x / 2, z, smem);
+    if (x / 2 < nqb) flash_bwd_q<D, COMP>(a, nqb - 1 - x / 2, z, smem);
   }
 }
 
@@ -655,8 +663,12 @@ hipError_t launch_flash_bwd(const FlashArgs& a, int d, hipStream_t s) {
   if (!flash_extents_ok(a)) return hipErrorInvalidValue;
   const int nqb = (a.seq + kFlashRows - 1) / kFlashRows, nkb = (a.seq + 63) / 64;
   const int n = 2 * (nqb > nkb ? nqb : nkb);
-  if (d == 128) hipLaunchKernelGGL(flash_bwd_kernel<128>, dim3(n, a.batch * a.heads), dim3(128), 0, s, a);
-  else if (d == 64) hipLaunchKernelGGL(flash_bwd_kernel<64>, dim3(n, a.batch * a.heads), dim3(128), 0, s, a);
+  const dim3 grid(n, a.batch * a.heads);
+  const bool comp = a.qkv_lo != nullptr;
+  if (d == 128 && comp) hipLaunchKernelGGL((flash_bwd_kernel<128, true>), grid, dim3(128), 0, s, a);
+  else if (d == 128) hipLaunchKernelGGL((flash_bwd_kernel<128, false>), grid, dim3(128), 0, s, a);
+  else if (d == 64 && comp) hipLaunchKernelGGL((flash_bwd_kernel<64, true>), grid, dim3(128), 0, s, a);
+  else if (d == 64) hipLaunchKernelGGL((flash_bwd_kernel<64, false>), grid, dim3(128), 0, s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
@@ -665,8 +677,11 @@ hipError_t launch_flash_fwd(const FlashArgs& a, int d, hipStream_t s) {
   if (a.seq <= 0 || a.batch <= 0 || a.heads <= 0) return hipSuccess;
   if (!flash_extents_ok(a)) return hipErrorInvalidValue;
   const dim3 grid((a.seq + kFlashRows - 1) / kFlashRows, a.batch * a.heads);
-  if (d == 128) hipLaunchKernelGGL(flash_fwd_kernel<128>, grid, dim3(256), 0, s, a);
-  else if (d == 64) hipLaunchKernelGGL(flash_fwd_kernel<64>, grid, dim3(256), 0, s, a);
+  const bool comp = a.qkv_lo != nullptr;
+  if (d == 128 && comp) hipLaunchKernelGGL((flash_fwd_kernel<128, true>), grid, dim3(256), 0, s, a);
+  else if (d == 128) hipLaunchKernelGGL((flash_fwd_kernel<128, false>), grid, dim3(256), 0, s, a);
+  else if (d == 64 && comp) hipLaunchKernelGGL((flash_fwd_kernel<64, true>), grid, dim3(256), 0, s, a);
+  else if (d == 64) hipLaunchKernelGGL((flash_fwd_kernel<64, false>), grid, dim3(256), 0, s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

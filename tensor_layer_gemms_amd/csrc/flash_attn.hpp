@@ -3,8 +3,8 @@
 // Forward: a work-group owns 64 query rows of one (sequence, head); two pairs of waves
 // stream the two halves of the visible keys in blocks of 32 through their own LDS rings
 // (DMA loads, three stages) and merge their partial results at the end. Per block the
-// logits S = (Q_hi K_hi^T + Q_hi K_lo^T + Q_lo K_hi^T) / sqrt(d) are formed on the matrix
-// cores, the causal mask is applied, the running row maximum and exponential sum are
+// logits S = Q K^T / sqrt(d) — with qkv_lo given, in the compensated form
+// (Q_hi K_hi^T + Q_hi K_lo^T + Q_lo K_hi^T) / sqrt(d) — are formed on the matrix cores, the causal mask is applied, the running row maximum and exponential sum are
 // updated (online softmax) and O += P V is accumulated with P taken straight from the
 // logit accumulators (rounded to bf16 as the matrix-core operand). S and P never reach
 // HBM. The forward writes ctx = O / l and the row log-sum-exp L = m + ln(l), from which
@@ -22,7 +22,7 @@ namespace mt {
 
 struct FlashArgs {
   const void* qkv;     // [B seq, ldq] bf16: Q of head k at column k d, K at hs + k d, V at 2 hs + k d
-  const void* qkv_lo;  // same layout: rounding remainders of Q and K
+  const void* qkv_lo;  // same layout: rounding remainders of Q and K, or null (plain Q K^T)
   void* ctx;           // [B seq, ldc] bf16: head k at column k d
   float* lse;          // [B, heads, seq] fp32 natural-log row log-sum-exp
   const void* dctx;    // backward: dL/dctx, layout of ctx

@@ -26,6 +26,7 @@ constexpr float kLnEps = 1e-5f;  // LayerNorm epsilon (silent on the pages; comm
 struct Dims {
   int64_t M, h, heads, at, d, seq, B, tp, hs, qkv, ft;
   bool bf16;
+  bool comp;   // MT_BF16_QK: Q and K as hi + lo pairs in the logits
   bool flash;  // fused attention kernels (bf16 path, head dims they support)
   int64_t es;  // bytes per activation element
 };
@@ -34,7 +35,7 @@ int validate_shape(const mt_shape* s, Dims* out) {
   if (!s) return MT_ERR_INVALID_ARG;
   if (s->h <= 0 || s->heads <= 0 || s->seq <= 0 || s->micro_batch <= 0 || s->tp <= 0) return MT_ERR_INVALID_ARG;
   if (s->shard < 0 || s->shard >= s->tp) return MT_ERR_INVALID_ARG;
-  if (s->dtype != MT_BF16 && s->dtype != MT_FP32) return MT_ERR_INVALID_ARG;
+  if (s->dtype != MT_BF16 && s->dtype != MT_FP32 && s->dtype != MT_BF16_QK) return MT_ERR_INVALID_ARG;
   if (s->h % s->heads != 0 || s->heads % s->tp != 0) return MT_ERR_INVALID_ARG;
   const int64_t d = s->h / s->heads;
   if (d % 8 != 0 || s->seq % 8 != 0) return MT_ERR_UNSUPPORTED;
@@ -54,7 +55,8 @@ int validate_shape(const mt_shape* s, Dims* out) {
   x.hs = x.at * d;
   x.qkv = 3 * x.hs;
   x.ft = 4 * x.h / x.tp;
-  x.bf16 = s->dtype == MT_BF16;
+  x.bf16 = s->dtype != MT_FP32;
+  x.comp = s->dtype == MT_BF16_QK;
   x.flash = x.bf16 && flash_supported((int)d);
   x.es = x.bf16 ? 2 : 4;
   *out = x;
@@ -82,7 +84,8 @@ struct LayerSaved {
   float *mean1, *rstd1, *mean2, *rstd2;
   float* x2;  // residual stream X + O + b_o, fp32
   void *u, *qkv, *p, *ctx, *v2, *a, *z;
-  // fused attention (instead of P): row log-sum-exp [B, a_t, s] and the Q, K remainders
+  // fused attention (instead of P): row log-sum-exp [B, a_t, s] and (MT_BF16_QK) the
+  // Q, K remainders
   float* lse;
   void* qkv_lo;
 };
@@ -97,7 +100,7 @@ size_t carve_layer_saved(const Dims& d, void* base, LayerSaved* s) {
   s->qkv = c.take(d.M * d.qkv * d.es);
   s->p = d.flash ? nullptr : c.take(d.B * d.at * d.seq * d.seq * d.es);
   s->lse = d.flash ? c.take<float>(d.B * d.at * d.seq * 4) : nullptr;
-  s->qkv_lo = d.flash ? c.take(d.M * d.qkv * 2) : nullptr;
+  s->qkv_lo = d.flash && d.comp ? c.take(d.M * d.qkv * 2) : nullptr;
   s->ctx = c.take(d.M * d.hs * d.es);
   s->x2 = c.take<float>(d.M * d.h * 4);
   s->v2 = c.take(d.M * d.h * d.es);
@@ -107,20 +110,20 @@ size_t carve_layer_saved(const Dims& d, void* base, LayerSaved* s) {
 }
 
 struct LayerFwdWs {
-  float* S;      // scores; before them (bf16 path) the fp32 partials of the QKV projection
+  float* S;      // scores; before them (MT_BF16_QK) the fp32 partials of the QKV projection
   void* o;       // out-projection partial, then FC2 partial
-  void* u_lo;    // bf16 path: rounding remainder of U
-  void* qkv_lo;  // bf16 path: rounding remainders of Q and K, in the QKV layout
+  void* u_lo;    // MT_BF16_QK: rounding remainder of U
+  void* qkv_lo;  // MT_BF16_QK, unfused attention: rounding remainders of Q and K (QKV layout)
 };
 
 size_t carve_layer_fwd_ws(const Dims& d, void* base, LayerFwdWs* w) {
   Carver c(base);
-  const int64_t qkv_partials = d.bf16 ? d.M * (d.qkv + 2 * d.hs) : 0;
+  const int64_t qkv_partials = d.comp ? d.M * (d.qkv + 2 * d.hs) : 0;
   const int64_t scores = d.flash ? 0 : d.B * d.at * d.seq * d.seq;
   w->S = c.take<float>(std::max<int64_t>(scores, qkv_partials) * 4);
   w->o = c.take(d.M * d.h * d.es);
-  w->u_lo = d.bf16 ? c.take(d.M * d.h * 2) : nullptr;
-  w->qkv_lo = d.bf16 && !d.flash ? c.take(d.M * d.qkv * 2) : nullptr;  // saved with fused attention
+  w->u_lo = d.comp ? c.take(d.M * d.h * 2) : nullptr;
+  w->qkv_lo = d.comp && !d.flash ? c.take(d.M * d.qkv * 2) : nullptr;  // saved with fused attention
   return c.off;
 }
 
@@ -330,20 +333,21 @@ int layer_fwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, void
   const float scale = 1.0f / std::sqrt((float)d.d);
   const int batch = (int)(d.B * d.at);
   Attn at{d};
-  void* qkv_lo = d.flash ? sv.qkv_lo : ws.qkv_lo;  // Q, K remainders (kept for the backward when fused)
+  // Q, K remainders (MT_BF16_QK; kept for the backward when fused), else null
+  void* qkv_lo = d.flash ? sv.qkv_lo : ws.qkv_lo;
 
-  // F1 LayerNorm 1 (bf16 path: also the rounding remainder U_lo of U)
-  q.run("ln1_fwd", 0, Mh * es * (bf ? 3 : 2), [&] {
+  // F1 LayerNorm 1 (MT_BF16_QK: also the rounding remainder U_lo of U)
+  q.run("ln1_fwd", 0, Mh * es * (d.comp ? 3 : 2), [&] {
     return launch_ln_fwd(bf, x, w.ln1_g, w.ln1_b, sv.u, ws.u_lo, sv.mean1, sv.rstd1, (int)d.M, (int)d.h, kLnEps,
                          stream);
   });
-  // F2 column-parallel QKV projection + bias. bf16 path: the Q and K columns are formed
+  // F2 column-parallel QKV projection + bias. MT_BF16_QK: the Q and K columns are formed
   // from U_hi + U_lo (a second K segment) and stored as hi + lo bf16 pairs, so the
   // softmax logits, whose sharp maxima amplify input rounding, see Q and K to ~16 bits.
-  q.run("qkv_fwd", gflop(d.M, d.qkv, d.h) + (bf ? gflop(d.M, 2 * d.hs, d.h) : 0), 0, [&] {
+  q.run("qkv_fwd", gflop(d.M, d.qkv, d.h) + (d.comp ? gflop(d.M, 2 * d.hs, d.h) : 0), 0, [&] {
     GemmArgs g = plain(sv.u, d.h, w.w_qkv, d.h, sv.qkv, d.qkv, d.M, d.qkv, d.h);
     g.vec = w.b_qkv;
-    if (!bf) return gemm(d, g, true, true, EPI_BIAS, 1, stream);
+    if (!d.comp) return gemm(d, g, true, true, EPI_BIAS, 1, stream);
     // The Q and K columns take U_hi W^T + U_lo W^T, twice the contraction of the V
     // columns. The two products run as equal-depth problems of one launch into fp32
     // partials (which fills the CUs evenly), and a pass adds them and the bias and
@@ -374,12 +378,12 @@ int layer_fwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, void
       return launch_flash_fwd(fa, (int)d.d, stream);
     });
   } else {
-    // F3 scores S = Q K^T / sqrt(d), causal tiles only, fp32 (bf16 path:
+    // F3 scores S = Q K^T / sqrt(d), causal tiles only, fp32 (MT_BF16_QK:
     // Q_hi K_hi^T + Q_hi K_lo^T + Q_lo K_hi^T)
-    q.run("attn_scores", at.flops() * (bf ? 3 : 1), 0, [&] {
+    q.run("attn_scores", at.flops() * (d.comp ? 3 : 1), 0, [&] {
       GemmArgs g = plain(sv.qkv, d.qkv, static_cast<const char*>(sv.qkv) + d.hs * d.es, d.qkv, ws.S, d.seq, d.seq,
                          d.seq, d.d);
-      if (bf) {
+      if (d.comp) {
         const char* lo = static_cast<const char*>(qkv_lo);
         g.seg_a[1] = sv.qkv;
         g.seg_b[1] = lo + d.hs * d.es;

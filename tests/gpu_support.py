@@ -47,7 +47,8 @@ def to_np(t) -> np.ndarray:
 
 
 def mt_shape(shape: si.LayerShape):
-    return mt_mod().make_shape(shape.h, shape.heads, shape.seq, shape.micro_batch, shape.tp, shape.shard, shape.dtype)
+    dtype = "bf16qk" if shape.qk_pairs else shape.dtype
+    return mt_mod().make_shape(shape.h, shape.heads, shape.seq, shape.micro_batch, shape.tp, shape.shard, dtype)
 
 
 def log(msg: str) -> None:
@@ -118,6 +119,11 @@ def run_mlp_gpu(shape: si.LayerShape, x: np.ndarray, dy: np.ndarray, p: Dict[str
     mt.mlp_bwd(sh, xd, w1, w2, saved, dyd, dx, dw1, db1, dw2, ws)
     torch.cuda.synchronize()
     return to_np(y), to_np(dx), dict(w_fc1=to_np(dw1), b_fc1=to_np(db1), w_fc2=to_np(dw2))
+
+
+def rel_rms(gpu: np.ndarray, ref: np.ndarray) -> float:
+    """RMS(gpu - ref) / RMS(ref)."""
+    return float(np.sqrt(np.mean((gpu - ref) ** 2)) / max(np.sqrt(np.mean(ref * ref)), 1e-30))
 
 
 def compare(name: str, gpu: np.ndarray, ref: np.ndarray, tol: float, normwise: bool = False,

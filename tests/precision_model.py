@@ -2,9 +2,10 @@
 
 The layer is computed with the oracle's formulas in fp64, except that every tensor the
 HIP path stores in bf16 between kernels is rounded to bf16 at the same point. With no
-rounding enabled the model IS the oracle; with the HIP path's set (ROUNDED) it
-predicts the HIP path's error against the oracle (it reproduced the measured GPU
-errors of the 175B shard to three digits). Switching single rounding points on or off
+rounding enabled the model IS the oracle; with the rounding set of one of the HIP
+path's bf16 modes (BF16 for MT_BF16, BF16_QK for MT_BF16_QK) it predicts that mode's
+error against the oracle (the BF16_QK set reproduced the measured GPU errors of the
+175B shard to three digits). Switching single rounding points on or off
 shows which of them drive which error, and which tolerance readings a bf16 path can
 meet at all.
 
@@ -23,14 +24,14 @@ import numpy as np
 import seeded_inputs as si
 from oracle.layer import gelu, gelu_grad, layernorm_bwd, layernorm_fwd
 
-# Rounding points of the bf16 HIP path. The residual stream X2 and its gradient dX2 are
-# fp32. U enters the QKV GEMM as U_hi + U_lo and Q, K enter the score GEMM as hi + lo
-# pairs, so neither is rounded there ("u_qkv", "qk_fwd" absent); the backward uses the
-# single bf16 U, Q, K ("u", "qk") and V is bf16 throughout ("v").
-ROUNDED = frozenset({"u", "qk", "v", "p", "ctx", "o", "v2", "a", "z", "y", "out",
+# Rounding points of the HIP path's MT_BF16_QK mode. The residual stream X2 and its
+# gradient dX2 are fp32. U enters the QKV GEMM as U_hi + U_lo and Q, K enter the score
+# products as hi + lo pairs, so neither is rounded there ("u_qkv", "qk_fwd" absent); the
+# backward uses the single bf16 U, Q, K ("u", "qk") and V is bf16 throughout ("v").
+BF16_QK = frozenset({"u", "qk", "v", "p", "ctx", "o", "v2", "a", "z", "y", "out",
                      "da", "dv2", "dx2_operand", "dctx", "ds", "dqkv", "du", "dx"})
-# A plain bf16 path: U rounded before the QKV GEMM and Q, K rounded before the scores.
-PLAIN_BF16 = ROUNDED | {"u_qkv", "qk_fwd"}
+# MT_BF16: U rounded before the QKV GEMM and Q, K rounded before the scores.
+BF16 = BF16_QK | {"u_qkv", "qk_fwd"}
 
 
 def _rb(a) -> np.ndarray:
@@ -128,6 +129,6 @@ if __name__ == "__main__":
     name = sys.argv[1] if len(sys.argv) > 1 else "gpt_h1024"
     case = si.workload_case(name)
     ref = layer(case, ())
-    _print("bf16 HIP path rounding set", metrics(layer(case, ROUNDED), ref))
-    _print("plain bf16 path (U and Q, K rounded before their products)", metrics(layer(case, PLAIN_BF16), ref))
+    _print("MT_BF16 (U and Q, K rounded before their products)", metrics(layer(case, BF16), ref))
+    _print("MT_BF16_QK (hi + lo U and Q, K in the logits)", metrics(layer(case, BF16_QK), ref))
     _print("only the QKV-GEMM operand U rounded", metrics(layer(case, {"u_qkv"}), ref))

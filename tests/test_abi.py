@@ -40,6 +40,8 @@ def test_exports_every_declared_symbol(lib):
 def _shape(**kw):
     base = dict(h=1024, heads=16, seq=1024, micro_batch=4, tp=1, shard=0, dtype="bf16")
     base.update(kw)
+    if isinstance(base["dtype"], int):  # a raw mt_dtype value, past the binding's check
+        return mt.Shape(*(base[k] for k in ("h", "heads", "seq", "micro_batch", "tp", "shard", "dtype")))
     return mt.make_shape(**base)
 
 
@@ -47,11 +49,17 @@ def test_buffer_queries_consistent(lib):
     s = _shape()  # head dim 64: fused attention
     M, h, f, a, seq, B = 4096, 1024, 4096, 16, 1024, 4
     saved = mt.layer_saved_bytes(s)
-    # U, QKV, the Q/K rounding remainders (QKV layout), ctx, V2, A, Z in bf16, the fp32
-    # residual X2, four fp32 row statistics and the fp32 row log-sum-exp (no P)
-    need = 2 * (M * h + 2 * M * 3 * h + M * h + M * h + 2 * M * f) + 4 * M * h + 16 * M + 4 * B * a * seq
+    # U, QKV, ctx, V2, A, Z in bf16, the fp32 residual X2, four fp32 row statistics and
+    # the fp32 row log-sum-exp (no P)
+    need = 2 * (M * h + M * 3 * h + M * h + M * h + 2 * M * f) + 4 * M * h + 16 * M + 4 * B * a * seq
     assert need <= saved <= need + 64 * 256
-    assert mt.layer_workspace_bytes(s) >= 4 * M * (3 * h + 2 * h)  # fp32 QKV partials
+    # MT_BF16_QK also saves the Q/K rounding remainders (QKV layout) and needs the fp32
+    # partials of the two QKV products and U's remainder in the workspace
+    sq = _shape(dtype="bf16qk")
+    need_q = need + 2 * M * 3 * h
+    assert need_q <= mt.layer_saved_bytes(sq) <= need_q + 64 * 256
+    assert mt.layer_workspace_bytes(sq) >= 4 * M * (3 * h + 2 * h) + 2 * M * h
+    assert mt.layer_workspace_bytes(s) <= mt.layer_workspace_bytes(sq)
     # head dim 160 keeps the materialised attention: P (bf16) in the saved store, fp32
     # scores in the workspace
     s160 = _shape(h=640, heads=4, seq=256, micro_batch=2)
@@ -76,6 +84,7 @@ def test_buffer_queries_consistent(lib):
     (dict(h=1028, heads=257), mt.MT_ERR_UNSUPPORTED),   # head dim 4
     (dict(h=65536, heads=512), mt.MT_ERR_UNSUPPORTED),  # LayerNorm row limit
     (dict(micro_batch=0), mt.MT_ERR_INVALID_ARG),
+    (dict(dtype=3), mt.MT_ERR_INVALID_ARG),             # no such mt_dtype
 ])
 def test_bad_shapes_rejected(lib, kw, status):
     s = _shape(**kw)

@@ -1,9 +1,10 @@
 """CPU checks of the bf16 rounding model used to choose the bf16 tolerance reading."""
 import numpy as np
+import pytest
 
 import oracle
 import seeded_inputs as si
-from precision_model import PLAIN_BF16, ROUNDED, layer, metrics
+from precision_model import BF16, BF16_QK, layer, metrics
 
 
 def _case():
@@ -22,9 +23,10 @@ def test_model_without_rounding_is_the_oracle():
         assert np.allclose(g[k], r_g[0][k], rtol=1e-10, atol=1e-10), k
 
 
-def test_bf16_rounding_stays_within_normwise_bar():
+@pytest.mark.parametrize("mode", ["bf16", "bf16qk"])
+def test_bf16_rounding_stays_within_normwise_bar(mode):
     case = _case()
-    m = metrics(layer(case, ROUNDED), layer(case, ()))
+    m = metrics(layer(case, BF16 if mode == "bf16" else BF16_QK), layer(case, ()))
     for k, (rms_rel, _, max_rel) in m.items():
         assert rms_rel < 2e-2 and max_rel < 2e-2, (k, m[k])
     assert max(v[0] for v in m.values()) > 1e-4  # the roundings are really applied
@@ -34,5 +36,5 @@ def test_compensated_qk_is_more_accurate_than_plain_bf16():
     """The hi/lo treatment of U and Q, K lowers the error of the attention gradients."""
     case = _case()
     ref = layer(case, ())
-    ours, plain = metrics(layer(case, ROUNDED), ref), metrics(layer(case, PLAIN_BF16), ref)
+    ours, plain = metrics(layer(case, BF16_QK), ref), metrics(layer(case, BF16), ref)
     assert ours["w_qkv"][0] < plain["w_qkv"][0] and ours["dx"][0] < plain["dx"][0]
