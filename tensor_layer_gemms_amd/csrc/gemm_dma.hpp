@@ -324,7 +324,6 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs& g, int bid, int z,
     for (int t = 0; t < nk; ++t) {
       wait_vmcnt<0>();
       dma_barrier();
-      if (t + 1 < nk) issue(t + 1);
       const bf16* sA = smem + (t & 1) * STAGE;
       const bf16* sB = sA + BM * BK;
       bf16x8 af[2][TM], bfr[2][TN];
@@ -332,6 +331,7 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs& g, int bid, int z,
       for (int i = 0; i < TM; ++i) af[0][i] = ra[i].read(sA, 0, lane);
 #pragma unroll
       for (int j = 0; j < TN; ++j) bfr[0][j] = rb[j].read(sB, 0, lane);
+      if (t + 1 < nk) issue(t + 1);  // after the first reads, which then fly under the issue
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int cb = ks & 1, nb = cb ^ 1;
@@ -346,6 +346,17 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs& g, int bid, int z,
 #pragma unroll
           for (int j = 0; j < TN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cb][j], af[cb][i], acc[i][j], 0, 0, 0);
+        if (ks + 1 < KS) {
+          // The next slice's LDS reads go out spread over this slice's first MFMAs.
+          constexpr int NM = TM * TN, NR = TM * (A_K ? 1 : 2) + TN * (B_K ? 1 : 2);
+          constexpr int q = NR / NM, r = NR % NM;
+#pragma unroll
+          for (int j = 0; j < NM; ++j) {
+            if (j < r) __builtin_amdgcn_sched_group_barrier(0x100, q + 1, 0);
+            else if constexpr (q > 0) __builtin_amdgcn_sched_group_barrier(0x100, q > 0 ? q : 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          }
+        }
       }
     }
   }
