@@ -14,7 +14,10 @@ f(X A_i) B_i equals f(X A) B) forward and backward; brute-force per-element
 attention loops; closed forms of LayerNorm, GeLU, the causal first query, a zero
 query projection and a zeroed residual branch; and torch's fp64 CPU functional ops
 with autograd as an independent library cross-check. adamw_step (oracle/adamw.py) is
-pinned in tests/test_oracle_adamw.py. No function is parity unpinned.
+pinned in tests/test_oracle_adamw.py. The sequence-parallel share
+(oracle/sequence_parallel.py) is pinned in tests/test_oracle_sp.py against the
+tensor-parallel layer, whose function it must reproduce exactly. No function is parity
+unpinned.
 """
 from .adamw import adamw_step  # noqa: F401
 from .layer import (  # noqa: F401
@@ -31,4 +34,13 @@ from .layer import (  # noqa: F401
     mlp_fwd,
     stage_bwd,
     stage_fwd,
+)
+from .sequence_parallel import (  # noqa: F401
+    all_gather_seq,
+    attn_block_bwd,
+    attn_block_fwd,
+    reduce_scatter_seq,
+    seq_rows,
+    sp_layer_bwd,
+    sp_layer_fwd,
 )
