@@ -70,6 +70,7 @@ def parse():
                     help="label of the kernel launch whose roofline is reported")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-optimizer", action="store_true", help="skip the fused AdamW step measurement")
+    ap.add_argument("--no-sp", action="store_true", help="skip the sequence-parallel share measurement")
     ap.add_argument("--qk-pairs", action="store_true",
                     help="run the MT_BF16_QK mode (attention logits from hi + lo pairs of Q and K)")
     ap.add_argument("--breakdown", action="store_true", help="also print a per-launch time breakdown (stderr)")
@@ -153,6 +154,75 @@ def optimizer_step(mt, si, torch, shape, stream, warmup: int = 2, iters: int = 1
     return {"kernel": "adamw", "params": n, "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
             "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "avg_ms": round(avg_ms, 4),
             "launches": len(recs), "bytes_per_launch": int(nbytes)}
+
+
+def sp_share(mt, si, torch, shape, w, x, dout, stream, warmup: int = 3, iters: int = 10):
+    """One rank's sequence-parallel share of the same layer step (shard 0 of the group):
+    LayerNorm, bias + residual on the rank's seq/tp rows, the attention and MLP blocks on
+    the gathered rows. The collectives are not part of one GPU's work: each gathered
+    buffer holds this rank's rows (written by its own calls) and synthetic rows standing
+    for the other ranks; the rank's reduce-scattered rows are its own partial's rows (the
+    one-GPU stand-in, as the identity is for the all-reduce). Micro-batch 1, so the
+    rank's rows are the first seq/tp rows and every slot is a pointer offset."""
+    if shape.micro_batch != 1 or shape.seq % shape.tp or shape.dtype != "bf16" or shape.qk_pairs:
+        return None
+    print("[bench] sequence-parallel share of the step (rank 0)", file=sys.stderr, flush=True)
+    sh = mt.make_shape(shape.h, shape.heads, shape.seq, shape.micro_batch, shape.tp, shape.shard, "bf16")
+    M, h = shape.tokens, shape.h
+    n = M // shape.tp
+    act = torch.bfloat16
+    f32 = dict(dtype=torch.float32, device="cuda")
+    U, V2, dOut, dX2 = (torch.randn(M, h, device="cuda").to(act) for _ in range(4))
+    O, Y, dV2, dU = (torch.empty(M, h, dtype=act, device="cuda") for _ in range(4))
+    xi, douti = x[:n], dout[:n]
+    x2, dx2f = torch.empty(n, h, **f32), torch.empty(n, h, **f32)
+    out_i, dx_i = torch.empty(n, h, dtype=act, device="cuda"), torch.empty(n, h, dtype=act, device="cuda")
+    st = [torch.empty(n, **f32) for _ in range(4)]
+    g = {k: torch.empty(v.shape, **f32) for k, v in w.items()}
+    asv = torch.empty(mt.attn_saved_bytes(sh), dtype=torch.uint8, device="cuda")
+    msv = torch.empty(mt.mlp_saved_bytes(sh), dtype=torch.uint8, device="cuda")
+    aws = torch.empty(mt.attn_workspace_bytes(sh), dtype=torch.uint8, device="cuda")
+    mws = torch.empty(mt.mlp_workspace_bytes(sh), dtype=torch.uint8, device="cuda")
+    lws = torch.empty(mt.sp_ln_workspace_bytes(sh), dtype=torch.uint8, device="cuda")
+    dOut[:n] = douti
+
+    def step():
+        mt.sp_ln_fwd(sh, xi, w["ln1_g"], w["ln1_b"], U[:n], st[0], st[1], stream=stream)
+        mt.attn_fwd(sh, U, w["w_qkv"], w["b_qkv"], w["w_o"], O, asv, aws, stream)
+        mt.sp_ln_fwd(sh, xi, w["ln2_g"], w["ln2_b"], V2[:n], st[2], st[3], resid=O[:n], bias=w["b_o"], x2=x2,
+                     stream=stream)
+        mt.mlp_fwd(sh, V2, w["w_fc1"], w["b_fc1"], w["w_fc2"], Y, msv, mws, stream)
+        mt.sp_add_fwd(sh, x2, Y[:n], w["b_fc2"], out_i, stream=stream)
+        mt.mlp_bwd(sh, V2, w["w_fc1"], w["w_fc2"], msv, dOut, dV2, g["w_fc1"], g["b_fc1"], g["w_fc2"], mws, stream)
+        mt.sp_ln_bwd(sh, dV2[:n], x2, w["ln2_g"], st[2], st[3], douti, dX2[:n], g["ln2_g"], g["ln2_b"], lws,
+                     xin_f32=True, dres_f32=False, dx_f32=dx2f, dsum=g["b_o"], dres_sum=g["b_fc2"], stream=stream)
+        mt.attn_bwd(sh, U, w["w_qkv"], w["w_o"], asv, dX2, dU, g["w_qkv"], g["b_qkv"], g["w_o"], aws, stream)
+        mt.sp_ln_bwd(sh, dU[:n], xi, w["ln1_g"], st[0], st[1], dx2f, dx_i, g["ln1_g"], g["ln1_b"], lws,
+                     xin_f32=False, dres_f32=True, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(iters):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / iters
+    mt.timing_reset()
+    mt.timing_enable(True, "sp_")
+    step()
+    torch.cuda.synchronize()
+    mt.timing_enable(False)
+    row_ms = sum(r[1] for r in mt.timing_records())
+    mt.timing_reset()
+    flops = si.model_flops(shape, causal=True)
+    # activations a rank keeps between its forward and backward for the row-local parts:
+    # x2 (fp32) and four fp32 row statistics over n rows, against M rows without SP
+    return {"rank": 0, "rows": n, "ms_per_step": round(ms, 4), "model_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "row_local_ms": round(row_ms, 4), "steps": iters,
+            "row_local_saved_bytes": int(n * h * 4 + 4 * n * 4), "tp_row_local_saved_bytes": int(M * h * 4 + 4 * M * 4)}
 
 
 def cpu_baseline(case, shape, min_seconds: float = 10.0, max_steps: int = 5):
@@ -276,6 +346,7 @@ def main():
                     "avg_ms": round(avg_ms, 4), "launches": len(recs), "gflop_per_launch": round(kflops / 1e9, 2)}
 
     optim = None if args.no_optimizer else optimizer_step(mt, si, torch, shape, stream)
+    sp = sp_share(mt, si, torch, shape, weights[0], acts[0], dout, stream) if L == 1 and not args.no_sp else None
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -305,6 +376,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "optimizer_step": optim,
+        "sp_share": sp,
         "recompute": recompute_report(shape, ms_per_step, mt.layer_saved_bytes(sh)) if L == 1 else None,
     }
     print(json.dumps(line), flush=True)

@@ -135,6 +135,67 @@ int mt_mlp_bwd(const mt_shape *shape, const void *x, const void *w_fc1, const vo
                size_t saved_bytes, const void *dy, void *dx_partial, float *dw_fc1, float *db_fc1, float *dw_fc2,
                void *workspace, size_t workspace_bytes, void *stream);
 
+/* Attention block alone, the head-parallel counterpart of mt_mlp_* (concept report,
+ * section 4.1: heads split over ranks, output projection split by rows):
+ *   QKV = u W_qkv^T + b_qkv;  ctx = causal softmax attention over the shard's heads;
+ *   o_partial = ctx W_o^T      with u [M, h], W_qkv [3*ht, h], b_qkv [3*ht], W_o [h, ht].
+ * No LayerNorm, no b_o, no residual: the sum of o_partial over the tp shards is the
+ * unsharded block. MT_BF16 and MT_FP32 only (MT_BF16_QK needs LayerNorm's rounding
+ * remainder of u, which a caller-supplied u does not carry: MT_ERR_UNSUPPORTED). */
+size_t mt_attn_saved_bytes(const mt_shape *shape);
+size_t mt_attn_workspace_bytes(const mt_shape *shape);
+int mt_attn_fwd(const mt_shape *shape, const void *u, const void *w_qkv, const void *b_qkv, const void *w_o,
+                void *o_partial, void *saved, size_t saved_bytes, void *workspace, size_t workspace_bytes,
+                void *stream);
+/* Backward given d_o [M, h] (the gradient of the block output): du_partial [M, h]
+ * (activation dtype; its sum over shards is the block's input gradient, section 4.2),
+ * dw_qkv [3*ht, h], db_qkv [3*ht], dw_o [h, ht] in fp32. u, the weights and `saved` must
+ * be those of the forward. */
+int mt_attn_bwd(const mt_shape *shape, const void *u, const void *w_qkv, const void *w_o, const void *saved,
+                size_t saved_bytes, const void *d_o, void *du_partial, float *dw_qkv, float *db_qkv, float *dw_o,
+                void *workspace, size_t workspace_bytes, void *stream);
+
+/* Sequence-parallel share of a layer (concept report, section 4.3: the sequence is split
+ * over the same group of devices as the tensor-parallel split, each device keeps one
+ * segment and runs LayerNorm locally; section 6.4: activations per device drop to S/tp;
+ * section 8(1): the all-reduce split into reduce-scatter and all-gather steps).
+ * Rank `shard` owns seq/tp positions of each sequence, rows = micro_batch * seq / tp
+ * tokens, stored [rows, h] in (sequence, position) order; seq % tp == 0 is required
+ * (MT_ERR_INVALID_ARG). One layer on rank i, the collectives being the caller's:
+ *   mt_sp_ln_fwd(x_i)             -> u_i              ; all-gather u   -> U [M, h]
+ *   mt_attn_fwd(U)                -> O_i partial      ; reduce-scatter -> O_rs [rows, h]
+ *   mt_sp_ln_fwd(x_i, O_rs, b_o)  -> x2_i (fp32), v2_i; all-gather v2  -> V2 [M, h]
+ *   mt_mlp_fwd(V2)                -> Y_i partial      ; reduce-scatter -> Y_rs [rows, h]
+ *   mt_sp_add_fwd(x2_i, Y_rs, b_fc2) -> out_i
+ * and backward with the collectives swapped (all-gather dout, then mt_mlp_bwd,
+ * reduce-scatter dV2, mt_sp_ln_bwd for LayerNorm 2, all-gather dX2, mt_attn_bwd,
+ * reduce-scatter dU, mt_sp_ln_bwd for LayerNorm 1). The replicated parameters' gradients
+ * from the mt_sp_* calls are this rank's partial sums over its rows (the group's
+ * all-reduce adds them). MT_BF16 and MT_FP32 only.
+ *
+ * mt_sp_ln_fwd: resid == NULL: y = LN(x) (bias and x2 unused, may be NULL);
+ *   else x2 = x + resid + bias (fp32, unrounded) and y = LN(x2). x, resid, y [rows, h];
+ *   gamma, beta, bias [h] in the activation dtype; mean, rstd [rows] fp32 (kept for the
+ *   backward). */
+int mt_sp_ln_fwd(const mt_shape *shape, const void *x, const void *resid, const void *bias, const void *gamma,
+                 const void *beta, float *x2, void *y, float *mean, float *rstd, void *stream);
+/* mt_sp_add_fwd: out = x2 + y + bias, x2 fp32 [rows, h], y and out [rows, h], bias [h]. */
+int mt_sp_add_fwd(const mt_shape *shape, const float *x2, const void *y, const void *bias, void *out, void *stream);
+/* mt_sp_ln_bwd: dx = dres + LN-backward(dy; xin, gamma, mean, rstd) over the rank's rows.
+ *   xin: the LayerNorm input (fp32 when xin_f32, e.g. x2; else the activation dtype);
+ *   dres: the residual path's gradient (fp32 when dres_f32); dx [rows, h] in the
+ *   activation dtype, dx_f32 (may be NULL) an fp32 copy. Column sums over the rows, fp32:
+ *   dgamma, dbeta (required); dsum = sum of dx (may be NULL; needs dx_f32, whose values
+ *   it sums: MT_ERR_INVALID_ARG otherwise); dres_sum = sum of dres (may be NULL).
+ *   LayerNorm 2: xin = x2, dres = dout -> dx = dX2, dsum = db_o, dres_sum = db_fc2.
+ *   LayerNorm 1: xin = x, dres = dX2 (fp32) -> dx = dX.
+ *   Workspace: mt_sp_ln_workspace_bytes. */
+size_t mt_sp_ln_workspace_bytes(const mt_shape *shape);
+int mt_sp_ln_bwd(const mt_shape *shape, const void *dy, const void *xin, int xin_f32, const void *gamma,
+                 const float *mean, const float *rstd, const void *dres, int dres_f32, void *dx, float *dx_f32,
+                 float *dgamma, float *dbeta, float *dsum, float *dres_sum, void *workspace, size_t workspace_bytes,
+                 void *stream);
+
 /* Fused AdamW step over n fp32 master parameters, one pass (the oreateai.com
  * Megatron-LM analysis, "In-Depth Analysis of Distributed Training Frameworks for Large
  * Models ... Megatron-LM", section 2.2: the fused optimizer step; section 3.1: beta1 0.9,

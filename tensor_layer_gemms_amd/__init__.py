@@ -52,6 +52,15 @@ _SIGS = {
     "mt_mlp_workspace_bytes": (_SZ, [ctypes.POINTER(Shape)]),
     "mt_mlp_fwd": (_I, [ctypes.POINTER(Shape), _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP, _SZ, _VP]),
     "mt_mlp_bwd": (_I, [ctypes.POINTER(Shape), _VP, _VP, _VP, _VP, _SZ, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "mt_attn_saved_bytes": (_SZ, [ctypes.POINTER(Shape)]),
+    "mt_attn_workspace_bytes": (_SZ, [ctypes.POINTER(Shape)]),
+    "mt_attn_fwd": (_I, [ctypes.POINTER(Shape), _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP, _SZ, _VP]),
+    "mt_attn_bwd": (_I, [ctypes.POINTER(Shape), _VP, _VP, _VP, _VP, _SZ, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "mt_sp_ln_fwd": (_I, [ctypes.POINTER(Shape), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "mt_sp_add_fwd": (_I, [ctypes.POINTER(Shape), _VP, _VP, _VP, _VP, _VP]),
+    "mt_sp_ln_workspace_bytes": (_SZ, [ctypes.POINTER(Shape)]),
+    "mt_sp_ln_bwd": (_I, [ctypes.POINTER(Shape), _VP, _VP, _I, _VP, _VP, _VP, _VP, _I, _VP, _VP, _VP, _VP, _VP,
+                          _VP, _VP, _SZ, _VP]),
     "mt_adamw_step": (_I, [ctypes.c_int64, _VP, _VP, _VP, _VP, _VP, ctypes.c_float, ctypes.c_float, ctypes.c_float,
                            ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_int32, _VP]),
     "mt_status_string": (ctypes.c_char_p, [_I]),
@@ -224,6 +233,59 @@ def mlp_bwd(shape: Shape, x, w_fc1, w_fc2, saved, dy, dx_partial, dw_fc1, db_fc1
     _check("mt_mlp_bwd", lib().mt_mlp_bwd(ctypes.byref(shape), _ptr(x), _ptr(w_fc1), _ptr(w_fc2), _ptr(saved),
                                           _nbytes(saved), _ptr(dy), _ptr(dx_partial), _ptr(dw_fc1), _ptr(db_fc1),
                                           _ptr(dw_fc2), _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def attn_saved_bytes(shape: Shape) -> int:
+    return lib().mt_attn_saved_bytes(ctypes.byref(shape))
+
+
+def attn_workspace_bytes(shape: Shape) -> int:
+    return lib().mt_attn_workspace_bytes(ctypes.byref(shape))
+
+
+def attn_fwd(shape: Shape, u, w_qkv, b_qkv, w_o, o_partial, saved, workspace, stream=None) -> None:
+    """mt_attn_fwd: o_partial = Attn(u W_qkv^T + b_qkv) W_o^T over the shard's heads."""
+    _check("mt_attn_fwd", lib().mt_attn_fwd(ctypes.byref(shape), _ptr(u), _ptr(w_qkv), _ptr(b_qkv), _ptr(w_o),
+                                            _ptr(o_partial), _ptr(saved), _nbytes(saved), _ptr(workspace),
+                                            _nbytes(workspace), _stream(stream)))
+
+
+def attn_bwd(shape: Shape, u, w_qkv, w_o, saved, d_o, du_partial, dw_qkv, db_qkv, dw_o, workspace,
+             stream=None) -> None:
+    """mt_attn_bwd: du_partial and fp32 dW_qkv, db_qkv, dW_o of the attention block."""
+    _check("mt_attn_bwd", lib().mt_attn_bwd(ctypes.byref(shape), _ptr(u), _ptr(w_qkv), _ptr(w_o), _ptr(saved),
+                                            _nbytes(saved), _ptr(d_o), _ptr(du_partial), _ptr(dw_qkv),
+                                            _ptr(db_qkv), _ptr(dw_o), _ptr(workspace), _nbytes(workspace),
+                                            _stream(stream)))
+
+
+def sp_ln_fwd(shape: Shape, x, gamma, beta, y, mean, rstd, resid=None, bias=None, x2=None, stream=None) -> None:
+    """mt_sp_ln_fwd over the rank's seq/tp share of the tokens: y = LN(x), or with resid,
+    x2 = x + resid + bias (fp32) and y = LN(x2)."""
+    _check("mt_sp_ln_fwd", lib().mt_sp_ln_fwd(ctypes.byref(shape), _ptr(x), _ptr(resid), _ptr(bias), _ptr(gamma),
+                                              _ptr(beta), _ptr(x2), _ptr(y), _ptr(mean), _ptr(rstd),
+                                              _stream(stream)))
+
+
+def sp_add_fwd(shape: Shape, x2, y, bias, out, stream=None) -> None:
+    """mt_sp_add_fwd: out = x2 + y + bias over the rank's rows."""
+    _check("mt_sp_add_fwd", lib().mt_sp_add_fwd(ctypes.byref(shape), _ptr(x2), _ptr(y), _ptr(bias), _ptr(out),
+                                                _stream(stream)))
+
+
+def sp_ln_workspace_bytes(shape: Shape) -> int:
+    return lib().mt_sp_ln_workspace_bytes(ctypes.byref(shape))
+
+
+def sp_ln_bwd(shape: Shape, dy, xin, gamma, mean, rstd, dres, dx, dgamma, dbeta, workspace, *, xin_f32: bool,
+              dres_f32: bool, dx_f32=None, dsum=None, dres_sum=None, stream=None) -> None:
+    """mt_sp_ln_bwd: dx = dres + LN-backward(dy) over the rank's rows, with the rank's
+    partial column sums dgamma, dbeta and optionally sum(dx) and sum(dres)."""
+    _check("mt_sp_ln_bwd", lib().mt_sp_ln_bwd(ctypes.byref(shape), _ptr(dy), _ptr(xin), 1 if xin_f32 else 0,
+                                              _ptr(gamma), _ptr(mean), _ptr(rstd), _ptr(dres), 1 if dres_f32 else 0,
+                                              _ptr(dx), _ptr(dx_f32), _ptr(dgamma), _ptr(dbeta), _ptr(dsum),
+                                              _ptr(dres_sum), _ptr(workspace), _nbytes(workspace),
+                                              _stream(stream)))
 
 
 def timing_enable(enable: bool = True, label_filter: Optional[str] = None) -> None:

@@ -324,46 +324,51 @@ FlashArgs flash_args(const Dims& d, const void* qkv, const void* qkv_lo, void* c
 }
 
 // ------------------------------------------------------------------------- forward
-int layer_fwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, void* out, const LayerSaved& sv,
-                   const LayerFwdWs& ws, hipStream_t stream) {
-  Seq q(stream);
+// Attention block of the shard (F2-F6): QKV_i = U W_qkv_i^T + b_qkv_i, causal attention
+// over the rank's heads, O_i = ctx_i W_o_i^T (the row-parallel partial), from the
+// LayerNorm output u [M, h] (and, MT_BF16_QK, its rounding remainder u_lo).
+struct AttnBufs {
+  void *qkv, *p, *ctx;  // saved: projections, probabilities (unfused), context
+  float* lse;           // saved: row log-sum-exp (fused)
+  void* qkv_lo_saved;   // saved: Q, K remainders (fused, MT_BF16_QK)
+  float* S;             // workspace: scores (unfused) or the QKV partials (MT_BF16_QK)
+  void* qkv_lo_ws;      // workspace: Q, K remainders (unfused, MT_BF16_QK)
+};
+
+void attn_fwd_part(Seq& q, const Dims& d, const void* u, const void* u_lo, const void* w_qkv, const void* b_qkv,
+                   const void* w_o, const AttnBufs& b, void* o, hipStream_t stream) {
   const bool bf = d.bf16;
   const double es = (double)d.es;
-  const double Mh = (double)d.M * d.h;
   const float scale = 1.0f / std::sqrt((float)d.d);
   const int batch = (int)(d.B * d.at);
   Attn at{d};
   // Q, K remainders (MT_BF16_QK; kept for the backward when fused), else null
-  void* qkv_lo = d.flash ? sv.qkv_lo : ws.qkv_lo;
-
-  // F1 LayerNorm 1 (MT_BF16_QK: also the rounding remainder U_lo of U)
-  q.run("ln1_fwd", 0, Mh * es * (d.comp ? 3 : 2), [&] {
-    return launch_ln_fwd(bf, x, w.ln1_g, w.ln1_b, sv.u, ws.u_lo, sv.mean1, sv.rstd1, (int)d.M, (int)d.h, kLnEps,
-                         stream);
-  });
+  void* qkv_lo = d.flash ? b.qkv_lo_saved : b.qkv_lo_ws;
+  (void)bf;
+  (void)es;
   // F2 column-parallel QKV projection + bias. MT_BF16_QK: the Q and K columns are formed
   // from U_hi + U_lo (a second K segment) and stored as hi + lo bf16 pairs, so the
   // softmax logits, whose sharp maxima amplify input rounding, see Q and K to ~16 bits.
   q.run("qkv_fwd", gflop(d.M, d.qkv, d.h) + (d.comp ? gflop(d.M, 2 * d.hs, d.h) : 0), 0, [&] {
-    GemmArgs g = plain(sv.u, d.h, w.w_qkv, d.h, sv.qkv, d.qkv, d.M, d.qkv, d.h);
-    g.vec = w.b_qkv;
+    GemmArgs g = plain(u, d.h, w_qkv, d.h, b.qkv, d.qkv, d.M, d.qkv, d.h);
+    g.vec = b_qkv;
     if (!d.comp) return gemm(d, g, true, true, EPI_BIAS, 1, stream);
     // The Q and K columns take U_hi W^T + U_lo W^T, twice the contraction of the V
     // columns. The two products run as equal-depth problems of one launch into fp32
     // partials (which fills the CUs evenly), and a pass adds them and the bias and
     // splits Q, K into hi + lo.
-    float* hi = ws.S;
-    float* lo = ws.S + d.M * d.qkv;
-    const GemmArgs ghi = plain(sv.u, d.h, w.w_qkv, d.h, hi, d.qkv, d.M, d.qkv, d.h);
-    const GemmArgs glo = plain(ws.u_lo, d.h, w.w_qkv, d.h, lo, 2 * d.hs, d.M, 2 * d.hs, d.h);
+    float* hi = b.S;
+    float* lo = b.S + d.M * d.qkv;
+    const GemmArgs ghi = plain(u, d.h, w_qkv, d.h, hi, d.qkv, d.M, d.qkv, d.h);
+    const GemmArgs glo = plain(u_lo, d.h, w_qkv, d.h, lo, 2 * d.hs, d.M, 2 * d.hs, d.h);
     const hipError_t e = launch_gemm_bf16_pair(ghi, true, true, EPI_STORE_F32, glo, true, true, EPI_STORE_F32, stream);
     if (e == hipSuccess)
-      return launch_qkv_finish(hi, lo, w.b_qkv, sv.qkv, qkv_lo, (int)d.M, (int)d.qkv, (int)(2 * d.hs), stream);
+      return launch_qkv_finish(hi, lo, b_qkv, b.qkv, qkv_lo, (int)d.M, (int)d.qkv, (int)(2 * d.hs), stream);
     if (e != hipErrorNotSupported) return e;
     // Operands the paired launch cannot address: one GEMM with a second K segment for
     // the Q and K columns.
-    g.seg_a[1] = ws.u_lo;
-    g.seg_b[1] = w.w_qkv;
+    g.seg_a[1] = u_lo;
+    g.seg_b[1] = w_qkv;
     g.nseg = 2;
     g.seg_n = (int)(2 * d.hs);
     g.C2 = qkv_lo;
@@ -374,21 +379,21 @@ int layer_fwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, void
   // log-sum-exp for the backward.
   if (d.flash) {
     q.run("attn_fwd", 2 * at.flops(), 0, [&] {
-      FlashArgs fa = flash_args(d, sv.qkv, qkv_lo, sv.ctx, sv.lse, scale);
+      FlashArgs fa = flash_args(d, b.qkv, qkv_lo, b.ctx, b.lse, scale);
       return launch_flash_fwd(fa, (int)d.d, stream);
     });
   } else {
     // F3 scores S = Q K^T / sqrt(d), causal tiles only, fp32 (MT_BF16_QK:
     // Q_hi K_hi^T + Q_hi K_lo^T + Q_lo K_hi^T)
     q.run("attn_scores", at.flops() * (d.comp ? 3 : 1), 0, [&] {
-      GemmArgs g = plain(sv.qkv, d.qkv, static_cast<const char*>(sv.qkv) + d.hs * d.es, d.qkv, ws.S, d.seq, d.seq,
+      GemmArgs g = plain(b.qkv, d.qkv, static_cast<const char*>(b.qkv) + d.hs * d.es, d.qkv, b.S, d.seq, d.seq,
                          d.seq, d.d);
       if (d.comp) {
         const char* lo = static_cast<const char*>(qkv_lo);
-        g.seg_a[1] = sv.qkv;
+        g.seg_a[1] = b.qkv;
         g.seg_b[1] = lo + d.hs * d.es;
         g.seg_a[2] = lo;
-        g.seg_b[2] = static_cast<const char*>(sv.qkv) + d.hs * d.es;
+        g.seg_b[2] = static_cast<const char*>(b.qkv) + d.hs * d.es;
         g.nseg = 3;
       }
       at.head_operand(d.qkv, g.a_so, g.a_si);
@@ -402,11 +407,11 @@ int layer_fwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, void
     });
     // F4 causal softmax -> P
     q.run("softmax_fwd", 0, (double)batch * at.causal_pairs() * (4 + es), [&] {
-      return launch_softmax_causal(bf, ws.S, sv.p, batch, (int)d.seq, stream);
+      return launch_softmax_causal(bf, b.S, b.p, batch, (int)d.seq, stream);
     });
     // F5 ctx = P V (k <= q), heads concatenated in columns
     q.run("attn_ctx", at.flops(), 0, [&] {
-      GemmArgs g = plain(sv.p, d.seq, static_cast<const char*>(sv.qkv) + 2 * d.hs * d.es, d.qkv, sv.ctx, d.hs, d.seq,
+      GemmArgs g = plain(b.p, d.seq, static_cast<const char*>(b.qkv) + 2 * d.hs * d.es, d.qkv, b.ctx, d.hs, d.seq,
                          d.d, d.seq);
       g.a_so = d.at * d.seq * d.seq;
       g.a_si = d.seq * d.seq;
@@ -419,9 +424,28 @@ int layer_fwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, void
   }
   // F6 row-parallel out-projection: partial sum O_i (the all-reduce input)
   q.run("out_proj_fwd", gflop(d.M, d.h, d.hs), 0, [&] {
-    GemmArgs g = plain(sv.ctx, d.hs, w.w_o, d.hs, ws.o, d.h, d.M, d.h, d.hs);
+    GemmArgs g = plain(b.ctx, d.hs, w_o, d.hs, o, d.h, d.M, d.h, d.hs);
     return gemm(d, g, true, true, EPI_STORE, 1, stream);
   });
+}
+
+AttnBufs attn_bufs(const LayerSaved& sv, const LayerFwdWs& ws) {
+  return AttnBufs{sv.qkv, sv.p, sv.ctx, sv.lse, sv.qkv_lo, ws.S, ws.qkv_lo};
+}
+
+int layer_fwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, void* out, const LayerSaved& sv,
+                   const LayerFwdWs& ws, hipStream_t stream) {
+  Seq q(stream);
+  const bool bf = d.bf16;
+  const double es = (double)d.es;
+  const double Mh = (double)d.M * d.h;
+
+  // F1 LayerNorm 1 (MT_BF16_QK: also the rounding remainder U_lo of U)
+  q.run("ln1_fwd", 0, Mh * es * (d.comp ? 3 : 2), [&] {
+    return launch_ln_fwd(bf, x, w.ln1_g, w.ln1_b, sv.u, ws.u_lo, sv.mean1, sv.rstd1, (int)d.M, (int)d.h, kLnEps,
+                         stream);
+  });
+  attn_fwd_part(q, d, sv.u, ws.u_lo, w.w_qkv, w.b_qkv, w.w_o, attn_bufs(sv, ws), ws.o, stream);
   // F7 X2 = X + AR(O_i) + b_o (AR = identity on one GPU; X2 kept in fp32), V2 = LN2(X2)
   q.run("add_ln2_fwd", 0, Mh * (3 * es + 4), [&] {
     return launch_add_ln_fwd(bf, x, ws.o, w.b_o, w.ln2_g, w.ln2_b, sv.x2, sv.v2, sv.mean2, sv.rstd2, (int)d.M,
@@ -447,65 +471,27 @@ int layer_fwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, void
 }
 
 // ------------------------------------------------------------------------- backward
-int layer_bwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, const LayerSaved& sv, const void* dout,
-                   void* dx, const mt_layer_grads& gr, const LayerBwdWs& ws, hipStream_t stream) {
-  Seq q(stream);
+// Backward of the attention block (B4-B7) given dO [M, h], the gradient of its output:
+// dW_o = dO^T ctx, dctx = dO W_o; attention backward; db_qkv, dW_qkv = dQKV^T U and the
+// input-gradient partial du = dQKV W_qkv.
+struct AttnBwdWs {
+  void *dctx, *ds, *dqkv;
+  float *D, *part, *spart;
+};
+
+void attn_bwd_part(Seq& q, const Dims& d, const void* u, const void* w_qkv, const void* w_o, const AttnBufs& sv,
+                   const void* dO, void* du, float* dw_qkv, float* db_qkv, float* dw_o, const AttnBwdWs& ws,
+                   hipStream_t stream) {
   const bool bf = d.bf16;
   const double es = (double)d.es;
-  const double Mh = (double)d.M * d.h;
   const float scale = 1.0f / std::sqrt((float)d.d);
   const int batch = (int)(d.B * d.at);
   const int M = (int)d.M;
   Attn at{d};
-
-  // B1 FC2: db_fc2, dW2 = dOut^T Z, dA = (dOut W2) * GeLU'(A)
-  q.run("db_fc2", 0, Mh * es, [&] {
-    return launch_colsum(bf, 0, dout, false, nullptr, false, nullptr, nullptr, gr.b_fc2, nullptr, ws.part, M,
-                         (int)d.h, stream);
-  });
-  q.run("fc2_dgrad_wgrad", 2 * gflop(d.M, d.ft, d.h), 0, [&] {
-    GemmArgs dg = plain(dout, d.h, w.w_fc2, d.ft, ws.da, d.ft, d.M, d.ft, d.h);
-    dg.aux = sv.a;
-    const GemmArgs wg = plain(dout, d.h, sv.z, d.ft, gr.w_fc2, d.ft, d.h, d.ft, d.M);
-    return gemm_dgrad_wgrad(d, dg, EPI_DGELU, wg, stream);
-  });
-  // B2 FC1: db_fc1, dW1 = dA^T V2, dV2 = dA W1 (partial)
-  q.run("db_fc1", 0, d.M * d.ft * es, [&] {
-    return launch_colsum(bf, 0, ws.da, false, nullptr, false, nullptr, nullptr, gr.b_fc1, nullptr, ws.part, M,
-                         (int)d.ft, stream);
-  });
-  q.run("fc1_dgrad_wgrad", 2 * gflop(d.M, d.h, d.ft), 0, [&] {
-    const GemmArgs dg = plain(ws.da, d.ft, w.w_fc1, d.h, ws.dv2, d.h, d.M, d.h, d.ft);
-    const GemmArgs wg = plain(ws.da, d.ft, sv.v2, d.h, gr.w_fc1, d.h, d.ft, d.h, d.M);
-    return gemm_dgrad_wgrad(d, dg, EPI_STORE, wg, stream, ws.spart);
-  });
-  // B3 dX2 = dOut + LN2-backward(AR(dV2)) (written as the GEMM operand and as an fp32
-  // copy for the residual path); dgamma2, dbeta2; db_o = colsum(dX2) — in one pass over
-  // the rows where the fused kernel covers h, else as separate column sums
-  const bool ln_sums = ln_bwd_sums_supported((int)d.h);
-  if (ln_sums) {
-    q.run("ln2_bwd", 0, Mh * (3 * es + 8), [&] {
-      return launch_ln_bwd_sums(bf, ws.dv2, sv.x2, true, w.ln2_g, sv.mean2, sv.rstd2, dout, false, ws.dx2, ws.dx2f,
-                                ws.part, gr.ln2_g, gr.ln2_b, gr.b_o, M, (int)d.h, stream);
-    });
-  } else {
-    q.run("ln2_bwd", 0, Mh * (3 * es + 8), [&] {
-      return launch_ln_bwd(bf, ws.dv2, sv.x2, true, w.ln2_g, sv.mean2, sv.rstd2, dout, false, ws.dx2, ws.dx2f, M,
-                           (int)d.h, stream);
-    });
-    q.run("ln2_param_grads", 0, Mh * (es + 4), [&] {
-      return launch_colsum(bf, 1, ws.dv2, false, sv.x2, true, sv.mean2, sv.rstd2, gr.ln2_g, gr.ln2_b, ws.part, M,
-                           (int)d.h, stream);
-    });
-    q.run("db_o", 0, Mh * 4, [&] {
-      return launch_colsum(bf, 0, ws.dx2f, true, nullptr, false, nullptr, nullptr, gr.b_o, nullptr, ws.part, M,
-                           (int)d.h, stream);
-    });
-  }
   // B4 out-projection: dW_o = dX2^T ctx, dctx = dX2 W_o
   q.run("out_proj_dgrad_wgrad", 2 * gflop(d.M, d.hs, d.h), 0, [&] {
-    const GemmArgs dg = plain(ws.dx2, d.h, w.w_o, d.hs, ws.dctx, d.hs, d.M, d.hs, d.h);
-    const GemmArgs wg = plain(ws.dx2, d.h, sv.ctx, d.hs, gr.w_o, d.hs, d.h, d.hs, d.M);
+    const GemmArgs dg = plain(dO, d.h, w_o, d.hs, ws.dctx, d.hs, d.M, d.hs, d.h);
+    const GemmArgs wg = plain(dO, d.h, sv.ctx, d.hs, dw_o, d.hs, d.h, d.hs, d.M);
     return gemm_dgrad_wgrad(d, dg, EPI_STORE, wg, stream, ws.spart);
   });
   // B5/B6 attention: D = rowsum(dctx * ctx) = rowsum(P * dP); dS = P * (dctx V^T - D)
@@ -516,7 +502,7 @@ int layer_bwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, cons
     // B5/B6 fused: P recomputed from Q, K and the saved log-sum-exp; dK, dV per key block
     // and dQ per query block, each summed in one work-group (no atomics).
     q.run("attn_bwd", 4 * at.flops(), 0, [&] {
-      FlashArgs fa = flash_args(d, sv.qkv, sv.qkv_lo, nullptr, sv.lse, scale);
+      FlashArgs fa = flash_args(d, sv.qkv, sv.qkv_lo_saved, nullptr, sv.lse, scale);
       fa.dctx = ws.dctx;
       fa.D = ws.D;
       fa.dqkv = ws.dqkv;
@@ -573,14 +559,70 @@ int layer_bwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, cons
   }
   // B7 QKV: db_qkv, dW_qkv = dQKV^T U, dU = dQKV W_qkv (partial)
   q.run("db_qkv", 0, d.M * d.qkv * es, [&] {
-    return launch_colsum(bf, 0, ws.dqkv, false, nullptr, false, nullptr, nullptr, gr.b_qkv, nullptr, ws.part, M,
+    return launch_colsum(bf, 0, ws.dqkv, false, nullptr, false, nullptr, nullptr, db_qkv, nullptr, ws.part, M,
                          (int)d.qkv, stream);
   });
   q.run("qkv_dgrad_wgrad", 2 * gflop(d.M, d.h, d.qkv), 0, [&] {
-    const GemmArgs dg = plain(ws.dqkv, d.qkv, w.w_qkv, d.h, ws.dv2, d.h, d.M, d.h, d.qkv);
-    const GemmArgs wg = plain(ws.dqkv, d.qkv, sv.u, d.h, gr.w_qkv, d.h, d.qkv, d.h, d.M);
+    const GemmArgs dg = plain(ws.dqkv, d.qkv, w_qkv, d.h, du, d.h, d.M, d.h, d.qkv);
+    const GemmArgs wg = plain(ws.dqkv, d.qkv, u, d.h, dw_qkv, d.h, d.qkv, d.h, d.M);
     return gemm_dgrad_wgrad(d, dg, EPI_STORE, wg, stream, ws.spart);
   });
+}
+
+int layer_bwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, const LayerSaved& sv, const void* dout,
+                   void* dx, const mt_layer_grads& gr, const LayerBwdWs& ws, hipStream_t stream) {
+  Seq q(stream);
+  const bool bf = d.bf16;
+  const double es = (double)d.es;
+  const double Mh = (double)d.M * d.h;
+  const int M = (int)d.M;
+
+  // B1 FC2: db_fc2, dW2 = dOut^T Z, dA = (dOut W2) * GeLU'(A)
+  q.run("db_fc2", 0, Mh * es, [&] {
+    return launch_colsum(bf, 0, dout, false, nullptr, false, nullptr, nullptr, gr.b_fc2, nullptr, ws.part, M,
+                         (int)d.h, stream);
+  });
+  q.run("fc2_dgrad_wgrad", 2 * gflop(d.M, d.ft, d.h), 0, [&] {
+    GemmArgs dg = plain(dout, d.h, w.w_fc2, d.ft, ws.da, d.ft, d.M, d.ft, d.h);
+    dg.aux = sv.a;
+    const GemmArgs wg = plain(dout, d.h, sv.z, d.ft, gr.w_fc2, d.ft, d.h, d.ft, d.M);
+    return gemm_dgrad_wgrad(d, dg, EPI_DGELU, wg, stream);
+  });
+  // B2 FC1: db_fc1, dW1 = dA^T V2, dV2 = dA W1 (partial)
+  q.run("db_fc1", 0, d.M * d.ft * es, [&] {
+    return launch_colsum(bf, 0, ws.da, false, nullptr, false, nullptr, nullptr, gr.b_fc1, nullptr, ws.part, M,
+                         (int)d.ft, stream);
+  });
+  q.run("fc1_dgrad_wgrad", 2 * gflop(d.M, d.h, d.ft), 0, [&] {
+    const GemmArgs dg = plain(ws.da, d.ft, w.w_fc1, d.h, ws.dv2, d.h, d.M, d.h, d.ft);
+    const GemmArgs wg = plain(ws.da, d.ft, sv.v2, d.h, gr.w_fc1, d.h, d.ft, d.h, d.M);
+    return gemm_dgrad_wgrad(d, dg, EPI_STORE, wg, stream, ws.spart);
+  });
+  // B3 dX2 = dOut + LN2-backward(AR(dV2)) (written as the GEMM operand and as an fp32
+  // copy for the residual path); dgamma2, dbeta2; db_o = colsum(dX2) — in one pass over
+  // the rows where the fused kernel covers h, else as separate column sums
+  const bool ln_sums = ln_bwd_sums_supported((int)d.h);
+  if (ln_sums) {
+    q.run("ln2_bwd", 0, Mh * (3 * es + 8), [&] {
+      return launch_ln_bwd_sums(bf, ws.dv2, sv.x2, true, w.ln2_g, sv.mean2, sv.rstd2, dout, false, ws.dx2, ws.dx2f,
+                                ws.part, gr.ln2_g, gr.ln2_b, gr.b_o, M, (int)d.h, stream);
+    });
+  } else {
+    q.run("ln2_bwd", 0, Mh * (3 * es + 8), [&] {
+      return launch_ln_bwd(bf, ws.dv2, sv.x2, true, w.ln2_g, sv.mean2, sv.rstd2, dout, false, ws.dx2, ws.dx2f, M,
+                           (int)d.h, stream);
+    });
+    q.run("ln2_param_grads", 0, Mh * (es + 4), [&] {
+      return launch_colsum(bf, 1, ws.dv2, false, sv.x2, true, sv.mean2, sv.rstd2, gr.ln2_g, gr.ln2_b, ws.part, M,
+                           (int)d.h, stream);
+    });
+    q.run("db_o", 0, Mh * 4, [&] {
+      return launch_colsum(bf, 0, ws.dx2f, true, nullptr, false, nullptr, nullptr, gr.b_o, nullptr, ws.part, M,
+                           (int)d.h, stream);
+    });
+  }
+  attn_bwd_part(q, d, sv.u, w.w_qkv, w.w_o, attn_bufs(sv, LayerFwdWs{}), ws.dx2, ws.dv2, gr.w_qkv, gr.b_qkv, gr.w_o,
+                AttnBwdWs{ws.dctx, ws.ds, ws.dqkv, ws.D, ws.part, ws.spart}, stream);
   // B8 dX = dX2 + LN1-backward(AR(dU)); dgamma1, dbeta1
   if (ln_sums) {
     q.run("ln1_bwd", 0, Mh * (3 * es + 4), [&] {
@@ -637,6 +679,59 @@ int mlp_bwd_impl(const Dims& d, const void* x, const void* w1, const void* w2, c
   });
   return q.status();
 }
+
+// ------------------------------------------------------------------------- attention block
+// Activation store of mt_attn_fwd -> mt_attn_bwd and the workspace either needs.
+size_t carve_attn_saved(const Dims& d, void* base, AttnBufs* b) {
+  Carver c(base);
+  b->qkv = c.take(d.M * d.qkv * d.es);
+  b->p = d.flash ? nullptr : c.take(d.B * d.at * d.seq * d.seq * d.es);
+  b->lse = d.flash ? c.take<float>(d.B * d.at * d.seq * 4) : nullptr;
+  b->qkv_lo_saved = nullptr;
+  b->ctx = c.take(d.M * d.hs * d.es);
+  return c.off;
+}
+size_t carve_attn_fwd_ws(const Dims& d, void* base, AttnBufs* b) {
+  Carver c(base);
+  b->S = d.flash ? nullptr : c.take<float>(d.B * d.at * d.seq * d.seq * 4);
+  b->qkv_lo_ws = nullptr;
+  return c.off;
+}
+size_t carve_attn_bwd_ws(const Dims& d, void* base, AttnBwdWs* w) {
+  Carver c(base);
+  w->dctx = c.take(d.M * d.hs * d.es);
+  w->ds = d.flash ? nullptr : c.take(d.B * d.at * d.seq * d.seq * d.es);
+  w->dqkv = c.take(d.M * d.qkv * d.es);
+  w->D = c.take<float>(d.B * d.at * d.seq * 4);
+  w->part = c.take<float>(colsum_partial_floats((int)d.M, (int)d.qkv, 0) * 4);
+  const int64_t sp = dgrad_split_floats(d);
+  w->spart = sp ? c.take<float>(sp * 4) : nullptr;
+  return c.off;
+}
+size_t attn_ws_bytes(const Dims& d) {
+  AttnBufs b;
+  AttnBwdWs w;
+  return std::max(carve_attn_fwd_ws(d, nullptr, &b), carve_attn_bwd_ws(d, nullptr, &w));
+}
+
+// ------------------------------------------------------------------------- sequence-parallel rows
+// The rank's share of the tokens under sequence parallelism: seq / tp positions of each
+// of the micro_batch sequences (seq must split evenly). The attention block has no
+// MT_BF16_QK form (its input arrives already rounded), so neither do these calls.
+int validate_sp(const mt_shape* s, Dims* d, int* rows) {
+  const int st = validate_shape(s, d);
+  if (st != MT_OK) return st;
+  if (d->comp) return MT_ERR_UNSUPPORTED;
+  if (s->seq % s->tp != 0) return MT_ERR_INVALID_ARG;
+  *rows = (int)(d->M / d->tp);
+  return MT_OK;
+}
+size_t sp_ln_ws_floats(int rows, int h) {
+  size_t n = std::max(colsum_partial_floats(rows, h, 1), colsum_partial_floats(rows, h, 0));
+  if (ln_bwd_sums_supported(h)) n = std::max(n, ln_bwd_sums_partial_floats(rows, h, 3));
+  return n;
+}
+bool null_or_aligned(const void* p) { return !p || aligned16(p); }
 
 bool weights_ok(const mt_layer_weights* w) {
   if (!w) return false;
@@ -762,6 +857,154 @@ int mt_mlp_bwd(const mt_shape* shape, const void* x, const void* w_fc1, const vo
   carve_mlp_ws(d, workspace, &ws);
   return mlp_bwd_impl(d, x, w_fc1, w_fc2, sv, dy, dx_partial, dw_fc1, db_fc1, dw_fc2, ws,
                       static_cast<hipStream_t>(stream));
+}
+
+size_t mt_attn_saved_bytes(const mt_shape* shape) {
+  Dims d;
+  if (validate_shape(shape, &d) != MT_OK || d.comp) return 0;
+  AttnBufs b;
+  return carve_attn_saved(d, nullptr, &b);
+}
+
+size_t mt_attn_workspace_bytes(const mt_shape* shape) {
+  Dims d;
+  if (validate_shape(shape, &d) != MT_OK || d.comp) return 0;
+  return attn_ws_bytes(d);
+}
+
+int mt_attn_fwd(const mt_shape* shape, const void* u, const void* w_qkv, const void* b_qkv, const void* w_o,
+                void* o_partial, void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  Dims d;
+  const int st = validate_shape(shape, &d);
+  if (st != MT_OK) return st;
+  if (d.comp) return MT_ERR_UNSUPPORTED;
+  if (!aligned16(u) || !aligned16(w_qkv) || !aligned16(b_qkv) || !aligned16(w_o) || !aligned16(o_partial) ||
+      !aligned16(saved) || !aligned16(workspace))
+    return MT_ERR_INVALID_ARG;
+  AttnBufs b;
+  if (saved_bytes < carve_attn_saved(d, nullptr, &b) || workspace_bytes < attn_ws_bytes(d)) return MT_ERR_WORKSPACE;
+  carve_attn_saved(d, saved, &b);
+  carve_attn_fwd_ws(d, workspace, &b);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  Seq q(s);
+  attn_fwd_part(q, d, u, nullptr, w_qkv, b_qkv, w_o, b, o_partial, s);
+  return q.status();
+}
+
+int mt_attn_bwd(const mt_shape* shape, const void* u, const void* w_qkv, const void* w_o, const void* saved,
+                size_t saved_bytes, const void* d_o, void* du_partial, float* dw_qkv, float* db_qkv, float* dw_o,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  Dims d;
+  const int st = validate_shape(shape, &d);
+  if (st != MT_OK) return st;
+  if (d.comp) return MT_ERR_UNSUPPORTED;
+  if (!aligned16(u) || !aligned16(w_qkv) || !aligned16(w_o) || !aligned16(saved) || !aligned16(d_o) ||
+      !aligned16(du_partial) || !aligned16(dw_qkv) || !aligned16(db_qkv) || !aligned16(dw_o) ||
+      !aligned16(workspace))
+    return MT_ERR_INVALID_ARG;
+  AttnBufs b;
+  if (saved_bytes < carve_attn_saved(d, nullptr, &b) || workspace_bytes < attn_ws_bytes(d)) return MT_ERR_WORKSPACE;
+  carve_attn_saved(d, const_cast<void*>(saved), &b);
+  AttnBwdWs w;
+  carve_attn_bwd_ws(d, workspace, &w);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  Seq q(s);
+  attn_bwd_part(q, d, u, w_qkv, w_o, b, d_o, du_partial, dw_qkv, db_qkv, dw_o, w, s);
+  return q.status();
+}
+
+int mt_sp_ln_fwd(const mt_shape* shape, const void* x, const void* resid, const void* bias, const void* gamma,
+                 const void* beta, float* x2, void* y, float* mean, float* rstd, void* stream) {
+  Dims d;
+  int rows = 0;
+  const int st = validate_sp(shape, &d, &rows);
+  if (st != MT_OK) return st;
+  if (!aligned16(x) || !aligned16(gamma) || !aligned16(beta) || !aligned16(y) || !aligned16(mean) ||
+      !aligned16(rstd) || !null_or_aligned(resid))
+    return MT_ERR_INVALID_ARG;
+  if (resid && (!aligned16(bias) || !aligned16(x2))) return MT_ERR_INVALID_ARG;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  Seq q(s);
+  const double rh = (double)rows * d.h, es = (double)d.es;
+  if (!resid) {
+    q.run("sp_ln1_fwd", 0, rh * 2 * es, [&] {
+      return launch_ln_fwd(d.bf16, x, gamma, beta, y, nullptr, mean, rstd, rows, (int)d.h, kLnEps, s);
+    });
+  } else {
+    q.run("sp_add_ln2_fwd", 0, rh * (3 * es + 4), [&] {
+      return launch_add_ln_fwd(d.bf16, x, resid, bias, gamma, beta, x2, y, mean, rstd, rows, (int)d.h, kLnEps, s);
+    });
+  }
+  return q.status();
+}
+
+int mt_sp_add_fwd(const mt_shape* shape, const float* x2, const void* y, const void* bias, void* out, void* stream) {
+  Dims d;
+  int rows = 0;
+  const int st = validate_sp(shape, &d, &rows);
+  if (st != MT_OK) return st;
+  if (!aligned16(x2) || !aligned16(y) || !aligned16(bias) || !aligned16(out)) return MT_ERR_INVALID_ARG;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  Seq q(s);
+  q.run("sp_bias_residual_fwd", 0, (double)rows * d.h * (2 * d.es + 4), [&] {
+    return launch_add_bias_residual(d.bf16, x2, y, bias, out, rows, (int)d.h, s);
+  });
+  return q.status();
+}
+
+size_t mt_sp_ln_workspace_bytes(const mt_shape* shape) {
+  Dims d;
+  int rows = 0;
+  if (validate_sp(shape, &d, &rows) != MT_OK) return 0;
+  return sp_ln_ws_floats(rows, (int)d.h) * 4;
+}
+
+int mt_sp_ln_bwd(const mt_shape* shape, const void* dy, const void* xin, int xin_f32, const void* gamma,
+                 const float* mean, const float* rstd, const void* dres, int dres_f32, void* dx, float* dx_f32,
+                 float* dgamma, float* dbeta, float* dsum, float* dres_sum, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  Dims d;
+  int rows = 0;
+  const int st = validate_sp(shape, &d, &rows);
+  if (st != MT_OK) return st;
+  if (!aligned16(dy) || !aligned16(xin) || !aligned16(gamma) || !aligned16(mean) || !aligned16(rstd) ||
+      !aligned16(dres) || !aligned16(dx) || !aligned16(dgamma) || !aligned16(dbeta) || !aligned16(workspace) ||
+      !null_or_aligned(dx_f32) || !null_or_aligned(dsum) || !null_or_aligned(dres_sum))
+    return MT_ERR_INVALID_ARG;
+  if (dsum && !dx_f32) return MT_ERR_INVALID_ARG;  // the sum of dx is taken over its fp32 values
+  if (workspace_bytes < sp_ln_ws_floats(rows, (int)d.h) * 4) return MT_ERR_WORKSPACE;
+  float* part = static_cast<float*>(workspace);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int h = (int)d.h;
+  const double rh = (double)rows * d.h, es = (double)d.es;
+  const double xb = xin_f32 ? 4 : es, rb = dres_f32 ? 4 : es;
+  Seq q(s);
+  if (ln_bwd_sums_supported(h)) {
+    q.run("sp_ln_bwd", 0, rh * (es + xb + rb + es + (dx_f32 ? 4 : 0)), [&] {
+      return launch_ln_bwd_sums(d.bf16, dy, xin, xin_f32 != 0, gamma, mean, rstd, dres, dres_f32 != 0, dx, dx_f32,
+                                part, dgamma, dbeta, dsum, rows, h, s);
+    });
+  } else {
+    q.run("sp_ln_bwd", 0, rh * (es + xb + rb + es + (dx_f32 ? 4 : 0)), [&] {
+      return launch_ln_bwd(d.bf16, dy, xin, xin_f32 != 0, gamma, mean, rstd, dres, dres_f32 != 0, dx, dx_f32, rows,
+                           h, s);
+    });
+    q.run("sp_ln_param_grads", 0, rh * (es + xb), [&] {
+      return launch_colsum(d.bf16, 1, dy, false, xin, xin_f32 != 0, mean, rstd, dgamma, dbeta, part, rows, h, s);
+    });
+    if (dsum)
+      q.run("sp_ln_dsum", 0, rh * 4, [&] {
+        return launch_colsum(d.bf16, 0, dx_f32, true, nullptr, false, nullptr, nullptr, dsum, nullptr, part, rows, h,
+                             s);
+      });
+  }
+  if (dres_sum)
+    q.run("sp_dres_sum", 0, rh * rb, [&] {
+      return launch_colsum(d.bf16, 0, dres, dres_f32 != 0, nullptr, false, nullptr, nullptr, dres_sum, nullptr, part,
+                           rows, h, s);
+    });
+  return q.status();
 }
 
 int mt_adamw_step(int64_t n, float* param, const float* grad, float* exp_avg, float* exp_avg_sq, void* param_bf16,

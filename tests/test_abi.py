@@ -151,3 +151,52 @@ def test_binding_rejects_mismatched_tensors():
     w = {k: torch.zeros(v) for k, v in mt.weight_shapes(s).items()}
     with pytest.raises(ValueError):
         mt.check_layer_tensors(s, w)  # host tensors are not device buffers
+
+
+def test_attention_block_and_sp_queries(lib):
+    """Buffer queries of the attention block and the sequence-parallel row calls: the
+    attention store holds at least the projections and the context; MT_BF16_QK and a
+    sequence that does not split evenly over tp are refused (size 0)."""
+    sh = _shape(h=256, heads=4, seq=64, micro_batch=2, tp=2)
+    M, ht = 2 * 64, 256 // 2
+    assert lib.mt_attn_saved_bytes(ctypes.byref(sh)) >= M * 3 * ht * 2 + M * ht * 2
+    assert lib.mt_attn_workspace_bytes(ctypes.byref(sh)) > 0
+    assert lib.mt_sp_ln_workspace_bytes(ctypes.byref(sh)) > 0
+    qk = _shape(h=256, heads=4, seq=64, micro_batch=2, tp=2, dtype=mt.MT_BF16_QK)
+    assert lib.mt_attn_saved_bytes(ctypes.byref(qk)) == 0
+    assert lib.mt_attn_workspace_bytes(ctypes.byref(qk)) == 0
+    assert lib.mt_sp_ln_workspace_bytes(ctypes.byref(qk)) == 0
+    uneven = _shape(h=384, heads=6, seq=72, micro_batch=1, tp=3)  # 72 % 3 == 0: accepted
+    assert lib.mt_sp_ln_workspace_bytes(ctypes.byref(uneven)) > 0
+    uneven = _shape(h=256, heads=8, seq=72, micro_batch=1, tp=8)  # 72 % 8 == 0
+    assert lib.mt_sp_ln_workspace_bytes(ctypes.byref(uneven)) > 0
+    uneven = _shape(h=256, heads=16, seq=72, micro_batch=1, tp=16)  # 72 % 16 != 0
+    assert lib.mt_sp_ln_workspace_bytes(ctypes.byref(uneven)) == 0
+
+
+def test_attention_block_and_sp_reject_bad_arguments(lib):
+    """Null or misaligned pointers, small buffers, MT_BF16_QK and an uneven sequence split
+    are rejected with the documented status before anything is launched."""
+    sh = _shape(h=256, heads=4, seq=64, micro_batch=2, tp=2)
+    A = 1 << 20  # an aligned host address (never dereferenced: validation fails first)
+    big = 1 << 40
+    attn_fwd = lib.mt_attn_fwd
+    assert attn_fwd(ctypes.byref(sh), 0, A, A, A, A, A, big, A, big, None) == mt.MT_ERR_INVALID_ARG
+    assert attn_fwd(ctypes.byref(sh), A + 2, A, A, A, A, A, big, A, big, None) == mt.MT_ERR_INVALID_ARG
+    assert attn_fwd(ctypes.byref(sh), A, A, A, A, A, A, 16, A, big, None) == mt.MT_ERR_WORKSPACE
+    assert attn_fwd(ctypes.byref(sh), A, A, A, A, A, A, big, A, 16, None) == mt.MT_ERR_WORKSPACE
+    qk = _shape(h=256, heads=4, seq=64, micro_batch=2, tp=2, dtype=mt.MT_BF16_QK)
+    assert attn_fwd(ctypes.byref(qk), A, A, A, A, A, A, big, A, big, None) == mt.MT_ERR_UNSUPPORTED
+    assert lib.mt_attn_bwd(ctypes.byref(qk), A, A, A, A, big, A, A, A, A, A, A, big, None) == mt.MT_ERR_UNSUPPORTED
+    assert lib.mt_attn_bwd(ctypes.byref(sh), A, A, A, A, big, A, A, 0, A, A, A, big, None) == mt.MT_ERR_INVALID_ARG
+    # mt_sp_ln_fwd: resid given without bias / x2
+    assert lib.mt_sp_ln_fwd(ctypes.byref(sh), A, A, 0, A, A, 0, A, A, A, None) == mt.MT_ERR_INVALID_ARG
+    assert lib.mt_sp_ln_fwd(ctypes.byref(sh), A, 0, 0, A, A, 0, 0, A, A, None) == mt.MT_ERR_INVALID_ARG
+    uneven = _shape(h=256, heads=16, seq=72, micro_batch=1, tp=16)
+    assert lib.mt_sp_ln_fwd(ctypes.byref(uneven), A, 0, 0, A, A, 0, A, A, A, None) == mt.MT_ERR_INVALID_ARG
+    assert lib.mt_sp_ln_fwd(ctypes.byref(qk), A, 0, 0, A, A, 0, A, A, A, None) == mt.MT_ERR_UNSUPPORTED
+    assert lib.mt_sp_add_fwd(ctypes.byref(sh), A, A, 0, A, None) == mt.MT_ERR_INVALID_ARG
+    # mt_sp_ln_bwd: dsum without dx_f32; small workspace
+    ln_bwd = lib.mt_sp_ln_bwd
+    assert ln_bwd(ctypes.byref(sh), A, A, 1, A, A, A, A, 0, A, 0, A, A, A, 0, A, big, None) == mt.MT_ERR_INVALID_ARG
+    assert ln_bwd(ctypes.byref(sh), A, A, 1, A, A, A, A, 0, A, A, A, A, A, A, A, 4, None) == mt.MT_ERR_WORKSPACE
