@@ -132,6 +132,8 @@ def run_sp_layer_gpu(shape: si.LayerShape, x: np.ndarray, dout: np.ndarray, shar
     (512, 4, 136, 2, 2, "bf16"),   # head dim 128: fused attention; 68-token segments
     (640, 4, 264, 1, 2, "bf16"),   # head dim 160: materialised attention, ragged tiles
     (512, 8, 64, 3, 4, "bf16"),    # tp=4, head dim 64, three sequences of 16-token segments
+    (256, 2, 64, 2, 1, "bf16"),    # tp=1: the share is the whole layer
+    (384, 6, 72, 1, 3, "bf16"),    # 24-token segments: the rank's row count is not a tile multiple
 ])
 def test_sequence_parallel_share_matches_oracle(h, heads, seq, mb, tp, dtype):
     shape = si.LayerShape(h=h, heads=heads, seq=seq, micro_batch=mb, tp=tp, dtype=dtype)
