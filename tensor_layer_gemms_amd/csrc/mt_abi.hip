@@ -149,7 +149,7 @@ size_t colsum_floats(const Dims& d) {
   size_t n = colsum_partial_floats((int)d.M, (int)d.h, 1);
   n = std::max(n, colsum_partial_floats((int)d.M, (int)d.ft, 0));
   n = std::max(n, colsum_partial_floats((int)d.M, (int)d.qkv, 0));
-  if (ln_bwd_sums_supported((int)d.h)) n = std::max(n, ln_bwd_sums_partial_floats((int)d.M, (int)d.h, 3));
+  if (ln_bwd_sums_supported((int)d.h)) n = std::max(n, ln_bwd_sums_partial_floats((int)d.M, (int)d.h, 4));
   return n;
 }
 
@@ -577,11 +577,15 @@ int layer_bwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, cons
   const double Mh = (double)d.M * d.h;
   const int M = (int)d.M;
 
-  // B1 FC2: db_fc2, dW2 = dOut^T Z, dA = (dOut W2) * GeLU'(A)
-  q.run("db_fc2", 0, Mh * es, [&] {
-    return launch_colsum(bf, 0, dout, false, nullptr, false, nullptr, nullptr, gr.b_fc2, nullptr, ws.part, M,
-                         (int)d.h, stream);
-  });
+  // B1 FC2: dW2 = dOut^T Z, dA = (dOut W2) * GeLU'(A); db_fc2 = colsum(dOut) is taken by the
+  // LayerNorm-2 pass below (which reads dOut as its residual input) where the fused kernel
+  // covers h, else here
+  const bool ln_sums = ln_bwd_sums_supported((int)d.h);
+  if (!ln_sums)
+    q.run("db_fc2", 0, Mh * es, [&] {
+      return launch_colsum(bf, 0, dout, false, nullptr, false, nullptr, nullptr, gr.b_fc2, nullptr, ws.part, M,
+                           (int)d.h, stream);
+    });
   q.run("fc2_dgrad_wgrad", 2 * gflop(d.M, d.ft, d.h), 0, [&] {
     GemmArgs dg = plain(dout, d.h, w.w_fc2, d.ft, ws.da, d.ft, d.M, d.ft, d.h);
     dg.aux = sv.a;
@@ -599,13 +603,12 @@ int layer_bwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, cons
     return gemm_dgrad_wgrad(d, dg, EPI_STORE, wg, stream, ws.spart);
   });
   // B3 dX2 = dOut + LN2-backward(AR(dV2)) (written as the GEMM operand and as an fp32
-  // copy for the residual path); dgamma2, dbeta2; db_o = colsum(dX2) — in one pass over
-  // the rows where the fused kernel covers h, else as separate column sums
-  const bool ln_sums = ln_bwd_sums_supported((int)d.h);
+  // copy for the residual path); dgamma2, dbeta2; db_o = colsum(dX2); db_fc2 = colsum(dOut)
+  // — in one pass over the rows where the fused kernel covers h, else as separate column sums
   if (ln_sums) {
     q.run("ln2_bwd", 0, Mh * (3 * es + 8), [&] {
       return launch_ln_bwd_sums(bf, ws.dv2, sv.x2, true, w.ln2_g, sv.mean2, sv.rstd2, dout, false, ws.dx2, ws.dx2f,
-                                ws.part, gr.ln2_g, gr.ln2_b, gr.b_o, M, (int)d.h, stream);
+                                ws.part, gr.ln2_g, gr.ln2_b, gr.b_o, gr.b_fc2, M, (int)d.h, stream);
     });
   } else {
     q.run("ln2_bwd", 0, Mh * (3 * es + 8), [&] {
@@ -627,7 +630,7 @@ int layer_bwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, cons
   if (ln_sums) {
     q.run("ln1_bwd", 0, Mh * (3 * es + 4), [&] {
       return launch_ln_bwd_sums(bf, ws.dv2, x, false, w.ln1_g, sv.mean1, sv.rstd1, ws.dx2f, true, dx, nullptr,
-                                ws.part, gr.ln1_g, gr.ln1_b, nullptr, M, (int)d.h, stream);
+                                ws.part, gr.ln1_g, gr.ln1_b, nullptr, nullptr, M, (int)d.h, stream);
     });
   } else {
     q.run("ln1_bwd", 0, Mh * (3 * es + 4), [&] {
@@ -728,7 +731,7 @@ int validate_sp(const mt_shape* s, Dims* d, int* rows) {
 }
 size_t sp_ln_ws_floats(int rows, int h) {
   size_t n = std::max(colsum_partial_floats(rows, h, 1), colsum_partial_floats(rows, h, 0));
-  if (ln_bwd_sums_supported(h)) n = std::max(n, ln_bwd_sums_partial_floats(rows, h, 3));
+  if (ln_bwd_sums_supported(h)) n = std::max(n, ln_bwd_sums_partial_floats(rows, h, 4));
   return n;
 }
 bool null_or_aligned(const void* p) { return !p || aligned16(p); }
@@ -980,10 +983,11 @@ int mt_sp_ln_bwd(const mt_shape* shape, const void* dy, const void* xin, int xin
   const double rh = (double)rows * d.h, es = (double)d.es;
   const double xb = xin_f32 ? 4 : es, rb = dres_f32 ? 4 : es;
   Seq q(s);
-  if (ln_bwd_sums_supported(h)) {
+  const bool fused = ln_bwd_sums_supported(h);
+  if (fused) {  // dres_sum rides along (or follows as a column sum inside the same call)
     q.run("sp_ln_bwd", 0, rh * (es + xb + rb + es + (dx_f32 ? 4 : 0)), [&] {
       return launch_ln_bwd_sums(d.bf16, dy, xin, xin_f32 != 0, gamma, mean, rstd, dres, dres_f32 != 0, dx, dx_f32,
-                                part, dgamma, dbeta, dsum, rows, h, s);
+                                part, dgamma, dbeta, dsum, dres_sum, rows, h, s);
     });
   } else {
     q.run("sp_ln_bwd", 0, rh * (es + xb + rb + es + (dx_f32 ? 4 : 0)), [&] {
@@ -999,7 +1003,7 @@ int mt_sp_ln_bwd(const mt_shape* shape, const void* dy, const void* xin, int xin
                              s);
       });
   }
-  if (dres_sum)
+  if (dres_sum && !fused)
     q.run("sp_dres_sum", 0, rh * rb, [&] {
       return launch_colsum(d.bf16, 0, dres, dres_f32 != 0, nullptr, false, nullptr, nullptr, dres_sum, nullptr, part,
                            rows, h, s);

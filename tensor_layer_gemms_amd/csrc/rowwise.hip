@@ -2,6 +2,8 @@
 // vectors along the contiguous hidden dimension and reduces with wavefront shuffles
 // plus one LDS exchange per block; reductions have a fixed order (no atomics), so the
 // results are bitwise reproducible.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "rowwise.hpp"
 
@@ -139,11 +141,13 @@ __global__ __launch_bounds__(kLnThreads) void ln_bwd_kernel(const T* __restrict_
 
 // LayerNorm backward fused with its column reductions. A block walks `rpb` consecutive
 // rows (the row math is ln_bwd_kernel's) and keeps, per thread and column, the sums
-// over its rows of dy * xhat (d gamma), dy (d beta) and, with NS = 3, dx (the bias
-// gradient of the sublayer whose output dx is); it writes them as one partial row per
-// sum and block, which colsum_final_kernel adds in a fixed order. The rows' inputs are
-// read once, where separate column-sum launches would read dy, x and dx again.
-template <typename T, typename TX, typename TR, int CPT, int NS>
+// over its rows of dy * xhat (d gamma), dy (d beta), with DSUM dx (the bias gradient of
+// the sublayer whose output dx is) and with RSUM the residual input resid (the bias
+// gradient of the sublayer whose output gradient resid is: dOut for LayerNorm 2); it
+// writes them as one partial row per sum and block, which colsum_final_kernel adds in a
+// fixed order. The rows' inputs are read once, where separate column-sum launches would
+// read dy, x, dx and resid again.
+template <typename T, typename TX, typename TR, int CPT, bool DSUM, bool RSUM>
 __global__ __launch_bounds__(kLnThreads) void ln_bwd_sums_kernel(const T* __restrict__ dy, const TX* __restrict__ x,
                                                                  const T* __restrict__ gamma,
                                                                  const float* __restrict__ mean,
@@ -152,6 +156,7 @@ __global__ __launch_bounds__(kLnThreads) void ln_bwd_sums_kernel(const T* __rest
                                                                  float* __restrict__ dxf, float* __restrict__ part,
                                                                  int rows, int h, int rpb) {
   constexpr int NW = kLnThreads / 64;
+  constexpr int NS = 2 + (DSUM ? 1 : 0) + (RSUM ? 1 : 0);
   __shared__ float red[2 * NW];
   const int nch = h / 8;
   const int r0 = blockIdx.x * rpb, r1 = min(rows, r0 + rpb);
@@ -181,6 +186,7 @@ __global__ __launch_bounds__(kLnThreads) void ln_bwd_sums_kernel(const T* __rest
           xh[c][e] = (xh[c][e] - mu) * rs;
           acc[0][c][e] += g[c][e] * xh[c][e];
           acc[1][c][e] += g[c][e];
+          if constexpr (RSUM) acc[NS - 1][c][e] += rv[c][e];
           g[c][e] *= gv[e];
           s[0] += g[c][e];
           s[1] += g[c][e] * xh[c][e];
@@ -199,7 +205,7 @@ __global__ __launch_bounds__(kLnThreads) void ln_bwd_sums_kernel(const T* __rest
         for (int e = 0; e < 8; ++e) out[e] = rv[c][e] + rs * (g[c][e] - mg - xh[c][e] * mgx);
         store8(dx + off, out);
         if (dxf) store8(dxf + off, out);
-        if constexpr (NS == 3) {
+        if constexpr (DSUM) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) acc[2][c][e] += out[e];
         }
@@ -271,17 +277,17 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(const TA* __restric
   }
 }
 
-// Stage 2: sum the row-slab partials of `nsum` (1 to 3) column sums, partial k of slab b
+// Stage 2: sum the row-slab partials of `nsum` (1 to 4) column sums, partial k of slab b
 // at part[(k nrb + b) cols + c]. Block: 64 columns x 4 slab groups; group g sums slabs
 // g, g + 4, ... in four interleaved chains (independent loads in flight), then the groups
 // are added in a fixed order. The order depends on the geometry only.
 __global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restrict__ part, float* __restrict__ out0,
                                                            float* __restrict__ out1, float* __restrict__ out2,
-                                                           int nrb, int cols, int nsum) {
-  __shared__ float red[3][4][64];
+                                                           float* __restrict__ out3, int nrb, int cols, int nsum) {
+  __shared__ float red[4][4][64];
   const int lane = threadIdx.x & 63, grp = threadIdx.x >> 6;
   const int c = blockIdx.x * 64 + lane;
-  float s[3] = {0.f, 0.f, 0.f};
+  float s[4] = {0.f, 0.f, 0.f, 0.f};
   if (c < cols) {
     for (int k = 0; k < nsum; ++k) {
       const float* p = part + (int64_t)k * nrb * cols + c;
@@ -298,10 +304,10 @@ __global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restri
     }
   }
 #pragma unroll
-  for (int k = 0; k < 3; ++k) red[k][grp][lane] = s[k];
+  for (int k = 0; k < 4; ++k) red[k][grp][lane] = s[k];
   __syncthreads();
   if (grp == 0 && c < cols) {
-    float* outs[3] = {out0, out1, out2};
+    float* outs[4] = {out0, out1, out2, out3};
     for (int k = 0; k < nsum; ++k)
       outs[k][c] = (red[k][0][lane] + red[k][1][lane]) + (red[k][2][lane] + red[k][3][lane]);
   }
@@ -512,31 +518,50 @@ int ln_sums_rpb(int rows) { return rows <= 256 ? 1 : (rows + 255) / 256; }
 template <typename T, typename TX, typename TR, int CPT>
 hipError_t ln_bwd_sums_launch(const void* dy, const void* x, const void* gamma, const float* mean, const float* rstd,
                               const void* resid, void* dx, float* dxf, float* part, float* dgamma, float* dbeta,
-                              float* dsum, int rows, int h, hipStream_t s) {
+                              float* dsum, float* rsum, int rows, int h, hipStream_t s) {
   const int rpb = ln_sums_rpb(rows), nblk = (rows + rpb - 1) / rpb;
-  if (dsum)
-    hipLaunchKernelGGL((ln_bwd_sums_kernel<T, TX, TR, CPT, 3>), dim3(nblk), dim3(kLnThreads), 0, s, (const T*)dy,
-                       (const TX*)x, (const T*)gamma, mean, rstd, (const TR*)resid, (T*)dx, dxf, part, rows, h, rpb);
-  else
-    hipLaunchKernelGGL((ln_bwd_sums_kernel<T, TX, TR, CPT, 2>), dim3(nblk), dim3(kLnThreads), 0, s, (const T*)dy,
-                       (const TX*)x, (const T*)gamma, mean, rstd, (const TR*)resid, (T*)dx, dxf, part, rows, h, rpb);
+  // The residual's column sum rides along up to 3 chunks per thread (h <= 12288); with 4
+  // its accumulators would spill, and it runs as a separate column sum after the pass.
+  constexpr bool kFuseR = CPT <= 3;
+  const bool fr = kFuseR && rsum != nullptr;
+  auto go = [&](auto dflag, auto rflag) {
+    hipLaunchKernelGGL((ln_bwd_sums_kernel<T, TX, TR, CPT, decltype(dflag)::value, decltype(rflag)::value>),
+                       dim3(nblk), dim3(kLnThreads), 0, s, (const T*)dy, (const TX*)x, (const T*)gamma, mean, rstd,
+                       (const TR*)resid, (T*)dx, dxf, part, rows, h, rpb);
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  if constexpr (kFuseR) {
+    if (dsum && fr) go(T_{}, T_{});
+    else if (dsum) go(T_{}, F_{});
+    else if (fr) go(F_{}, T_{});
+    else go(F_{}, F_{});
+  } else {
+    if (dsum) go(T_{}, F_{});
+    else go(F_{}, F_{});
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(colsum_final_kernel, dim3((h + 63) / 64), dim3(256), 0, s, part, dgamma, dbeta, dsum, nblk, h,
-                     dsum ? 3 : 2);
-  return hipGetLastError();
+  float* out2 = dsum ? dsum : (fr ? rsum : nullptr);
+  float* out3 = dsum && fr ? rsum : nullptr;
+  hipLaunchKernelGGL(colsum_final_kernel, dim3((h + 63) / 64), dim3(256), 0, s, part, dgamma, dbeta, out2, out3, nblk,
+                     h, 2 + (dsum ? 1 : 0) + (fr ? 1 : 0));
+  e = hipGetLastError();
+  if (e != hipSuccess || !rsum || fr) return e;
+  return launch_colsum(std::is_same<T, bf16>::value, 0, resid, std::is_same<TR, float>::value, nullptr, false, nullptr,
+                       nullptr, rsum, nullptr, part, rows, h, s);
 }
 
 template <typename T, typename TX, typename TR>
 hipError_t ln_bwd_sums_t(const void* dy, const void* x, const void* gamma, const float* mean, const float* rstd,
                          const void* resid, void* dx, float* dxf, float* part, float* dgamma, float* dbeta, float* dsum,
-                         int rows, int h, hipStream_t s) {
+                         float* rsum, int rows, int h, hipStream_t s) {
   const int need = (h / 8 + kLnThreads - 1) / kLnThreads;
   switch (need) {
-    case 1: return ln_bwd_sums_launch<T, TX, TR, 1>(dy, x, gamma, mean, rstd, resid, dx, dxf, part, dgamma, dbeta, dsum, rows, h, s);
-    case 2: return ln_bwd_sums_launch<T, TX, TR, 2>(dy, x, gamma, mean, rstd, resid, dx, dxf, part, dgamma, dbeta, dsum, rows, h, s);
-    case 3: return ln_bwd_sums_launch<T, TX, TR, 3>(dy, x, gamma, mean, rstd, resid, dx, dxf, part, dgamma, dbeta, dsum, rows, h, s);
-    case 4: return ln_bwd_sums_launch<T, TX, TR, 4>(dy, x, gamma, mean, rstd, resid, dx, dxf, part, dgamma, dbeta, dsum, rows, h, s);
+    case 1: return ln_bwd_sums_launch<T, TX, TR, 1>(dy, x, gamma, mean, rstd, resid, dx, dxf, part, dgamma, dbeta, dsum, rsum, rows, h, s);
+    case 2: return ln_bwd_sums_launch<T, TX, TR, 2>(dy, x, gamma, mean, rstd, resid, dx, dxf, part, dgamma, dbeta, dsum, rsum, rows, h, s);
+    case 3: return ln_bwd_sums_launch<T, TX, TR, 3>(dy, x, gamma, mean, rstd, resid, dx, dxf, part, dgamma, dbeta, dsum, rsum, rows, h, s);
+    case 4: return ln_bwd_sums_launch<T, TX, TR, 4>(dy, x, gamma, mean, rstd, resid, dx, dxf, part, dgamma, dbeta, dsum, rsum, rows, h, s);
     default: return hipErrorNotSupported;
   }
 }
@@ -544,16 +569,18 @@ hipError_t ln_bwd_sums_t(const void* dy, const void* x, const void* gamma, const
 template <typename T>
 hipError_t ln_bwd_sums_dispatch(const void* dy, const void* x, bool x_f32, const void* gamma, const float* mean,
                                 const float* rstd, const void* resid, bool resid_f32, void* dx, float* dxf,
-                                float* part, float* dgamma, float* dbeta, float* dsum, int rows, int h,
+                                float* part, float* dgamma, float* dbeta, float* dsum, float* rsum, int rows, int h,
                                 hipStream_t s) {
   if (x_f32 && !resid_f32)
-    return ln_bwd_sums_t<T, float, T>(dy, x, gamma, mean, rstd, resid, dx, dxf, part, dgamma, dbeta, dsum, rows, h, s);
+    return ln_bwd_sums_t<T, float, T>(dy, x, gamma, mean, rstd, resid, dx, dxf, part, dgamma, dbeta, dsum, rsum, rows,
+                                      h, s);
   if (!x_f32 && resid_f32)
-    return ln_bwd_sums_t<T, T, float>(dy, x, gamma, mean, rstd, resid, dx, dxf, part, dgamma, dbeta, dsum, rows, h, s);
+    return ln_bwd_sums_t<T, T, float>(dy, x, gamma, mean, rstd, resid, dx, dxf, part, dgamma, dbeta, dsum, rsum, rows,
+                                      h, s);
   if (x_f32 && resid_f32)
-    return ln_bwd_sums_t<T, float, float>(dy, x, gamma, mean, rstd, resid, dx, dxf, part, dgamma, dbeta, dsum, rows,
-                                          h, s);
-  return ln_bwd_sums_t<T, T, T>(dy, x, gamma, mean, rstd, resid, dx, dxf, part, dgamma, dbeta, dsum, rows, h, s);
+    return ln_bwd_sums_t<T, float, float>(dy, x, gamma, mean, rstd, resid, dx, dxf, part, dgamma, dbeta, dsum, rsum,
+                                          rows, h, s);
+  return ln_bwd_sums_t<T, T, T>(dy, x, gamma, mean, rstd, resid, dx, dxf, part, dgamma, dbeta, dsum, rsum, rows, h, s);
 }
 
 template <typename TA, typename TX>
@@ -569,8 +596,8 @@ hipError_t colsum_t(int mode, const void* a, const void* x, const float* mean, c
                        (const TX*)x, mean, rstd, partial, rows, cols, rpb, nrb);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(colsum_final_kernel, dim3((cols + 63) / 64), dim3(256), 0, s, partial, out0, out1, nullptr, nrb,
-                     cols, mode == 1 ? 2 : 1);
+  hipLaunchKernelGGL(colsum_final_kernel, dim3((cols + 63) / 64), dim3(256), 0, s, partial, out0, out1, nullptr,
+                     nullptr, nrb, cols, mode == 1 ? 2 : 1);
   return hipGetLastError();
 }
 
@@ -623,14 +650,14 @@ size_t ln_bwd_sums_partial_floats(int rows, int h, int nsum) {
 
 hipError_t launch_ln_bwd_sums(bool is_bf16, const void* dy, const void* x, bool x_f32, const void* gamma,
                               const float* mean, const float* rstd, const void* resid, bool resid_f32, void* dx,
-                              float* dx_f32, float* part, float* dgamma, float* dbeta, float* dsum, int rows, int h,
-                              hipStream_t s) {
+                              float* dx_f32, float* part, float* dgamma, float* dbeta, float* dsum, float* rsum,
+                              int rows, int h, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   if (!ln_bwd_sums_supported(h)) return hipErrorNotSupported;
   return is_bf16 ? ln_bwd_sums_dispatch<bf16>(dy, x, x_f32, gamma, mean, rstd, resid, resid_f32, dx, dx_f32, part,
-                                              dgamma, dbeta, dsum, rows, h, s)
+                                              dgamma, dbeta, dsum, rsum, rows, h, s)
                  : ln_bwd_sums_dispatch<float>(dy, x, x_f32, gamma, mean, rstd, resid, resid_f32, dx, dx_f32, part,
-                                               dgamma, dbeta, dsum, rows, h, s);
+                                               dgamma, dbeta, dsum, rsum, rows, h, s);
 }
 
 size_t colsum_partial_floats(int rows, int cols, int mode) {

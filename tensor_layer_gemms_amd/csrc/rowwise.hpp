@@ -35,16 +35,17 @@ hipError_t launch_ln_bwd(bool is_bf16, const void* dy, const void* x, bool x_f32
                          float* dx_f32, int rows, int h, hipStream_t s);
 
 // LayerNorm backward (as launch_ln_bwd) fused with its column sums: dgamma[c] =
-// sum_r dy[r, c] xhat[r, c], dbeta[c] = sum_r dy[r, c] and, when dsum is not null,
-// dsum[c] = sum_r dx[r, c] (the fp32 values before rounding). `part` holds
-// ln_bwd_sums_partial_floats(rows, h, dsum ? 3 : 2) floats; fixed reduction order.
+// sum_r dy[r, c] xhat[r, c], dbeta[c] = sum_r dy[r, c], when dsum is not null
+// dsum[c] = sum_r dx[r, c] (the fp32 values before rounding) and when rsum is not null
+// rsum[c] = sum_r resid[r, c]. `part` holds ln_bwd_sums_partial_floats(rows, h, 4) floats
+// (and at least colsum_partial_floats(rows, h, 0)); fixed reduction order.
 // Supported when ln_bwd_sums_supported(h) (h / 8 chunks over at most 4 per thread).
 bool ln_bwd_sums_supported(int h);
 size_t ln_bwd_sums_partial_floats(int rows, int h, int nsum);
 hipError_t launch_ln_bwd_sums(bool is_bf16, const void* dy, const void* x, bool x_f32, const void* gamma,
                               const float* mean, const float* rstd, const void* resid, bool resid_f32, void* dx,
-                              float* dx_f32, float* part, float* dgamma, float* dbeta, float* dsum, int rows, int h,
-                              hipStream_t s);
+                              float* dx_f32, float* part, float* dgamma, float* dbeta, float* dsum, float* rsum,
+                              int rows, int h, hipStream_t s);
 
 // Column sums over `rows` rows, deterministic two-stage reduction through `partial`.
 // mode 0: out0[c] = sum_r a[r, c].
