@@ -256,8 +256,8 @@ def main():
         copy_probe(args.copy_probe)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the tensor-parallel "
-              "all-reduce is not part of it. Run with --gpus 1.", file=sys.stderr)
+        print(f"bench.py: measures one GPU's tensor-parallel shard only (asked for --gpus {args.gpus}); the "
+              "tensor-parallel all-reduce is not part of it. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -10,7 +10,7 @@ tensor-parallel blocks) need the whole sequence. Section 6.4: each device then h
 S/tp of the sequence, so its activations shrink to 1/tp. Section 8(1): the
 tensor-parallel all-reduce is carried out as a reduce-scatter and an all-gather.
 
-Readings where the pages leave the step open (stated in the design doc as well):
+Readings where the pages leave the step open:
   - Rank i owns positions [i s/t, (i+1) s/t) of every sequence of the micro-batch; its
     rows are kept in (sequence, position) order.
   - All-gather before each tensor-parallel block (of the LayerNorm output, and in the
