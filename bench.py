@@ -172,7 +172,9 @@ def sp_share(mt, si, torch, shape, w, x, dout, stream, warmup: int = 3, iters: i
     n = M // shape.tp
     act = torch.bfloat16
     f32 = dict(dtype=torch.float32, device="cuda")
-    U, V2, dOut, dX2 = (torch.randn(M, h, device="cuda").to(act) for _ in range(4))
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1)  # seeded synthetic rows standing for the other ranks
+    U, V2, dOut, dX2 = (torch.randn(M, h, device="cuda", generator=gen).to(act) for _ in range(4))
     O, Y, dV2, dU = (torch.empty(M, h, dtype=act, device="cuda") for _ in range(4))
     xi, douti = x[:n], dout[:n]
     x2, dx2f = torch.empty(n, h, **f32), torch.empty(n, h, **f32)
