@@ -78,6 +78,60 @@ def test_mlp_shards_sum_to_unsharded_block(dtype, tp):
         assert compare(f"dW2[{i}]", gr["w_fc2"], g_ref[0]["w_fc2"][:, i * fs:(i + 1) * fs], tol, nw)[0]
 
 
+def _run_attn_gpu(shape, u, d_o, p):
+    """mt_attn_fwd + mt_attn_bwd of one shard; returns (o_partial, du_partial, grads)."""
+    import torch
+    import tensor_layer_gemms_amd as mt
+    from gpu_support import mt_shape, to_dev, to_np
+    sh = mt_shape(shape)
+    dt = shape.dtype
+    ud, dod = to_dev(u, dt), to_dev(d_o, dt)
+    wq, bq, wo = to_dev(p["w_qkv"], dt), to_dev(p["b_qkv"], dt), to_dev(p["w_o"], dt)
+    ht = shape.h // shape.tp
+    assert wq.shape == (3 * ht, shape.h) and wo.shape == (shape.h, ht) and ud.shape == (shape.tokens, shape.h)
+    saved = torch.empty(mt.attn_saved_bytes(sh), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(mt.attn_workspace_bytes(sh), dtype=torch.uint8, device="cuda")
+    o, du = torch.empty_like(ud), torch.empty_like(ud)
+    g = {k: torch.empty(p[k].shape, dtype=torch.float32, device="cuda") for k in ("w_qkv", "b_qkv", "w_o")}
+    mt.attn_fwd(sh, ud, wq, bq, wo, o, saved, ws)
+    mt.attn_bwd(sh, ud, wq, wo, saved, dod, du, g["w_qkv"], g["b_qkv"], g["w_o"], ws)
+    torch.cuda.synchronize()
+    return to_np(o), to_np(du), {k: to_np(v) for k, v in g.items()}
+
+
+@pytest.mark.parametrize("dtype,tp,h,heads,seq,mb", [
+    ("fp32", 2, 64, 4, 32, 2),       # unfused attention, literal 1e-4 bar
+    ("bf16", 2, 512, 4, 136, 2),     # head dim 128: fused attention
+    ("bf16", 4, 512, 8, 72, 3),      # head dim 64, three sequences
+    ("bf16", 2, 640, 4, 104, 1),     # head dim 160: materialised attention
+])
+def test_attn_shards_sum_to_unsharded_block(dtype, tp, h, heads, seq, mb):
+    """The pages' head-parallel split on the GPU: every shard of the attention block
+    (mt_attn_*) run in turn on one device; the sum of the output partials and of the
+    input-gradient partials against the unsharded oracle block, and each shard's weight
+    gradients against the matching slice of the unsharded ones."""
+    from gpu_support import compare
+    shape = si.LayerShape(h=h, heads=heads, seq=seq, micro_batch=mb, tp=tp, dtype=dtype)
+    log(f"[attn block] {dtype} tp={tp} h={h} heads={heads} seq={seq} micro_batch={mb}")
+    case = si.make_case(shape.replace(tp=1), seed=h + tp, global_weights=True, random_affine=True)
+    g = case.global_layers[0]
+    o_ref, c = oracle.attn_block_fwd(case.x, g, mb, seq, shape.head_dim)
+    du_ref, g_ref = oracle.attn_block_bwd(case.dout, c, g)
+    o_sum = du_sum = 0.0
+    tol, nw = TOL[dtype], dtype == "bf16"
+    ok = True
+    for i in range(tp):
+        p = si.shard_slice(g, shape, i)
+        o, du, gr = _run_attn_gpu(shape.replace(shard=i), case.x, case.dout, p)
+        o_sum, du_sum = o_sum + o, du_sum + du
+        want = si.shard_slice(dict(g, **g_ref), shape, i)
+        for k in ("w_qkv", "b_qkv", "w_o"):
+            ok &= compare(f"{k}[{i}]", gr[k], want[k], tol, nw)[0]
+    ok &= compare("sum o", o_sum, o_ref, tol, nw)[0]
+    ok &= compare("sum du", du_sum, du_ref, tol, nw)[0]
+    assert ok
+
+
 @pytest.mark.parametrize("h,heads,seq,mb,tp,shard", [
     (320, 5, 136, 3, 1, 0),    # several tiles, ragged token and feature tails
     (640, 4, 264, 1, 2, 1),    # head dim 160, shard 1 of 2, ragged seq
