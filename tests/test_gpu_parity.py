@@ -165,6 +165,20 @@ def test_qk_pairs_lower_the_logit_error():
     assert not bad, bad
 
 
+@pytest.mark.parametrize("h,heads,seq,mb,tp,shard,dtype", [
+    (64, 4, 8, 1, 4, 3, "fp32"),     # 8 tokens, one head (of 16) per shard, last shard
+    (128, 2, 8, 1, 2, 1, "bf16"),    # one head of 64 per shard: fused attention on an 8-row block
+    (256, 2, 8, 3, 2, 0, "bf16"),    # head dim 128, three 8-token sequences in one row block each
+    (512, 4, 16, 2, 1, 0, "bf16"),   # tp = 1, two 16-token sequences
+])
+def test_layer_degenerate_shapes(h, heads, seq, mb, tp, shard, dtype):
+    """The smallest sequences the ABI accepts (a fraction of one attention block), one head
+    per shard, and tp = 1: every output and gradient against the oracle."""
+    shape = si.LayerShape(h=h, heads=heads, seq=seq, micro_batch=mb, tp=tp, shard=shard, dtype=dtype)
+    case = _layer_case(shape, seed=seq + h, random_affine=True)
+    _check_layer(shape, case)
+
+
 def test_layer_fp32_multi_tile():
     shape = si.LayerShape(h=192, heads=3, seq=200, micro_batch=2, tp=1, dtype="fp32")
     _check_layer(shape, _layer_case(shape, seed=3, random_affine=True))
