@@ -278,40 +278,47 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(const TA* __restric
 }
 
 // Stage 2: sum the row-slab partials of `nsum` (1 to 4) column sums, partial k of slab b
-// at part[(k nrb + b) cols + c]. Block: 64 columns x 4 slab groups; group g sums slabs
-// g, g + 4, ... in four interleaved chains (independent loads in flight), then the groups
-// are added in a fixed order. The order depends on the geometry only.
-__global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restrict__ part, float* __restrict__ out0,
-                                                           float* __restrict__ out1, float* __restrict__ out2,
-                                                           float* __restrict__ out3, int nrb, int cols, int nsum) {
-  __shared__ float red[4][4][64];
-  const int lane = threadIdx.x & 63, grp = threadIdx.x >> 6;
-  const int c = blockIdx.x * 64 + lane;
-  float s[4] = {0.f, 0.f, 0.f, 0.f};
-  if (c < cols) {
-    for (int k = 0; k < nsum; ++k) {
-      const float* p = part + (int64_t)k * nrb * cols + c;
-      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-      int b = grp;
-      for (; b + 12 < nrb; b += 16) {
-        a0 += p[(int64_t)b * cols];
-        a1 += p[(int64_t)(b + 4) * cols];
-        a2 += p[(int64_t)(b + 8) * cols];
-        a3 += p[(int64_t)(b + 12) * cols];
-      }
-      for (; b < nrb; b += 4) a0 += p[(int64_t)b * cols];
-      s[k] = (a0 + a1) + (a2 + a3);
-    }
-  }
+// at part[(k nrb + b) cols + c] (cols a multiple of 4, 16-byte aligned rows). A block owns
+// 256 columns of one sum, 4 per lane (16-byte loads); its 16 waves take slabs w, w + 16,
+// ..., in eight interleaved chains (eight loads in flight per lane: the pass is bound by
+// load latency, not bandwidth), then the waves' sums are added in wave order. The order
+// depends on the geometry only.
+constexpr int kFinalWaves = 16;
+__global__ __launch_bounds__(64 * kFinalWaves) void colsum_final_kernel(const float* __restrict__ part,
+                                                                        float* __restrict__ out0,
+                                                                        float* __restrict__ out1,
+                                                                        float* __restrict__ out2,
+                                                                        float* __restrict__ out3, int nrb, int cols) {
+  constexpr int W = kFinalWaves;
+  __shared__ f32x4 red[W][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int k = blockIdx.y;
+  const int c = (blockIdx.x * 64 + lane) * 4;
+  f32x4 acc[8];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) red[k][grp][lane] = s[k];
+  for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (c < cols) {
+    const float* p = part + (int64_t)k * nrb * cols + c;
+    int b = w;
+    for (; b + 7 * W < nrb; b += 8 * W) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] += *reinterpret_cast<const f32x4*>(p + (int64_t)(b + j * W) * cols);
+    }
+    for (; b < nrb; b += W) acc[0] += *reinterpret_cast<const f32x4*>(p + (int64_t)b * cols);
+  }
+  red[w][lane] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
   __syncthreads();
-  if (grp == 0 && c < cols) {
-    float* outs[4] = {out0, out1, out2, out3};
-    for (int k = 0; k < nsum; ++k)
-      outs[k][c] = (red[k][0][lane] + red[k][1][lane]) + (red[k][2][lane] + red[k][3][lane]);
+  if (w == 0 && c < cols) {
+    f32x4 t = red[0][lane];
+#pragma unroll
+    for (int i = 1; i < W; ++i) t += red[i][lane];
+    float* out = k == 0 ? out0 : k == 1 ? out1 : k == 2 ? out2 : out3;
+    *reinterpret_cast<f32x4*>(out + c) = t;
   }
 }
+
+// Grid of colsum_final_kernel: 256 columns per block along x, one sum per y.
+dim3 colsum_final_grid(int cols, int nsum) { return dim3((unsigned)((cols / 4 + 63) / 64), (unsigned)nsum); }
 
 // ------------------------------------------------------------------ bias + residual
 template <typename T>
@@ -426,25 +433,36 @@ __global__ __launch_bounds__(256) void softmax_causal_kernel(const float* __rest
 }
 
 // ------------------------------------------------------------------ attention row dot
+// D[b, k, q] = sum_c dctx[r, k, c] ctx[r, k, c], r = b seq + q. The (row, head) pairs are
+// the rows of a contiguous [rows * heads, d] matrix; 16 lanes share a pair, each summing
+// its 16-byte chunks c = lane, lane + 16, ..., so a wave reads 4 pairs' elements
+// contiguously; the 16 lanes' sums are added by shuffles in a fixed order.
 template <typename T>
 __global__ __launch_bounds__(256) void attn_rowdot_kernel(const T* __restrict__ dctx, const T* __restrict__ ctx,
                                                           float* __restrict__ D, int64_t nrows, int seq, int heads,
                                                           int d) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= nrows * heads) return;
-  const int64_t r = t / heads;
-  const int k = (int)(t % heads);
-  const int64_t base = r * (int64_t)heads * d + (int64_t)k * d;
+  const int64_t t = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
+  const int sub = threadIdx.x & 15;
+  const bool ok = t < nrows * heads;  // no early exit: every lane takes part in the shuffles
   float s = 0.f;
-  for (int c = 0; c < d; c += 8) {
-    float a[8], b[8];
-    load8(dctx + base + c, a);
-    load8(ctx + base + c, b);
+  if (ok) {
+    const int64_t base = t * d;
+    for (int c = sub * 8; c < d; c += 128) {
+      float a[8], b[8];
+      load8(dctx + base + c, a);
+      load8(ctx + base + c, b);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s += a[e] * b[e];
+      for (int e = 0; e < 8; ++e) s += a[e] * b[e];
+    }
   }
-  const int64_t b = r / seq, q = r % seq;
-  D[(b * heads + k) * seq + q] = s;
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+  if (ok && sub == 0) {
+    const int64_t r = t / heads;
+    const int k = (int)(t % heads);
+    const int64_t b = r / seq, q = r % seq;
+    D[(b * heads + k) * seq + q] = s;
+  }
 }
 
 int ln_cpt(int h) {
@@ -544,8 +562,8 @@ hipError_t ln_bwd_sums_launch(const void* dy, const void* x, const void* gamma, 
   if (e != hipSuccess) return e;
   float* out2 = dsum ? dsum : (fr ? rsum : nullptr);
   float* out3 = dsum && fr ? rsum : nullptr;
-  hipLaunchKernelGGL(colsum_final_kernel, dim3((h + 63) / 64), dim3(256), 0, s, part, dgamma, dbeta, out2, out3, nblk,
-                     h, 2 + (dsum ? 1 : 0) + (fr ? 1 : 0));
+  hipLaunchKernelGGL(colsum_final_kernel, colsum_final_grid(h, 2 + (dsum ? 1 : 0) + (fr ? 1 : 0)),
+                     dim3(64 * kFinalWaves), 0, s, part, dgamma, dbeta, out2, out3, nblk, h);
   e = hipGetLastError();
   if (e != hipSuccess || !rsum || fr) return e;
   return launch_colsum(std::is_same<T, bf16>::value, 0, resid, std::is_same<TR, float>::value, nullptr, false, nullptr,
@@ -596,8 +614,8 @@ hipError_t colsum_t(int mode, const void* a, const void* x, const float* mean, c
                        (const TX*)x, mean, rstd, partial, rows, cols, rpb, nrb);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(colsum_final_kernel, dim3((cols + 63) / 64), dim3(256), 0, s, partial, out0, out1, nullptr,
-                     nullptr, nrb, cols, mode == 1 ? 2 : 1);
+  hipLaunchKernelGGL(colsum_final_kernel, colsum_final_grid(cols, mode == 1 ? 2 : 1), dim3(64 * kFinalWaves), 0, s,
+                     partial, out0, out1, nullptr, nullptr, nrb, cols);
   return hipGetLastError();
 }
 
@@ -670,6 +688,7 @@ hipError_t launch_colsum(bool is_bf16, int mode, const void* a, bool a_f32, cons
                          const float* mean, const float* rstd, float* out0, float* out1, float* partial, int rows,
                          int cols, hipStream_t s) {
   if (cols <= 0) return hipSuccess;
+  if (cols % 8 != 0) return hipErrorInvalidValue;  // 8-column chunks in both passes
   if (!is_bf16 || (a_f32 && (mode == 0 || x_f32)))
     return colsum_t<float, float>(mode, a, x, mean, rstd, out0, out1, partial, rows, cols, s);
   if (a_f32) return colsum_t<float, bf16>(mode, a, x, mean, rstd, out0, out1, partial, rows, cols, s);
@@ -711,7 +730,7 @@ hipError_t launch_attn_rowdot(bool is_bf16, const void* dctx, const void* ctx, f
   const int64_t nrows = (int64_t)batch * seq;
   const int64_t n = nrows * heads;
   if (n <= 0) return hipSuccess;
-  const dim3 grid((unsigned)((n + 255) / 256));
+  const dim3 grid((unsigned)((n + 15) / 16));  // 16 lanes per (row, head)
   if (is_bf16)
     hipLaunchKernelGGL(attn_rowdot_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)dctx, (const bf16*)ctx, D, nrows,
                        seq, heads, d);
