@@ -7,8 +7,8 @@ shard 0 of tp=8 (h=12288, 12 of 96 heads of 128, seq 2048, micro-batch 1, bf16).
 
 Reported (one JSON line): model TFLOP/s = 3 x (forward GEMM + causal attention FLOPs)
 per step / step time, its fraction of the MI355X dense bf16 MFMA peak, the roofline
-of the dominant kernel (timed live with HIP events on the library's stream around
-that kernel's launches inside the timed steps), the fp64 oracle timed on the host, and
+of the dominant kernel (the step's largest launch, the FC2 backward pair; timed live
+with HIP events on the library's stream around that launch inside the timed steps), the fp64 oracle timed on the host, and
 (outside the timed steps) the fused AdamW step over the shard's parameters against HBM
 bandwidth.
 """
@@ -26,9 +26,13 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 METRIC = "model TFLOP/s per GPU, GPT layer-shard fwd+bwd; % of bf16 MFMA peak"
-# HBM traffic of the dominant kernel, measured with rocprofv3 counters and committed as a
-# summary; it is reported only while the GEMM sources hash to the value recorded there.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fc1_fwd_gpt175b_tp8_traffic.txt")
+# HBM traffic of the reported kernel launch, measured with rocprofv3 counters and committed
+# as a summary per launch label; it is reported only while the GEMM sources hash to the
+# value recorded there.
+def traffic_file(label: str) -> str:
+    return os.path.join(ROOT, "profiles", f"{label}_gpt175b_tp8_traffic.txt")
+
+
 GEMM_SOURCES = ["tensor_layer_gemms_amd/csrc/gemm_dma.hpp", "tensor_layer_gemms_amd/csrc/gemm_kernels.hpp",
                 "tensor_layer_gemms_amd/csrc/gemm_bf16.hip", "tensor_layer_gemms_amd/csrc/gemm.hpp",
                 "tensor_layer_gemms_amd/csrc/device_common.hpp"]
@@ -48,7 +52,7 @@ def committed_traffic(kernel: str):
     summary is missing, is for another kernel, or predates the current GEMM sources."""
     try:
         kv = {}
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(kernel)) as f:
             for line in f:
                 if ":" in line and not line.startswith("#"):
                     k, v = line.split(":", 1)
@@ -66,8 +70,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gpt175b_tp8")
-    ap.add_argument("--dominant", default="fc1_fwd",
-                    help="label of the kernel launch whose roofline is reported")
+    ap.add_argument("--dominant", default="fc2_dgrad_wgrad",
+                    help="label of the kernel launch whose roofline is reported (default: the step's largest "
+                         "launch, the FC2 backward dgrad + wgrad pair)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-optimizer", action="store_true", help="skip the fused AdamW step measurement")
     ap.add_argument("--no-sp", action="store_true", help="skip the sequence-parallel share measurement")
