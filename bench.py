@@ -8,15 +8,22 @@ shard 0 of tp=8 (h=12288, 12 of 96 heads of 128, seq 2048, micro-batch 1, bf16).
 Reported (one JSON line): model TFLOP/s = 3 x (forward GEMM + causal attention FLOPs)
 per step / step time, its fraction of the MI355X dense bf16 MFMA peak, the roofline
 of the dominant kernel (the step's largest launch, the FC2 backward pair; timed live
-with HIP events on the library's stream around that launch inside the timed steps), the fp64 oracle timed on the host, and
-(outside the timed steps) the fused AdamW step over the shard's parameters against HBM
-bandwidth.
+with HIP events that the library records on its stream around that launch, in a pass of
+further steps after the headline ones), the graphics clock sampled while steps run, the
+fp64 oracle timed on the host, and (outside the timed steps) the fused AdamW step over
+the shard's parameters against HBM bandwidth.
+
+Headline timing: W warmup steps, then K steps with library timing off, each between its
+own pair of HIP events on the library's stream, each preceded (outside its events) by a
+512 MiB write that evicts the previous step's data from the 256 MB MALL; ms_per_step is
+the median of the K step times.
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -62,6 +69,90 @@ def committed_traffic(kernel: str):
         return float(kv["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None
+
+
+SCRUB_BYTES = 512 << 20  # written before every timed step: twice the 256 MB MALL
+
+
+def dominant_pass(mt, torch, step, scrub, stream, label: str, steps: int):
+    """Roofline of the launch labelled `label`: its algorithmic FLOPs over its average
+    duration, from HIP events the library records around that launch on its stream
+    during `steps` further steps (scrubbed like the headline steps)."""
+    mt.timing_reset()
+    mt.timing_enable(True, label)
+    for i in range(steps):
+        scrub.fill_(i & 0xFF)
+        step()
+    torch.cuda.synchronize()
+    mt.timing_enable(False)
+    recs = [r for r in mt.timing_records() if r[0] == label]
+    mt.timing_reset()
+    if not recs:
+        return None
+    durs = sorted(r[1] for r in recs)
+    avg_ms = sum(durs) / len(durs)
+    kflops = recs[0][2]
+    achieved = kflops / (avg_ms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": committed_traffic(label), "kernel": label,
+            "avg_ms": round(avg_ms, 4), "median_ms": round(statistics.median(durs), 4), "launches": len(recs),
+            "gflop_per_launch": round(kflops / 1e9, 2)}
+
+
+def clock_pass(torch, step, stream, steps: int):
+    """Graphics clock while the steps run: amd-smi's GPU metrics sampled from a host
+    thread every ~2 ms during `steps` untimed steps (median and range of the samples,
+    MHz). None when the amd-smi library is not usable here."""
+    import threading
+    try:
+        sys.path.insert(0, "/opt/rocm/share/amd_smi")
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handle = amdsmi.amdsmi_get_processor_handles()[0]
+    except Exception as e:  # noqa: BLE001 - the clock is reported as unavailable
+        return {"mhz": None, "reason": f"amd-smi unavailable: {type(e).__name__}"}
+
+    def read():
+        m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+        for key in ("average_gfxclk_frequency", "current_gfxclk"):
+            v = m.get(key)
+            if isinstance(v, (list, tuple)):
+                v = [x for x in v if isinstance(x, (int, float)) and 0 < x < 10000]
+                v = sum(v) / len(v) if v else None
+            if isinstance(v, (int, float)) and 0 < v < 10000:
+                return key, float(v)
+        return None, None
+
+    samples, src, stop = [], [None], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                k, v = read()
+            except Exception:  # noqa: BLE001
+                k, v = None, None
+            if v is not None:
+                samples.append(v)
+                src[0] = k
+            time.sleep(0.002)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    torch.cuda.synchronize()
+    th.start()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    try:
+        amdsmi.amdsmi_shut_down()
+    except Exception:  # noqa: BLE001
+        pass
+    if not samples:
+        return {"mhz": None, "reason": "no gpu-metrics clock field"}
+    samples.sort()
+    return {"mhz": round(statistics.median(samples), 1), "min": samples[0], "max": samples[-1],
+            "samples": len(samples), "source": f"amd-smi gpu_metrics {src[0]}"}
 
 
 def parse():
@@ -238,9 +329,13 @@ def cpu_baseline(case, shape, min_seconds: float = 10.0, max_steps: int = 5):
     import numpy as np
     import oracle
     import seeded_inputs as si
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        pools = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max([i.get("num_threads", 1) for i in pools] or [1])
+        if pools:
+            blas = f"{pools[0].get('internal_api', '?')} {pools[0].get('version', '')}".strip()
     except Exception:  # pragma: no cover - threadpoolctl missing
         threads = os.cpu_count() or 1
     t0 = time.perf_counter()
@@ -254,7 +349,20 @@ def cpu_baseline(case, shape, min_seconds: float = 10.0, max_steps: int = 5):
     flops = steps * si.model_flops(shape)
     return {"value": round(flops / dt / 1e12, 4), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{steps} full fwd+bwd step(s) of the same shard (h={case.shape.h}, M={shape.tokens}) in "
-                      f"NumPy fp64, {dt:.1f} s", "seconds": round(dt, 2)}
+                      f"NumPy fp64, {dt:.1f} s", "seconds": round(dt, 2), "cpu": cpu_model(), "blas": blas,
+            "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (first processor in /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
@@ -322,42 +430,38 @@ def main():
         breakdown = mt.timing_records()
         mt.timing_reset()
 
+    # Headline: K steps with library timing off. Each step is bracketed by its own pair of
+    # events on the library's stream; before each step (outside its events) a 512 MiB
+    # write evicts the previous step's weights and activations from the 256 MB MALL.
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    mt.timing_reset()
-    mt.timing_enable(True, args.dominant)
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    scrub = torch.empty(SCRUB_BYTES, dtype=torch.uint8, device="cuda")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
+    for i, (a, b) in enumerate(ev):
+        scrub.fill_(i & 0xFF)
+        a.record(stream)
         step()
-    end.record(stream)
+        b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    mt.timing_enable(False)
-    recs = [r for r in mt.timing_records() if r[0] == args.dominant]
-    mt.timing_reset()
-    ms_per_step = start.elapsed_time(end) / args.steps
+    step_ms = sorted(a.elapsed_time(b) for a, b in ev)
+    ms_per_step = statistics.median(step_ms)
     flops_step = L * si.model_flops(shape, causal=True)
     dense_step = L * si.model_flops(shape, causal=False)
     value = flops_step / (ms_per_step * 1e-3) / 1e12
 
-    roofline = None
-    if recs:
-        avg_ms = sum(r[1] for r in recs) / len(recs)
-        kflops = recs[0][2]
-        achieved = kflops / (avg_ms * 1e-3) / 1e12
-        traffic = committed_traffic(args.dominant)
-        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic, "kernel": args.dominant,
-                    "avg_ms": round(avg_ms, 4), "launches": len(recs), "gflop_per_launch": round(kflops / 1e9, 2)}
+    # The dominant launch, timed in a separate pass of the same steps: the library records
+    # HIP events around that launch only.
+    roofline = dominant_pass(mt, torch, step, scrub, stream, args.dominant, args.steps)
+    sclk = clock_pass(torch, step, stream, steps=max(args.steps, 20))
 
     optim = None if args.no_optimizer else optimizer_step(mt, si, torch, shape, stream)
     sp = sp_share(mt, si, torch, shape, weights[0], acts[0], dout, stream) if L == 1 and not args.no_sp else None
 
     cpu = None
     if not args.no_cpu_baseline:
-        print("[bench] timing the fp64 oracle on the host (one step)", file=sys.stderr, flush=True)
+        print("[bench] timing the fp64 oracle on the host (whole steps, at least 10 s)", file=sys.stderr, flush=True)
         cpu = cpu_baseline(case, shape)
 
     if breakdown:
@@ -380,6 +484,10 @@ def main():
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "dense_count_tflops": round(dense_step / (ms_per_step * 1e-3) / 1e12, 2),
         "wall_s_timed": round(wall, 3),
+        "step_ms": {"median": round(ms_per_step, 4), "mean": round(sum(step_ms) / len(step_ms), 4),
+                    "min": round(step_ms[0], 4), "max": round(step_ms[-1], 4),
+                    "mall_scrub_bytes": SCRUB_BYTES},
+        "sclk": sclk,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "optimizer_step": optim,

@@ -219,10 +219,14 @@ const char *mt_status_string(int status);
 /* Per-launch timing (the throughput-breakdown aid). While enabled, each launch whose
  * label contains `label_filter` (NULL or "" = every launch) is bracketed by two HIP
  * events on the call's stream and recorded with its label and algorithmic FLOPs and
- * bytes. Enabling creates events on the host; records persist until mt_timing_reset.
- * mt_timing_get waits for record i's end event and returns its duration in ms.
- * Returns MT_OK or an error status. Not meant to be toggled while calls are in flight
- * on other threads. */
+ * bytes. The events come from a library-wide pool: while timing is enabled, a call
+ * that finds the pool empty creates events (hipEventCreate) inside the call, so a
+ * timed call is not a pure launch sequence; mt_timing_reset returns the recorded
+ * events to the pool, and they live until the process ends. The flag is atomic and
+ * the records and pool are locked, so enabling, resetting and reading are safe from
+ * any thread; a call in flight on another thread while the flag flips may or may not
+ * be timed. Records persist until mt_timing_reset. mt_timing_get waits for record i's
+ * end event and returns its duration in ms. Returns MT_OK or an error status. */
 int mt_timing_enable(int enable, const char *label_filter);
 int mt_timing_reset(void);
 int mt_timing_count(void);

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -196,12 +197,17 @@ struct TimingRec {
   double flops, bytes;
 };
 
+// Timing state (the only state the library keeps). g_timing is read without the lock
+// by every launch sequence, so it is atomic; the filter, the records and the event pool
+// are only touched under g_tmu.
 std::mutex g_tmu;
-bool g_timing = false;
+std::atomic<bool> g_timing{false};
 std::string g_filter;
 std::vector<TimingRec> g_recs;
 std::vector<hipEvent_t> g_free;
 
+// An event from the pool, or a new one (hipEventCreate: only while timing is enabled).
+// Called with g_tmu held.
 hipEvent_t timing_event() {
   if (!g_free.empty()) {
     hipEvent_t e = g_free.back();
@@ -222,9 +228,10 @@ class Seq {
     if (err_ != hipSuccess) return false;
     hipEvent_t a = nullptr, b = nullptr;
     bool timed = false;
-    if (g_timing) {
+    if (g_timing.load(std::memory_order_acquire)) {
       std::lock_guard<std::mutex> lk(g_tmu);
-      if (g_timing && (g_filter.empty() || std::strstr(label, g_filter.c_str()) != nullptr)) {
+      if (g_timing.load(std::memory_order_relaxed) &&
+          (g_filter.empty() || std::strstr(label, g_filter.c_str()) != nullptr)) {
         a = timing_event();
         b = timing_event();
         timed = a && b;
@@ -232,9 +239,15 @@ class Seq {
     }
     if (timed && hipEventRecord(a, s_) != hipSuccess) timed = false;
     err_ = f();
-    if (timed && hipEventRecord(b, s_) == hipSuccess) {
+    if (timed && hipEventRecord(b, s_) != hipSuccess) timed = false;
+    if (a || b) {
       std::lock_guard<std::mutex> lk(g_tmu);
-      g_recs.push_back({label, a, b, flops, bytes});
+      if (timed) {
+        g_recs.push_back({label, a, b, flops, bytes});
+      } else {  // a half-acquired or unrecorded pair goes back to the pool
+        if (a) g_free.push_back(a);
+        if (b) g_free.push_back(b);
+      }
     }
     return err_ == hipSuccess;
   }
@@ -1057,8 +1070,8 @@ const char* mt_status_string(int status) {
 
 int mt_timing_enable(int enable, const char* label_filter) {
   std::lock_guard<std::mutex> lk(g_tmu);
-  g_timing = enable != 0;
   g_filter = label_filter ? label_filter : "";
+  g_timing.store(enable != 0, std::memory_order_release);
   return MT_OK;
 }
 

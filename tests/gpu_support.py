@@ -15,6 +15,8 @@ tensor.
 """
 from __future__ import annotations
 
+import json
+import os
 import sys
 from typing import Dict, List, Tuple
 
@@ -145,7 +147,24 @@ def compare(name: str, gpu: np.ndarray, ref: np.ndarray, tol: float, normwise: b
         extra = ""
     log(f"  {name:10s} max|err| {err:.3e}  rms {rms:.3e}  max/rms {err / max(rms, 1e-30):.2e}{extra}  "
         f"{'ok' if ok else 'FAIL'}")
+    record(name, gpu, ref, ok)
     return ok, err, rms
+
+
+def record(name: str, gpu: np.ndarray, ref: np.ndarray, ok: bool) -> None:
+    """With MT_PARITY_LOG set, append one JSON line per compared tensor to that file:
+    the test, the tensor and its three error ratios (max|err| / RMS, RMS(err) / RMS,
+    max|err| / max|T|)."""
+    path = os.environ.get("MT_PARITY_LOG")
+    if not path or not ref.size:
+        return
+    d = np.abs(gpu - ref)
+    rms = max(float(np.sqrt(np.mean(ref * ref))), 1e-300)
+    rec = {"test": os.environ.get("PYTEST_CURRENT_TEST", os.environ.get("MT_PARITY_CASE", "")).split(" (")[0],
+           "tensor": name, "max_rms": float(d.max()) / rms, "rms_rel": float(np.sqrt(np.mean(d * d))) / rms,
+           "max_max": float(d.max()) / max(float(np.abs(ref).max()), 1e-300), "ok": bool(ok)}
+    with open(path, "a") as f:
+        f.write(json.dumps(rec) + "\n")
 
 
 def check_all(gpu_out, gpu_dx, gpu_grads, ref_out, ref_dx, ref_grads, tol: float, keys=None,
