@@ -80,3 +80,18 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_workload_modes_follow_the_green_parity_tests():
+    """bench.py reports a workload only in a mode whose oracle parity test exists: the 1T
+    shard and the h=8192 stage default to (and only allow) the compensated logits."""
+    import bench
+    import seeded_inputs as si
+    assert set(bench.PARITY_MODES) == set(si.WORKLOADS)
+    assert bench.workload_mode("gpt175b_tp8") == "bf16"
+    assert bench.workload_mode("gpt175b_tp8", "bf16qk") == "bf16qk"
+    assert bench.workload_mode("gpt1t_tp8") == "bf16qk"
+    assert bench.workload_mode("gpt_h8192_stage_mb4") == "bf16qk"
+    for wl, mode in (("gpt1t_tp8", "bf16"), ("gpt_h8192_stage_mb2", "bf16"), ("gpt175b_tp8", "fp32")):
+        with pytest.raises(SystemExit):
+            bench.workload_mode(wl, mode)
