@@ -69,7 +69,8 @@ typedef enum {
   MT_ERR_INVALID_ARG = 1, /* null pointer, misalignment, inconsistent shape */
   MT_ERR_UNSUPPORTED = 2, /* valid shape outside the supported limits above */
   MT_ERR_HIP = 3,         /* a HIP launch or runtime call failed */
-  MT_ERR_WORKSPACE = 4    /* saved / workspace buffer smaller than the *_bytes query */
+  MT_ERR_WORKSPACE = 4,   /* saved / workspace buffer smaller than the *_bytes query */
+  MT_ERR_NOALLOC_LIMIT = 5 /* mt_mlp_bwd_noalloc: the shape's scratch exceeds MT_NOALLOC_SCRATCH_BYTES */
 } mt_status;
 
 typedef enum { MT_BF16 = 0, MT_FP32 = 1, MT_BF16_QK = 2 } mt_dtype;
@@ -134,6 +135,28 @@ int mt_mlp_fwd(const mt_shape *shape, const void *x, const void *w_fc1, const vo
 int mt_mlp_bwd(const mt_shape *shape, const void *x, const void *w_fc1, const void *w_fc2, const void *saved,
                size_t saved_bytes, const void *dy, void *dx_partial, float *dw_fc1, float *db_fc1, float *dw_fc2,
                void *workspace, size_t workspace_bytes, void *stream);
+
+/* mt_mlp_bwd for callers that cannot allocate device memory (code being captured into
+ * a HIP graph, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments without the workspace, the same kernels and bit-identical results. The
+ * scratch those kernels need (the dA tile buffer and the column-sum partials,
+ * mt_mlp_workspace_bytes(shape) bytes) comes from a static device array of
+ * MT_NOALLOC_SCRATCH_BYTES inside the library: the HIP runtime allocates it on each
+ * device when it loads the library's code there, and it is held until the process
+ * ends. The call allocates nothing itself (no hipMalloc/hipFree, no events: per-launch
+ * timing is skipped for it). Its first call on a device looks up that device's copy of
+ * the array (hipGetSymbolAddress) with the device current; `stream` must belong to the
+ * current device (else MT_ERR_INVALID_ARG). Every call on a device shares that
+ * device's array: calls that overlap on one device (other streams, other threads)
+ * race and must be serialised by the caller; nothing in the array needs to start at
+ * zero (every scratch value is written before it is read). Returns
+ * MT_ERR_NOALLOC_LIMIT, before launching anything, when mt_mlp_workspace_bytes(shape)
+ * exceeds MT_NOALLOC_SCRATCH_BYTES (e.g. bf16 with M * 4h/tp above ~28M elements);
+ * otherwise as mt_mlp_bwd. */
+#define MT_NOALLOC_SCRATCH_BYTES (64u << 20)
+int mt_mlp_bwd_noalloc(const mt_shape *shape, const void *x, const void *w_fc1, const void *w_fc2,
+                       const void *saved, size_t saved_bytes, const void *dy, void *dx_partial, float *dw_fc1,
+                       float *db_fc1, float *dw_fc2, void *stream);
 
 /* Attention block alone, the head-parallel counterpart of mt_mlp_* (concept report,
  * section 4.1: heads split over ranks, output projection split by rows):

@@ -17,7 +17,8 @@ from typing import Dict, List, Optional, Tuple
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmt.so")
 
-MT_OK, MT_ERR_INVALID_ARG, MT_ERR_UNSUPPORTED, MT_ERR_HIP, MT_ERR_WORKSPACE = range(5)
+MT_OK, MT_ERR_INVALID_ARG, MT_ERR_UNSUPPORTED, MT_ERR_HIP, MT_ERR_WORKSPACE, MT_ERR_NOALLOC_LIMIT = range(6)
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MT_NOALLOC_SCRATCH_BYTES of include/mt.h
 MT_BF16, MT_FP32, MT_BF16_QK = 0, 1, 2
 _DTYPES = {"bf16": MT_BF16, "fp32": MT_FP32, "bf16qk": MT_BF16_QK}
 
@@ -52,6 +53,7 @@ _SIGS = {
     "mt_mlp_workspace_bytes": (_SZ, [ctypes.POINTER(Shape)]),
     "mt_mlp_fwd": (_I, [ctypes.POINTER(Shape), _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP, _SZ, _VP]),
     "mt_mlp_bwd": (_I, [ctypes.POINTER(Shape), _VP, _VP, _VP, _VP, _SZ, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "mt_mlp_bwd_noalloc": (_I, [ctypes.POINTER(Shape), _VP, _VP, _VP, _VP, _SZ, _VP, _VP, _VP, _VP, _VP, _VP]),
     "mt_attn_saved_bytes": (_SZ, [ctypes.POINTER(Shape)]),
     "mt_attn_workspace_bytes": (_SZ, [ctypes.POINTER(Shape)]),
     "mt_attn_fwd": (_I, [ctypes.POINTER(Shape), _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP, _SZ, _VP]),
@@ -233,6 +235,16 @@ def mlp_bwd(shape: Shape, x, w_fc1, w_fc2, saved, dy, dx_partial, dw_fc1, db_fc1
     _check("mt_mlp_bwd", lib().mt_mlp_bwd(ctypes.byref(shape), _ptr(x), _ptr(w_fc1), _ptr(w_fc2), _ptr(saved),
                                           _nbytes(saved), _ptr(dy), _ptr(dx_partial), _ptr(dw_fc1), _ptr(db_fc1),
                                           _ptr(dw_fc2), _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def mlp_bwd_noalloc(shape: Shape, x, w_fc1, w_fc2, saved, dy, dx_partial, dw_fc1, db_fc1, dw_fc2,
+                    stream=None) -> None:
+    """mt_mlp_bwd_noalloc: mt_mlp_bwd with its scratch in the library's static device
+    array (no workspace argument; the call allocates nothing)."""
+    _check("mt_mlp_bwd_noalloc", lib().mt_mlp_bwd_noalloc(ctypes.byref(shape), _ptr(x), _ptr(w_fc1), _ptr(w_fc2),
+                                                          _ptr(saved), _nbytes(saved), _ptr(dy), _ptr(dx_partial),
+                                                          _ptr(dw_fc1), _ptr(db_fc1), _ptr(dw_fc2),
+                                                          _stream(stream)))
 
 
 def attn_saved_bytes(shape: Shape) -> int:

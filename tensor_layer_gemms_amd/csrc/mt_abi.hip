@@ -220,15 +220,17 @@ hipEvent_t timing_event() {
 }
 
 // Enqueues one launch (f returns hipError_t), optionally bracketed by timing events.
+// With timing off (no_timing), a sequence never touches the timing state, so it
+// creates no events.
 class Seq {
  public:
-  explicit Seq(hipStream_t s) : s_(s) {}
+  explicit Seq(hipStream_t s, bool no_timing = false) : s_(s), no_timing_(no_timing) {}
   template <class F>
   bool run(const char* label, double flops, double bytes, F&& f) {
     if (err_ != hipSuccess) return false;
     hipEvent_t a = nullptr, b = nullptr;
     bool timed = false;
-    if (g_timing.load(std::memory_order_acquire)) {
+    if (!no_timing_ && g_timing.load(std::memory_order_acquire)) {
       std::lock_guard<std::mutex> lk(g_tmu);
       if (g_timing.load(std::memory_order_relaxed) &&
           (g_filter.empty() || std::strstr(label, g_filter.c_str()) != nullptr)) {
@@ -256,6 +258,7 @@ class Seq {
 
  private:
   hipStream_t s_;
+  bool no_timing_;
   hipError_t err_ = hipSuccess;
 };
 
@@ -676,8 +679,9 @@ int mlp_fwd_impl(const Dims& d, const void* x, const void* w1, const void* b1, c
 }
 
 int mlp_bwd_impl(const Dims& d, const void* x, const void* w1, const void* w2, const MlpSaved& sv, const void* dy,
-                 void* dx, float* dw1, float* db1, float* dw2, const MlpWs& ws, hipStream_t stream) {
-  Seq q(stream);
+                 void* dx, float* dw1, float* db1, float* dw2, const MlpWs& ws, hipStream_t stream,
+                 bool no_timing = false) {
+  Seq q(stream, no_timing);
   q.run("fc2_dgrad_wgrad", 2 * gflop(d.M, d.ft, d.h), 0, [&] {
     GemmArgs dg = plain(dy, d.h, w2, d.ft, ws.da, d.ft, d.M, d.ft, d.h);
     dg.aux = sv.a;
@@ -765,6 +769,39 @@ bool grads_ok(const mt_layer_grads* g) {
   for (const void* q : p)
     if (!aligned16(q)) return false;
   return true;
+}
+
+// ------------------------------------------------------------------------- static scratch
+// The workspace of mt_mlp_bwd_noalloc: a fixed device array in the library's code
+// object, allocated by the HIP runtime when it loads the module on a device and held
+// until the process ends. Host code never uses the array's name as an address (on the
+// host it is a stand-in symbol): scratch_address asks the runtime for the current
+// device's copy once per device and keeps it.
+constexpr size_t kNoallocScratchBytes = (size_t)MT_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`; the stream (if any) must belong to that
+// device. Returns MT_OK, MT_ERR_INVALID_ARG (stream of another device) or MT_ERR_HIP.
+int scratch_address(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MT_ERR_HIP;
+  if (stream) {
+    int sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return MT_ERR_HIP;
+    if (sdev != dev) return MT_ERR_INVALID_ARG;
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MT_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MT_OK;
 }
 
 }  // namespace
@@ -873,6 +910,28 @@ int mt_mlp_bwd(const mt_shape* shape, const void* x, const void* w_fc1, const vo
   carve_mlp_ws(d, workspace, &ws);
   return mlp_bwd_impl(d, x, w_fc1, w_fc2, sv, dy, dx_partial, dw_fc1, db_fc1, dw_fc2, ws,
                       static_cast<hipStream_t>(stream));
+}
+
+int mt_mlp_bwd_noalloc(const mt_shape* shape, const void* x, const void* w_fc1, const void* w_fc2, const void* saved,
+                       size_t saved_bytes, const void* dy, void* dx_partial, float* dw_fc1, float* db_fc1,
+                       float* dw_fc2, void* stream) {
+  Dims d;
+  int st = validate_shape(shape, &d);
+  if (st != MT_OK) return st;
+  if (!aligned16(x) || !aligned16(w_fc1) || !aligned16(w_fc2) || !aligned16(saved) || !aligned16(dy) ||
+      !aligned16(dx_partial) || !aligned16(dw_fc1) || !aligned16(db_fc1) || !aligned16(dw_fc2))
+    return MT_ERR_INVALID_ARG;
+  MlpSaved sv;
+  MlpWs ws;
+  if (saved_bytes < carve_mlp_saved(d, nullptr, &sv)) return MT_ERR_WORKSPACE;
+  if (carve_mlp_ws(d, nullptr, &ws) > kNoallocScratchBytes) return MT_ERR_NOALLOC_LIMIT;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  void* base = nullptr;
+  st = scratch_address(s, &base);
+  if (st != MT_OK) return st;
+  carve_mlp_saved(d, const_cast<void*>(saved), &sv);
+  carve_mlp_ws(d, base, &ws);
+  return mlp_bwd_impl(d, x, w_fc1, w_fc2, sv, dy, dx_partial, dw_fc1, db_fc1, dw_fc2, ws, s, /*no_timing=*/true);
 }
 
 size_t mt_attn_saved_bytes(const mt_shape* shape) {
@@ -1064,6 +1123,8 @@ const char* mt_status_string(int status) {
     case MT_ERR_UNSUPPORTED: return "unsupported shape (head dim or seq not a multiple of 8, seq > 4096, h too large)";
     case MT_ERR_HIP: return "HIP launch or runtime error";
     case MT_ERR_WORKSPACE: return "saved or workspace buffer smaller than the *_bytes query";
+    case MT_ERR_NOALLOC_LIMIT:
+      return "the shape needs more scratch than the static no-alloc buffer holds (MT_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

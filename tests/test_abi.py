@@ -200,3 +200,19 @@ def test_attention_block_and_sp_reject_bad_arguments(lib):
     ln_bwd = lib.mt_sp_ln_bwd
     assert ln_bwd(ctypes.byref(sh), A, A, 1, A, A, A, A, 0, A, 0, A, A, A, 0, A, big, None) == mt.MT_ERR_INVALID_ARG
     assert ln_bwd(ctypes.byref(sh), A, A, 1, A, A, A, A, 0, A, A, A, A, A, A, A, 4, None) == mt.MT_ERR_WORKSPACE
+
+
+def test_mlp_bwd_noalloc_host_checks(lib):
+    """mt_mlp_bwd_noalloc refuses, before touching the device, a null pointer, a small
+    saved store and a shape whose scratch exceeds the static array."""
+    A, big = 1 << 20, 1 << 40
+    fn = lib.mt_mlp_bwd_noalloc
+    over = _shape(h=8192, heads=64, seq=2048, micro_batch=8, tp=8)  # 132 MiB of scratch
+    assert mt.mlp_workspace_bytes(over) > mt.NOALLOC_SCRATCH_BYTES
+    assert fn(ctypes.byref(over), A, A, A, A, big, A, A, A, A, A, None) == mt.MT_ERR_NOALLOC_LIMIT
+    ok = _shape(h=12288, heads=96, seq=2048, micro_batch=1, tp=8)  # 27 MiB: fits
+    assert mt.mlp_workspace_bytes(ok) <= mt.NOALLOC_SCRATCH_BYTES
+    assert fn(ctypes.byref(ok), A, A, 0, A, big, A, A, A, A, A, None) == mt.MT_ERR_INVALID_ARG
+    assert fn(ctypes.byref(ok), A, A, A, A, mt.mlp_saved_bytes(ok) - 1, A, A, A, A, A,
+              None) == mt.MT_ERR_WORKSPACE
+    assert "no-alloc" in mt.status_string(mt.MT_ERR_NOALLOC_LIMIT)
