@@ -24,6 +24,7 @@ enum EpiKind : int {
   EPI_DGELU = 4,      // C = acc * GeLU'(aux[m, n])            (aux = saved pre-activation)
   EPI_DSOFTMAX = 5,   // C = aux[m, n] * (acc - vec[m])        (aux = P, vec = rowsum(P * dP))
   EPI_BIAS_SPLIT = 6, // v = acc + bias[n]; C = bf16(v); for n < seg_n also C2 = bf16(v - bf16(v))
+  EPI_BIAS_RESID = 7, // C = acc + bias[n] + aux[m, n]              (aux = fp32 residual, layout of C)
 };
 
 enum Causal : int {

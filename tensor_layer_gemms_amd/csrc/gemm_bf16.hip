@@ -262,6 +262,7 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, bool a_k, bool b_k, int kind, int
       case EPI_BIAS_SPLIT: return dispatch<true, true, EPI_BIAS_SPLIT>(g, batch, s);
       case EPI_BIAS_GELU: return dispatch<true, true, EPI_BIAS_GELU>(g, batch, s);
       case EPI_DSOFTMAX: return dispatch<true, true, EPI_DSOFTMAX>(g, batch, s);
+      case EPI_BIAS_RESID: return dispatch<true, true, EPI_BIAS_RESID>(g, batch, s);
     }
   } else if (a_k && !b_k) {  // input gradients (dY W), P V, dS K
     switch (kind) {

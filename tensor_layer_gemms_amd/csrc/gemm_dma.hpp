@@ -63,18 +63,24 @@ __device__ __forceinline__ int kc_swz(int row, int chunk) {
 __device__ __forceinline__ int mc_swz(int krow, int chunk) { return chunk ^ ((krow & 3) << 2); }
 
 // DMA loads of one ROWS x BK operand tile (ROWS along m or n). The tile is 2 ROWS BK
-// bytes = ROWS BK / 512 wave instructions of 1 KB; wave w issues instructions w, w + NW,
-// ... Lane L of instruction q fills LDS bytes [q 1024 + 16 L, +16): LDS row
-// q RPI + L / CPR, stored chunk L % CPR, which holds the logical chunk the swizzle maps
-// there.
+// bytes = ROWS BK / 512 wave instructions of 1 KB. Lane L of instruction q fills LDS
+// bytes [q 1024 + 16 L, +16): LDS row q RPI + L / CPR, stored chunk L % CPR, which holds
+// the logical chunk the swizzle maps there.
+// Loader waves: with 8 waves (two per SIMD) only waves 0-3, one per SIMD, issue the
+// loads (wave w instructions w, w + 4, ...), so the other wave of every SIMD never waits
+// for loads of its own and runs its MFMAs while its partner issues and waits; measured on
+// the layer's shapes: forward GEMMs 4-15% faster, input and weight gradients 3-6%, than
+// with every wave issuing an equal share at the same point of the step. With 4 waves
+// every wave issues (instructions w, w + 4, ...).
 template <int ROWS, int BK, int NW, bool KC>
 struct DmaLoader {
   static constexpr int ROW_ELEMS = KC ? BK : ROWS;  // elements per LDS row
   static constexpr int CPR = ROW_ELEMS / 8;          // 16-byte chunks per LDS row
   static constexpr int RPI = 64 / CPR;               // LDS rows per wave instruction
   static constexpr int INSTR = ROWS * BK / 512;      // instructions per tile
-  static constexpr int PER_WAVE = INSTR / NW;        // instructions per wave
-  static_assert(INSTR % NW == 0, "tile must split evenly over the waves");
+  static constexpr int LW = NW == 8 ? 4 : NW;        // loader waves
+  static constexpr int PER_WAVE = INSTR / LW;        // instructions per loader wave
+  static_assert(INSTR % LW == 0, "tile must split evenly over the loader waves");
   static_assert(KC || (ROWS >= 128 && (ROWS & (ROWS - 1)) == 0), "m-contiguous tiles: power of two >= 128");
   __amdgpu_buffer_rsrc_t rsrc;
   uint32_t invalid;  // an offset at the end of the range: reads zeros
@@ -95,9 +101,10 @@ struct DmaLoader {
   }
 
   __device__ __forceinline__ void issue(bf16* lds_stage, int k0, int kend, int wave, int lane) const {
+    if (wave >= LW) return;  // wave-uniform
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
-      const int q = wave + i * NW;
+      const int q = wave + i * LW;
       const int r = q * RPI + lane / CPR;
       const int p = lane % CPR;
       uint32_t off;
@@ -230,6 +237,15 @@ __device__ __forceinline__ void epi_staged(const GemmArgs& g, f32x16 (&acc)[TM][
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = p[e] * (g.alpha * v[e] - d);
+          } else if constexpr (KIND == EPI_BIAS_RESID) {
+            float b[4] = {0.f, 0.f, 0.f, 0.f};
+            f32x4 r = {0.f, 0.f, 0.f, 0.f};
+            if (ok) {
+              load4_bf16(static_cast<const bf16*>(g.vec) + n, b);
+              r = *reinterpret_cast<const f32x4*>(static_cast<const float*>(g.aux) + coff + (int64_t)m * g.ldc + n);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] += b[e] + r[e];
           }
           put(s0, rho, c, v);
           if constexpr (TWO) {

@@ -22,6 +22,7 @@ hipError_t launch_gemm_f32(const GemmArgs& g, bool a_k, bool b_k, int kind, int 
       case EPI_BIAS: return run<true, true, EPI_BIAS>(g, batch, s);
       case EPI_BIAS_GELU: return run<true, true, EPI_BIAS_GELU>(g, batch, s);
       case EPI_DSOFTMAX: return run<true, true, EPI_DSOFTMAX>(g, batch, s);
+      case EPI_BIAS_RESID: return run<true, true, EPI_BIAS_RESID>(g, batch, s);
     }
   } else if (a_k && !b_k) {
     switch (kind) {

@@ -28,6 +28,9 @@ __device__ __forceinline__ void epi_store(const GemmArgs& g, int64_t coff, int64
     const float p = to_f32(static_cast<const T*>(g.aux)[idx]);
     const float d = static_cast<const float*>(g.vec)[voff + m];
     static_cast<T*>(g.C)[idx] = from_f32<T>(p * (g.alpha * v - d));
+  } else if constexpr (KIND == EPI_BIAS_RESID) {
+    const float r = static_cast<const float*>(g.aux)[idx];
+    static_cast<T*>(g.C)[idx] = from_f32<T>(v + to_f32(static_cast<const T*>(g.vec)[n]) + r);
   }
 }
 
@@ -98,6 +101,12 @@ __device__ __forceinline__ void epi_store4(const GemmArgs& g, int64_t coff, int6
     const float d = static_cast<const float*>(g.vec)[voff + m];
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = p[e] * (g.alpha * acc[e] - d);
+  } else if constexpr (KIND == EPI_BIAS_RESID) {
+    float b[4];
+    load4_bf16(static_cast<const bf16*>(g.vec) + n, b);
+    const f32x4 r = *reinterpret_cast<const f32x4*>(static_cast<const float*>(g.aux) + idx);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = acc[e] + b[e] + r[e];
   }
   store4_bf16(static_cast<bf16*>(g.C) + idx, v);
 }

@@ -474,14 +474,16 @@ int layer_fwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, void
     g.C2 = sv.z;
     return gemm(d, g, true, true, EPI_BIAS_GELU, 1, stream);
   });
-  // F9 row-parallel FC2: partial sum Y_i
+  // F9 row-parallel FC2, partial sum Y_i, and F10 Out = X2 + AR(Y_i) + b_fc2 in its
+  // epilogue: with the all-reduce the identity on one GPU, the partial is added to the fp32
+  // residual stream and the bias straight from the fp32 accumulators (it is never stored;
+  // a tensor-parallel group would store it as the all-reduce's input and add after it, as
+  // mt_mlp_fwd and mt_sp_add_fwd do)
   q.run("fc2_fwd", gflop(d.M, d.h, d.ft), 0, [&] {
-    GemmArgs g = plain(sv.z, d.ft, w.w_fc2, d.ft, ws.o, d.h, d.M, d.h, d.ft);
-    return gemm(d, g, true, true, EPI_STORE, 1, stream);
-  });
-  // F10 Out = X2 + AR(Y_i) + b_fc2
-  q.run("bias_residual_fwd", 0, Mh * (2 * es + 4), [&] {
-    return launch_add_bias_residual(bf, sv.x2, ws.o, w.b_fc2, out, (int)d.M, (int)d.h, stream);
+    GemmArgs g = plain(sv.z, d.ft, w.w_fc2, d.ft, out, d.h, d.M, d.h, d.ft);
+    g.vec = w.b_fc2;
+    g.aux = sv.x2;
+    return gemm(d, g, true, true, EPI_BIAS_RESID, 1, stream);
   });
   return q.status();
 }
