@@ -36,8 +36,8 @@ METRIC = "model TFLOP/s per GPU, GPT layer-shard fwd+bwd; % of bf16 MFMA peak"
 # HBM traffic of the reported kernel launch, measured with rocprofv3 counters and committed
 # as a summary per launch label; it is reported only while the GEMM sources hash to the
 # value recorded there.
-def traffic_file(label: str) -> str:
-    return os.path.join(ROOT, "profiles", f"{label}_gpt175b_tp8_traffic.txt")
+def traffic_file(label: str, workload: str = "gpt175b_tp8") -> str:
+    return os.path.join(ROOT, "profiles", f"{label}_{workload}_traffic.txt")
 
 
 GEMM_SOURCES = ["tensor_layer_gemms_amd/csrc/gemm_dma.hpp", "tensor_layer_gemms_amd/csrc/gemm_kernels.hpp",
@@ -54,12 +54,13 @@ def gemm_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def committed_traffic(kernel: str):
-    """Bytes per launch of `kernel` from the committed counter summary, or None when the
-    summary is missing, is for another kernel, or predates the current GEMM sources."""
+def committed_traffic(kernel: str, workload: str = "gpt175b_tp8"):
+    """Bytes per launch of `kernel` from the committed counter summary of `workload`, or
+    None when the summary is missing, is for another kernel, or predates the current GEMM
+    sources."""
     try:
         kv = {}
-        with open(traffic_file(kernel)) as f:
+        with open(traffic_file(kernel, workload)) as f:
             for line in f:
                 if ":" in line and not line.startswith("#"):
                     k, v = line.split(":", 1)
@@ -94,7 +95,7 @@ def workload_mode(workload: str, requested=None) -> str:
     return requested
 
 
-def dominant_pass(mt, torch, step, scrub, stream, label: str, steps: int):
+def dominant_pass(mt, torch, step, scrub, stream, label: str, steps: int, workload: str):
     """Roofline of the launch labelled `label`: its algorithmic FLOPs over its average
     duration, from HIP events the library records around that launch on its stream
     during `steps` further steps (scrubbed like the headline steps)."""
@@ -114,15 +115,17 @@ def dominant_pass(mt, torch, step, scrub, stream, label: str, steps: int):
     kflops = recs[0][2]
     achieved = kflops / (avg_ms * 1e-3) / 1e12
     return {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": committed_traffic(label), "kernel": label,
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": committed_traffic(label, workload), "kernel": label,
             "avg_ms": round(avg_ms, 4), "median_ms": round(statistics.median(durs), 4), "launches": len(recs),
             "gflop_per_launch": round(kflops / 1e9, 2)}
 
 
-def clock_pass(torch, step, stream, steps: int):
-    """Graphics clock while the steps run: amd-smi's GPU metrics sampled from a host
-    thread every ~2 ms during `steps` untimed steps (median and range of the samples,
-    MHz). None when the amd-smi library is not usable here."""
+def clock_pass(torch, step, stream, seconds: float = 3.0, settle: float = 1.0):
+    """Graphics clock while the steps run: amd-smi's GPU metrics (the mean of the eight
+    XCDs' current clocks, MHz), sampled from a host thread every ~20 ms while untimed
+    steps run for `seconds`; the metrics table refreshes about once a second, so samples
+    from the first `settle` seconds (still showing the idle clock) are dropped. Median and
+    range of the kept samples; None when the amd-smi library is not usable here."""
     import threading
     try:
         sys.path.insert(0, "/opt/rocm/share/amd_smi")
@@ -134,34 +137,35 @@ def clock_pass(torch, step, stream, steps: int):
 
     def read():
         m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
-        for key in ("average_gfxclk_frequency", "current_gfxclk"):
-            v = m.get(key)
-            if isinstance(v, (list, tuple)):
-                v = [x for x in v if isinstance(x, (int, float)) and 0 < x < 10000]
-                v = sum(v) / len(v) if v else None
-            if isinstance(v, (int, float)) and 0 < v < 10000:
-                return key, float(v)
-        return None, None
+        v = m.get("current_gfxclks")
+        if isinstance(v, (list, tuple)):
+            v = [x for x in v if isinstance(x, (int, float)) and 0 < x < 10000]
+            if v:
+                return sum(v) / len(v)
+        v = m.get("current_gfxclk")
+        return float(v) if isinstance(v, (int, float)) and 0 < v < 10000 else None
 
-    samples, src, stop = [], [None], threading.Event()
+    samples, stop = [], threading.Event()
+    t_start = [0.0]
 
     def sampler():
         while not stop.is_set():
             try:
-                k, v = read()
+                v = read()
             except Exception:  # noqa: BLE001
-                k, v = None, None
-            if v is not None:
+                v = None
+            if v is not None and time.perf_counter() - t_start[0] >= settle:
                 samples.append(v)
-                src[0] = k
-            time.sleep(0.002)
+            time.sleep(0.02)
 
     th = threading.Thread(target=sampler, daemon=True)
     torch.cuda.synchronize()
+    t_start[0] = time.perf_counter()
     th.start()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
+    while time.perf_counter() - t_start[0] < seconds:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
     stop.set()
     th.join()
     try:
@@ -171,8 +175,9 @@ def clock_pass(torch, step, stream, steps: int):
     if not samples:
         return {"mhz": None, "reason": "no gpu-metrics clock field"}
     samples.sort()
-    return {"mhz": round(statistics.median(samples), 1), "min": samples[0], "max": samples[-1],
-            "samples": len(samples), "source": f"amd-smi gpu_metrics {src[0]}"}
+    return {"mhz": round(statistics.median(samples), 1), "min": round(samples[0], 1), "max": round(samples[-1], 1),
+            "samples": len(samples), "source": "amd-smi gpu_metrics current_gfxclks (mean of the XCDs), "
+                                              f"{seconds - settle:.0f} s of steps after {settle:.0f} s settling"}
 
 
 def parse():
@@ -187,6 +192,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-optimizer", action="store_true", help="skip the fused AdamW step measurement")
     ap.add_argument("--no-sp", action="store_true", help="skip the sequence-parallel share measurement")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the graphics-clock samples (3 s of untimed steps; for profiled runs)")
     ap.add_argument("--mode", choices=["bf16", "bf16qk", "fp32"], default=None,
                     help="precision mode (default: the workload's, see PARITY_MODES); bf16qk = MT_BF16_QK, the "
                          "attention logits from hi + lo pairs of Q and K")
@@ -472,8 +479,8 @@ def main():
 
     # The dominant launch, timed in a separate pass of the same steps: the library records
     # HIP events around that launch only.
-    roofline = dominant_pass(mt, torch, step, scrub, stream, args.dominant, args.steps)
-    sclk = clock_pass(torch, step, stream, steps=max(args.steps, 20))
+    roofline = dominant_pass(mt, torch, step, scrub, stream, args.dominant, args.steps, args.workload)
+    sclk = None if args.no_clock else clock_pass(torch, step, stream)
 
     optim = None if args.no_optimizer else optimizer_step(mt, si, torch, shape, stream)
     sp = sp_share(mt, si, torch, shape, weights[0], acts[0], dout, stream) if L == 1 and not args.no_sp else None
