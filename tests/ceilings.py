@@ -1,0 +1,156 @@
+"""Per-tensor max-error ceilings of the bf16 parity tests.
+
+The bar of a bf16 output tensor T has two parts:
+  * normwise:  RMS(T_gpu - T_oracle) <= 2e-2 * RMS(T_oracle);
+  * elementwise: max|T_gpu - T_oracle| <= c_T * RMS(T_oracle), where c_T is the literal
+    2e-2 unless the rounding model (oracle/rounding.py: the oracle's formulas with bf16
+    rounding at the bf16 path's storage points) predicts a larger max|err| / RMS for T
+    on the same inputs:
+        c_T = max(2e-2, 1.5 * m_T * max(1, e_T / r_T)),
+    m_T and r_T the model's max|err| / RMS and RMS(err) / RMS, e_T the GPU's RMS(err) /
+    RMS. The model predicts each tensor's error without bias: over the 655 bf16 tensors
+    of the GPU tests the measured max / predicted max (after the RMS scaling) has median
+    1.00, 90th percentile 1.08 and 99th percentile 1.29, and its largest value is 1.43 (a
+    LayerNorm-gain gradient: the largest of a few thousand heavy-tailed column sums is a
+    noisy statistic, one realisation on each side). The factor 1.5 covers that spread.
+    The max prediction is scaled by the measured normwise error where that is larger
+    (fp32 accumulation order and the fused softmax's running maximum put the kernels'
+    error scale a few percent above the model's in places); the normwise part caps that
+    at 2e-2.
+A correct bf16 path cannot meet 2e-2 x RMS elementwise where the model, which has no
+GPU arithmetic in it, already exceeds it (near-tied logits flipping under the rounding
+of U, Q and K; heavy-tailed weight gradients). A regression confined to a few rows or
+tiles raises the largest error and hardly the RMS error: it fails unless its errors stay
+below the ceiling (2e-2 x RMS for most tensors, at most 0.18 x RMS for a single layer's
+tensors, 0.37 x RMS for the dX of the 4-layer stage).
+
+Small cases are predicted here at test time; the full-size cases come from
+tests/golden/precision_ceilings.json (written by tests/golden/make_precision_ceilings.py).
+"""
+from __future__ import annotations
+
+import json
+import os
+from typing import Dict, List, Optional, Tuple
+
+import numpy as np
+
+import seeded_inputs as si
+from oracle import rounding
+
+CEILING_FACTOR = 1.5
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "precision_ceilings.json")
+
+
+def mode_of(shape: si.LayerShape) -> str:
+    return "bf16qk" if shape.qk_pairs else "bf16"
+
+
+Pred = Tuple[float, float]  # the model's (max|err| / RMS, RMS(err) / RMS) of a tensor
+
+
+def ceiling(pred: Optional[Pred], tol: float = 2e-2, rms_gpu: float = 0.0) -> float:
+    """max|err| / RMS allowed for a tensor whose model prediction is `pred`, given the
+    GPU's own RMS(err) / RMS."""
+    if pred is None:
+        return tol
+    m, r = pred
+    scale = rms_gpu / r if r > 0 and rms_gpu > r else 1.0
+    return max(tol, CEILING_FACTOR * m * scale)
+
+
+def stored(key: str) -> Dict[str, Pred]:
+    """Predictions per tensor of a full-size case ("workload:mode")."""
+    with open(GOLDEN) as f:
+        data = json.load(f)
+    if key not in data:
+        raise KeyError(f"{key}: no stored prediction (run tests/golden/make_precision_ceilings.py {key})")
+    return {k: (v[0], v[1]) for k, v in data[key].items()}
+
+
+def _max_rms(a, b) -> Pred:
+    r = rounding.ratios(a, b)
+    return r[0], r[1]
+
+
+def layer(shape: si.LayerShape, x, dout, params) -> Dict[str, Pred]:
+    """Predictions for one shard's layer (mt_layer_fwd + mt_layer_bwd)."""
+    B, s, d = shape.micro_batch, shape.seq, shape.head_dim
+    ref = rounding.layer(x, dout, [params], B, s, d, ())
+    mod = rounding.layer(x, dout, [params], B, s, d, rounding.MODES[mode_of(shape)])
+    out = {"out": _max_rms(mod[0], ref[0]), "dx": _max_rms(mod[1], ref[1])}
+    out.update({k: _max_rms(mod[2][0][k], ref[2][0][k]) for k in ref[2][0]})
+    return out
+
+
+def stage(shape: si.LayerShape, x, dout, layers) -> Dict[str, Pred]:
+    """Predictions for consecutive layers (names "out", "dx", "l<l>.<tensor>")."""
+    B, s, d = shape.micro_batch, shape.seq, shape.head_dim
+    ref = rounding.stage(x, dout, layers, B, s, d, ())
+    mod = rounding.stage(x, dout, layers, B, s, d, rounding.MODES[mode_of(shape)])
+    out = {"out": _max_rms(mod[0], ref[0]), "dx": _max_rms(mod[1], ref[1])}
+    for l in range(len(layers)):
+        out.update({f"l{l}.{k}": _max_rms(mod[2][l][k], ref[2][l][k]) for k in ref[2][l]})
+    return out
+
+
+def mlp_shards(shape: si.LayerShape, x, dout, shards: List[dict]) -> Dict[str, Pred]:
+    """Predictions for the MLP block run shard by shard (mt_mlp_*): the summed output
+    and input-gradient partials ("sum y", "sum dx") and each shard's gradients."""
+    R = rounding._R(rounding.MODES["bf16"])
+    E = rounding._R(())
+    res = {}
+    for tag, r in (("mod", R), ("ref", E)):
+        ys, dxs, gs = [], [], []
+        for p in shards:
+            p = {k: np.asarray(v, np.float64) for k, v in p.items()}
+            y, c = rounding.mlp_fwd(np.asarray(x, np.float64), p, r)
+            dx, g = rounding.mlp_bwd(np.asarray(dout, np.float64), c, r)
+            ys.append(y), dxs.append(dx), gs.append(g)
+        res[tag] = (sum(ys), sum(dxs), gs)
+    mod, ref = res["mod"], res["ref"]
+    out = {"sum y": _max_rms(mod[0], ref[0]), "sum dx": _max_rms(mod[1], ref[1])}
+    names = {"w_fc1": "dW1", "b_fc1": "db1", "w_fc2": "dW2"}
+    for i in range(len(shards)):
+        out.update({f"{names[k]}[{i}]": _max_rms(mod[2][i][k], ref[2][i][k]) for k in names})
+    return out
+
+
+def attn_shards(shape: si.LayerShape, u, dout, shards: List[dict]) -> Dict[str, Pred]:
+    """Predictions for the attention block run shard by shard (mt_attn_*): "sum o",
+    "sum du" and each shard's "<tensor>[i]" gradients."""
+    B, s, d = shape.micro_batch, shape.seq, shape.head_dim
+    u = np.asarray(u, np.float64)
+    res = {}
+    for tag, names in (("mod", rounding.MODES["bf16"]), ("ref", ())):
+        r = rounding._R(names)
+        os_, dus, gs = [], [], []
+        for p in shards:
+            p = {k: np.asarray(v, np.float64) for k, v in p.items()}
+            o, c = rounding.attn_fwd(u, u, p, B, s, d, r)
+            du, g = rounding.attn_bwd(np.asarray(dout, np.float64), c, r)
+            os_.append(o), dus.append(du), gs.append(g)
+        res[tag] = (sum(os_), sum(dus), gs)
+    mod, ref = res["mod"], res["ref"]
+    out = {"sum o": _max_rms(mod[0], ref[0]), "sum du": _max_rms(mod[1], ref[1])}
+    for i in range(len(shards)):
+        out.update({f"{k}[{i}]": _max_rms(mod[2][i][k], ref[2][i][k]) for k in ("w_qkv", "b_qkv", "w_o")})
+    return out
+
+
+def sp_ranks(shape: si.LayerShape, x, dout, shards: List[dict], rows: List[np.ndarray]) -> List[Dict[str, Pred]]:
+    """Predictions per rank of the sequence-parallel share: the rank's rows of out and dx,
+    its shard gradients and its partial sums (over its rows) of the replicated ones; the
+    reduce-scatter outputs are rounded once after the sum."""
+    B, s, d = shape.micro_batch, shape.seq, shape.head_dim
+    ref = rounding.layer(x, dout, shards, B, s, d, (), ar_round=True)
+    mod = rounding.layer(x, dout, shards, B, s, d, rounding.MODES["bf16"], ar_round=True)
+    out = []
+    for i, rr in enumerate(rows):
+        p = {"out": _max_rms(mod[0][rr], ref[0][rr]), "dx": _max_rms(mod[1][rr], ref[1][rr])}
+        for k in ("w_qkv", "b_qkv", "w_o", "w_fc1", "b_fc1", "w_fc2"):
+            p[k] = _max_rms(mod[2][i][k], ref[2][i][k])
+        for k, v in ref[3].items():
+            p[k] = _max_rms(mod[3][k][rr].sum(0), v[rr].sum(0))
+        out.append(p)
+    return out

@@ -1,16 +1,20 @@
 """Parity of the HIP path (through the C ABI) with the fp64 oracle, on seeded inputs.
 
 Every output of the layer is compared: Out, dX and all twelve parameter gradients,
-to the bar stated in gpu_support (fp32: max-abs <= 1e-4 RMS; bf16: normwise 2e-2).
+to the bar stated in gpu_support (fp32: max-abs <= 1e-4 RMS; bf16: RMS error <= 2e-2
+RMS and max error <= c_T RMS, c_T the literal 2e-2 unless the bf16 rounding model
+predicts more for that tensor, then 1.5 x the prediction: tests/ceilings.py).
 Shapes go from the tiny fp32 layer through multi-tile shapes with ragged tails and
-odd head dims to the workloads' full sizes.
+odd head dims to the workloads' full sizes, in both bf16 modes wherever bench.py can
+report the workload in that mode.
 """
 import numpy as np
 import pytest
 
+import ceilings
 import oracle
 import seeded_inputs as si
-from gpu_support import (TOL, check_all, log, oracle_layer, run_layer_gpu, run_mlp_gpu, run_stage_gpu)
+from gpu_support import (TOL, check_all, compare, log, oracle_layer, run_layer_gpu, run_mlp_gpu, run_stage_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -19,13 +23,18 @@ def _layer_case(shape, seed=0, random_affine=False, global_weights=True):
     return si.make_case(shape, seed=seed, global_weights=global_weights, random_affine=random_affine)
 
 
-def _check_layer(shape, case, params=None):
+def _check_layer(shape, case, params=None, stored_key=None):
+    """One layer shard against the oracle; bf16 ceilings from the rounding model (run
+    here, or stored for the full-size workloads)."""
     params = params if params is not None else case.layers[0]
     log(f"layer {shape}")
     g_out, g_dx, g_gr = run_layer_gpu(shape, case.x, case.dout, params)
     r_out, r_dx, r_gr = oracle_layer(shape, case.x, case.dout, params)
-    bad = check_all(g_out, g_dx, g_gr, r_out, r_dx, r_gr, TOL[shape.dtype])
-    assert not bad, f"tensors over tolerance: {bad}"
+    preds = None
+    if shape.dtype == "bf16":
+        preds = ceilings.stored(stored_key) if stored_key else ceilings.layer(shape, case.x, case.dout, params)
+    bad = check_all(g_out, g_dx, g_gr, r_out, r_dx, r_gr, TOL[shape.dtype], preds=preds)
+    assert not bad, f"tensors over the bar: {bad}"
 
 
 TINY = si.WORKLOADS["tiny_fp32"].shape
@@ -67,15 +76,17 @@ def test_mlp_shards_sum_to_unsharded_block(dtype, tp):
     y_ref, c = oracle.mlp_fwd(case.x, [g])
     dx_ref, g_ref = oracle.mlp_bwd(case.dout, c, [g])
     tol = TOL[dtype]
-    from gpu_support import compare
     nw = dtype == "bf16"
-    assert compare("sum y", y_sum, y_ref, tol, nw)[0]
-    assert compare("sum dx", dx_sum, dx_ref, tol, nw)[0]
+    pr = ceilings.mlp_shards(shape, case.x, case.dout, [si.shard_slice(g, shape, i) for i in range(tp)]) if nw else {}
+    ok = compare("sum y", y_sum, y_ref, tol, nw, pr.get("sum y"))[0]
+    ok &= compare("sum dx", dx_sum, dx_ref, tol, nw, pr.get("sum dx"))[0]
     fs = 4 * shape.h // tp
     for i, gr in enumerate(grads):
-        assert compare(f"dW1[{i}]", gr["w_fc1"], g_ref[0]["w_fc1"][i * fs:(i + 1) * fs], tol, nw)[0]
-        assert compare(f"db1[{i}]", gr["b_fc1"], g_ref[0]["b_fc1"][i * fs:(i + 1) * fs], tol, nw)[0]
-        assert compare(f"dW2[{i}]", gr["w_fc2"], g_ref[0]["w_fc2"][:, i * fs:(i + 1) * fs], tol, nw)[0]
+        ok &= compare(f"dW1[{i}]", gr["w_fc1"], g_ref[0]["w_fc1"][i * fs:(i + 1) * fs], tol, nw, pr.get(f"dW1[{i}]"))[0]
+        ok &= compare(f"db1[{i}]", gr["b_fc1"], g_ref[0]["b_fc1"][i * fs:(i + 1) * fs], tol, nw, pr.get(f"db1[{i}]"))[0]
+        ok &= compare(f"dW2[{i}]", gr["w_fc2"], g_ref[0]["w_fc2"][:, i * fs:(i + 1) * fs], tol, nw,
+                      pr.get(f"dW2[{i}]"))[0]
+    assert ok
 
 
 def _run_attn_gpu(shape, u, d_o, p):
@@ -110,7 +121,6 @@ def test_attn_shards_sum_to_unsharded_block(dtype, tp, h, heads, seq, mb):
     (mt_attn_*) run in turn on one device; the sum of the output partials and of the
     input-gradient partials against the unsharded oracle block, and each shard's weight
     gradients against the matching slice of the unsharded ones."""
-    from gpu_support import compare
     shape = si.LayerShape(h=h, heads=heads, seq=seq, micro_batch=mb, tp=tp, dtype=dtype)
     log(f"[attn block] {dtype} tp={tp} h={h} heads={heads} seq={seq} micro_batch={mb}")
     case = si.make_case(shape.replace(tp=1), seed=h + tp, global_weights=True, random_affine=True)
@@ -119,6 +129,7 @@ def test_attn_shards_sum_to_unsharded_block(dtype, tp, h, heads, seq, mb):
     du_ref, g_ref = oracle.attn_block_bwd(case.dout, c, g)
     o_sum = du_sum = 0.0
     tol, nw = TOL[dtype], dtype == "bf16"
+    pr = ceilings.attn_shards(shape, case.x, case.dout, [si.shard_slice(g, shape, i) for i in range(tp)]) if nw else {}
     ok = True
     for i in range(tp):
         p = si.shard_slice(g, shape, i)
@@ -126,9 +137,9 @@ def test_attn_shards_sum_to_unsharded_block(dtype, tp, h, heads, seq, mb):
         o_sum, du_sum = o_sum + o, du_sum + du
         want = si.shard_slice(dict(g, **g_ref), shape, i)
         for k in ("w_qkv", "b_qkv", "w_o"):
-            ok &= compare(f"{k}[{i}]", gr[k], want[k], tol, nw)[0]
-    ok &= compare("sum o", o_sum, o_ref, tol, nw)[0]
-    ok &= compare("sum du", du_sum, du_ref, tol, nw)[0]
+            ok &= compare(f"{k}[{i}]", gr[k], want[k], tol, nw, pr.get(f"{k}[{i}]"))[0]
+    ok &= compare("sum o", o_sum, o_ref, tol, nw, pr.get("sum o"))[0]
+    ok &= compare("sum du", du_sum, du_ref, tol, nw, pr.get("sum du"))[0]
     assert ok
 
 
@@ -148,9 +159,9 @@ def test_layer_bf16_multi_tile(h, heads, seq, mb, tp, shard, qk_pairs):
 
 def test_qk_pairs_lower_the_logit_error():
     """MT_BF16_QK against MT_BF16 on the same inputs. At h=8192 the logits are large
-    enough that the CPU rounding model (tests/precision_model.py) predicts RMS errors of
-    0.99% (bf16) against 0.58% (bf16qk) for dW_qkv and 0.91% against 0.55% for dX: the
-    hi + lo logits must bring both at least 20% closer to the oracle."""
+    enough that the plain bf16 logits leave RMS errors of about 1% for dW_qkv and dX (the
+    GPU measures 0.98% and 0.90%, against 0.58% and 0.56% with the hi + lo logits): the
+    compensated mode must bring both at least 20% closer to the oracle."""
     from gpu_support import rel_rms
     shape = si.LayerShape(h=8192, heads=64, seq=256, micro_batch=1, tp=8, shard=3)  # head dim 128, fused
     case = si.make_case(shape, seed=31, global_weights=False, random_affine=True)
@@ -161,7 +172,8 @@ def test_qk_pairs_lower_the_logit_error():
     e_pairs = (rel_rms(pairs[2]["w_qkv"], r_gr["w_qkv"]), rel_rms(pairs[1], r_dx))
     log(f"  rms error dW_qkv, dX: bf16 {e_plain}, bf16qk {e_pairs}")
     assert e_pairs[0] < 0.8 * e_plain[0] and e_pairs[1] < 0.8 * e_plain[1]
-    bad = check_all(*pairs, r_out, r_dx, r_gr, TOL["bf16"])
+    qk = shape.replace(qk_pairs=True)
+    bad = check_all(*pairs, r_out, r_dx, r_gr, TOL["bf16"], preds=ceilings.layer(qk, case.x, case.dout, case.layers[0]))
     assert not bad, bad
 
 
@@ -184,18 +196,20 @@ def test_layer_fp32_multi_tile():
     _check_layer(shape, _layer_case(shape, seed=3, random_affine=True))
 
 
-def test_gpt_h1024_full():
+@pytest.mark.parametrize("mode", ["bf16", "bf16qk"])
+def test_gpt_h1024_full(mode):
     w = si.WORKLOADS["gpt_h1024"]
     case = si.workload_case("gpt_h1024")
-    _check_layer(w.shape, case)
+    _check_layer(w.shape.replace(qk_pairs=mode == "bf16qk"), case, stored_key=f"gpt_h1024:{mode}")
 
 
 @pytest.mark.timeout(900)
-def test_gpt175b_tp8_shard_full():
+@pytest.mark.parametrize("mode", ["bf16", "bf16qk"])
+def test_gpt175b_tp8_shard_full(mode):
     """The 175B-shaped shard at full size, every output against the full oracle."""
     w = si.WORKLOADS["gpt175b_tp8"]
     case = si.workload_case("gpt175b_tp8")
-    _check_layer(w.shape, case)
+    _check_layer(w.shape.replace(qk_pairs=mode == "bf16qk"), case, stored_key=f"gpt175b_tp8:{mode}")
 
 
 def test_bitwise_deterministic():
@@ -216,98 +230,88 @@ def test_stage_two_layers_small():
     layers = [[p] for p in case.layers]
     r_out, caches = oracle.stage_fwd(case.x, layers, shape.micro_batch, shape.seq, shape.head_dim)
     r_dx, r_grads = oracle.stage_bwd(case.dout, caches, layers)
-    bad = check_all(out, dx, grads[0], r_out, r_dx, r_grads[0][0], TOL["bf16"])
-    for k in r_grads[1][0]:
-        from gpu_support import compare
-        if not compare(f"l1.{k}", grads[1][k], r_grads[1][0][k], TOL["bf16"], True)[0]:
-            bad.append("l1." + k)
+    preds = ceilings.stage(shape, case.x, case.dout, case.layers)
+    bad = _check_stage(out, dx, grads, r_out, r_dx, [g[0] for g in r_grads], preds)
     assert not bad, bad
+
+
+def _check_stage(out, dx, grads, r_out, r_dx, r_grads, preds):
+    """Every output of a stage: out, dx, and each layer's gradients as "l<l>.<tensor>"."""
+    bad = []
+    for name, g, r in [("out", out, r_out), ("dx", dx, r_dx)]:
+        if not compare(name, g, r, TOL["bf16"], True, preds.get(name))[0]:
+            bad.append(name)
+    for l, rg in enumerate(r_grads):
+        for k in sorted(rg):
+            name = f"l{l}.{k}"
+            if not compare(name, grads[l][k], rg[k], TOL["bf16"], True, preds.get(name))[0]:
+                bad.append(name)
+    return bad
 
 
 # ------------------------------------------------------------------ full-size workloads
 @pytest.mark.timeout(1800)
 def test_gpt1t_tp8_shard_full():
     """The 1T-shaped shard (head dim 160) at full size against the full oracle, in the
-    MT_BF16_QK mode: its logits are large enough that bf16 Q and K alone put the
-    attention gradients near 3% normwise (CPU rounding model), over the 2e-2 bar."""
+    MT_BF16_QK mode, the mode bench.py runs it in: with bf16 Q and K alone its large
+    logits put the normwise error of Out, dX and the attention gradients at ~3%
+    (measured and predicted by the rounding model), over the 2e-2 bar."""
     w = si.WORKLOADS["gpt1t_tp8"]
     case = si.workload_case("gpt1t_tp8")
-    _check_layer(w.shape.replace(qk_pairs=True), case)
+    _check_layer(w.shape.replace(qk_pairs=True), case, stored_key="gpt1t_tp8:bf16qk")
 
 
-_STAGE_REF = {}
-
-
-def _stage_reference():
-    """Oracle of the h=8192 4-layer stage at micro-batch 1 (computed once)."""
-    if "ref" not in _STAGE_REF:
-        w = si.WORKLOADS["gpt_h8192_stage_mb1"]
-        case = si.workload_case("gpt_h8192_stage_mb1")
-        layers = [[p] for p in case.layers]
-        sh = w.shape
-        out, caches = oracle.stage_fwd(case.x, layers, sh.micro_batch, sh.seq, sh.head_dim)
-        dx, grads = oracle.stage_bwd(case.dout, caches, layers)
-        del caches
-        _STAGE_REF["ref"] = (out, dx, [g[0] for g in grads])
-    return _STAGE_REF["ref"]
-
-
-# A stage composes 4 bf16 layers, and the rounding errors of every layer (its bf16 GEMM
-# operands and the bf16 activations and gradients handed between layers) accumulate. The
-# CPU model of the path's rounding points (tests/precision_model.py run layer by layer)
-# puts the max-error ratio max|err| / max|T| of a correct bf16 path at 1.6-1.9% for this
-# stage's deepest gradients and dX, at the edge of the 2e-2 bar, while the RMS ratios stay
-# at <= 1.5%. Stage tests therefore assert the RMS part of the bar for every tensor and
-# report the max part; single-layer tests assert both.
-STAGE_MAX_PART = False
-# The stage's four h=8192 layers run in the MT_BF16_QK mode. In MT_BF16 (bf16 Q and K in
-# the logits) the rounding of the large logits compounds over the layers and puts the
-# RMS error of the first layers' dW_qkv, dW_o and d(ln1 gain) at 2.1-2.3%, over the bar;
-# with the hi + lo logits every tensor stays at <= 1.5%.
+# The h=8192 stage runs in the MT_BF16_QK mode (as bench.py runs it): in MT_BF16 the
+# rounding of the large logits compounds over the four layers and puts the RMS error of
+# the first layers' dW_qkv, dW_o and d(ln1 gain) at 2.1-2.3%, over the bar.
 STAGE_SHAPE = dict(qk_pairs=True)
 
 
+def _stage_oracle(mb):
+    w = si.WORKLOADS[f"gpt_h8192_stage_mb{mb}"]
+    case = si.workload_case(f"gpt_h8192_stage_mb{mb}")
+    layers = [[p] for p in case.layers]
+    sh = w.shape
+    out, caches = oracle.stage_fwd(case.x, layers, sh.micro_batch, sh.seq, sh.head_dim)
+    dx, grads = oracle.stage_bwd(case.dout, caches, layers)
+    del caches
+    return w, case, (out, dx, [g[0] for g in grads])
+
+
 @pytest.mark.timeout(1800)
-def test_stage_h8192_mb1_full():
-    """4 consecutive h=8192 tp=8 layers as one stage, micro-batch 1, every output."""
-    w = si.WORKLOADS["gpt_h8192_stage_mb1"]
-    case = si.workload_case("gpt_h8192_stage_mb1")
+@pytest.mark.parametrize("mb", [1, 2, 4])
+def test_stage_h8192_full(mb):
+    """4 consecutive h=8192 tp=8 layers as one stage at micro-batch mb: every output and
+    every layer's gradients against the full oracle of the stage."""
+    w, case, (r_out, r_dx, r_grads) = _stage_oracle(mb)
     shape = w.shape.replace(**STAGE_SHAPE)
     log(f"stage {shape} x{w.layers}")
     out, dx, grads = run_stage_gpu(shape, case.x, case.dout, case.layers)
-    r_out, r_dx, r_grads = _stage_reference()
-    bad = check_all(out, dx, grads[0], r_out, r_dx, r_grads[0], TOL["bf16"], max_part=STAGE_MAX_PART)
-    from gpu_support import compare
-    for l in range(1, w.layers):
-        for k in r_grads[l]:
-            if not compare(f"l{l}.{k}", grads[l][k], r_grads[l][k], TOL["bf16"], True, STAGE_MAX_PART)[0]:
-                bad.append(f"l{l}.{k}")
+    bad = _check_stage(out, dx, grads, r_out, r_dx, r_grads, ceilings.stored(f"gpt_h8192_stage_mb{mb}:bf16qk"))
     assert not bad, bad
 
 
 @pytest.mark.timeout(1800)
-@pytest.mark.parametrize("mb", [2, 4, 8])
-def test_stage_h8192_micro_batch_sampled(mb):
-    """Micro-batch mb of the same stage. Sequences are independent in the layer, and
-    sequence 0's inputs are the same seeded rows at every micro-batch size, so the rows
-    of sequence 0 of Out and dX must match the micro-batch-1 oracle. Weight gradients
-    are sums over sequences: those of the mb-sequence batch must equal the sum of the
-    per-sequence runs (linearity, checked on the GPU path itself). Every per-token value
-    of the path is computed with the same arithmetic at any micro-batch (no tile choice
-    changes an element's accumulation order or operands), so the two sides differ only
-    in the fp32 summation order over tokens: the bar is the fp32 one. For the same
-    reason sequence 0's rows of Out and dX equal those of the micro-batch-1 run of
-    sequence 0 bit for bit (batch invariance)."""
-    from gpu_support import compare
+def test_stage_h8192_micro_batch8_sampled():
+    """Micro-batch 8 of the same stage. Sequences are independent in the layer and
+    sequence 0's inputs are the same seeded rows at every micro-batch size, so sequence
+    0's rows of Out and dX must equal those of the micro-batch-1 run bit for bit (no
+    kernel's per-element arithmetic depends on the number of tokens) and meet the
+    micro-batch-1 oracle. Weight gradients are sums over sequences: they must equal the
+    sum of the eight per-sequence runs (each of which is a micro-batch-1 run, checked
+    against the oracle by test_stage_h8192_full) to the fp32 bar, the runs differing
+    only in the fp32 summation order over tokens."""
+    mb = 8
     w = si.WORKLOADS[f"gpt_h8192_stage_mb{mb}"]
     case = si.workload_case(f"gpt_h8192_stage_mb{mb}")
     s = w.shape.seq
     shape = w.shape.replace(**STAGE_SHAPE)
     log(f"stage {shape} x{w.layers}")
     out, dx, grads = run_stage_gpu(shape, case.x, case.dout, case.layers)
-    r_out, r_dx, _ = _stage_reference()
-    assert compare("out[seq0]", out[:s], r_out, TOL["bf16"], True, STAGE_MAX_PART)[0]
-    assert compare("dx[seq0]", dx[:s], r_dx, TOL["bf16"], True, STAGE_MAX_PART)[0]
+    _, _, (r_out, r_dx, _) = _stage_oracle(1)
+    preds = ceilings.stored("gpt_h8192_stage_mb1:bf16qk")
+    assert compare("out[seq0]", out[:s], r_out, TOL["bf16"], True, preds["out"])[0]
+    assert compare("dx[seq0]", dx[:s], r_dx, TOL["bf16"], True, preds["dx"])[0]
     one = shape.replace(micro_batch=1)
     total = None
     for b in range(mb):
@@ -319,4 +323,4 @@ def test_stage_h8192_micro_batch_sampled(mb):
         total = gb if total is None else [{k: t[k] + g[k] for k in t} for t, g in zip(total, gb)]
     for l in range(w.layers):
         for k in ("w_qkv", "w_fc1", "b_o", "ln1_g"):
-            assert compare(f"l{l}.{k} sum", grads[l][k], total[l][k], TOL["fp32"], True)[0]
+            assert compare(f"l{l}.{k} sum", grads[l][k], total[l][k], TOL["fp32"], False)[0]

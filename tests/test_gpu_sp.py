@@ -8,13 +8,16 @@ the calls are plain torch indexing and sums (the collectives are the caller's; a
 reduce-scatter's output is rounded to the activation dtype once, after an fp32 sum).
 Each rank's out rows, dx rows, shard weight gradients and replicated-parameter partial
 gradients are compared with oracle.sp_layer_fwd / sp_layer_bwd (pinned against the
-tensor-parallel layer in tests/test_oracle_sp.py) at the bar of the layer tests.
+tensor-parallel layer in tests/test_oracle_sp.py) at the bar of the layer tests, the
+bf16 ceilings from the rounding model of the tensor-parallel layer with the
+reduce-scatter outputs rounded once (tests/ceilings.py).
 """
 from __future__ import annotations
 
 import numpy as np
 import pytest
 
+import ceilings
 import oracle
 import seeded_inputs as si
 from gpu_support import TOL, check_all, log, mt_mod, mt_shape, to_dev, to_np, torch_mod
@@ -145,9 +148,10 @@ def test_sequence_parallel_share_matches_oracle(h, heads, seq, mb, tp, dtype):
     rows = [_rows(i, tp, mb, seq) for i in range(tp)]
     r_out, c = oracle.sp_layer_fwd([case.x[r] for r in rows], shards, mb, seq, shape.head_dim)
     r_dx, r_g = oracle.sp_layer_bwd([case.dout[r] for r in rows], c, shards)
+    preds = ceilings.sp_ranks(shape, case.x, case.dout, shards, rows) if dtype == "bf16" else [None] * tp
     bad = []
     for i in range(tp):
         log(f"[sp] rank {i}")
         bad += [f"rank {i}: {k}" for k in check_all(outs[i], dxs[i], grads[i], r_out[i], r_dx[i], r_g[i],
-                                                        TOL[dtype], keys=SHARD_KEYS + REPLICATED)]
+                                                        TOL[dtype], keys=SHARD_KEYS + REPLICATED, preds=preds[i])]
     assert not bad, bad
