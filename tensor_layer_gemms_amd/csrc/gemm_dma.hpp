@@ -100,6 +100,40 @@ struct DmaLoader {
     rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base), (short)0, (int)invalid, 0x00020000);
   }
 
+  // Fast path of a full k-step (k0 + BK <= kend, every lane's k in range): the lane's byte
+  // offset of instruction i at k = 0 is a per-tile constant (vo[i], from offsets()), and
+  // the step's advance, uniform over the work-group, goes in the instruction's SGPR
+  // offset. Masked lanes (an m-contiguous operand's columns past rows_valid) carry
+  // `invalid`; k-contiguous rows past rows_valid lie past the range by themselves. Both
+  // read zeros whether or not the hardware's range check counts the SGPR offset, as long
+  // as no sum wraps 32 bits: fast() requires twice the range to stay below 4 GiB.
+  __device__ __forceinline__ bool fast() const { return (uint64_t)invalid * 2u < 0xFFFFFFF0ull; }
+  __device__ __forceinline__ void offsets(int wave, int lane, uint32_t (&vo)[PER_WAVE]) const {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int q = (wave < LW ? wave : 0) + i * LW;
+      const int r = q * RPI + lane / CPR;
+      const int p = lane % CPR;
+      if constexpr (KC) {
+        vo[i] = (uint32_t)(r * ld + kc_swz<BK>(r, p) * 8) * 2u;
+      } else {
+        const int m = mc_swz(r, p) * 8;
+        vo[i] = m < rows_valid ? (uint32_t)(r * ld + m) * 2u : invalid;
+      }
+    }
+  }
+  __device__ __forceinline__ void issue_full(bf16* lds_stage, int k0, const uint32_t* vo, int wave) const {
+    if (wave >= LW) return;  // wave-uniform
+    const uint32_t soff = KC ? (uint32_t)k0 * 2u : (uint32_t)k0 * (uint32_t)ld * 2u;
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int q = wave + i * LW;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(lds_stage + q * 512), 16, vo[i], soff, 0, 0);
+    }
+  }
+
+  // General path (tail steps, causal k ranges, segmented m-contiguous operands): every
+  // lane checks its k against kend (and its m against rows_valid) each step.
   __device__ __forceinline__ void issue(bf16* lds_stage, int k0, int kend, int wave, int lane) const {
     if (wave >= LW) return;  // wave-uniform
 #pragma unroll
@@ -316,10 +350,35 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs& g, int bid, int z,
 
   const int nk1 = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
   const int nk = nk1 * nseg;
+  // per-lane offsets of the full-step loads (shared by the segments, whose operands have
+  // the same strides; an m-contiguous operand masks per lane, so with several segments,
+  // whose ranges differ, it stays on the general path)
+  using LA = DmaLoader<BM, BK, NW, A_K>;
+  using LB = DmaLoader<BN, BK, NW, B_K>;
+  uint32_t va[LA::PER_WAVE], vb[LB::PER_WAVE];
+  la[0].offsets(wave, lane, va);
+  lb[0].offsets(wave, lane, vb);
+  bool full_ok = (A_K || nseg == 1) && (B_K || nseg == 1);
+#pragma unroll
+  for (int s = 0; s < kMaxSeg; ++s)
+    if (s < nseg) full_ok = full_ok && la[s].fast() && lb[s].fast();
   auto issue = [&](int t) {  // loads of step t into stage t % NS
     const int sg = (t >= nk1) + (t >= 2 * nk1);
     const int k0 = kbeg + (t - sg * nk1) * BK;
     bf16* st = smem + (t % NS) * STAGE;
+    if (full_ok && k0 + BK <= kend) {
+      if (sg == 0) {
+        la[0].issue_full(st, k0, va, wave);
+        lb[0].issue_full(st + BM * BK, k0, vb, wave);
+      } else if (sg == 1) {
+        la[1].issue_full(st, k0, va, wave);
+        lb[1].issue_full(st + BM * BK, k0, vb, wave);
+      } else {
+        la[2].issue_full(st, k0, va, wave);
+        lb[2].issue_full(st + BM * BK, k0, vb, wave);
+      }
+      return;
+    }
     if (sg == 0) {
       la[0].issue(st, k0, kend, wave, lane);
       lb[0].issue(st + BM * BK, k0, kend, wave, lane);
