@@ -8,11 +8,6 @@ namespace mt {
 namespace {
 
 constexpr int kFlashRows = 64;  // query rows per work-group (waves of 32 rows)
-constexpr int kFlashKeys = 32;  // keys per streamed block
-// LDS ring depth: every row block of a head streams the same key blocks at about the same
-// pace, so each block's loads tend to miss in L2 together; three stages give them two
-// steps to arrive.
-constexpr int kStages = 3;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -89,37 +84,50 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t seq_rsrc(const bf16* base, int
 }
 
 // ---------------------------------------------------------------------------- forward
-// Work-group: 64 query rows of sequence b, head k, and 4 waves in two pairs. Both pairs
-// own the same rows (wave w: rows q0 + 32 (w & 1) ..) and split the row block's keys:
-// pair 0 streams the first half of its key blocks, pair 1 the second half, each through
-// its own three-stage LDS ring, so the longest chain of dependent key steps (the deepest
-// row block walks every key of the sequence) is halved. At the end pair 1 hands its
-// running (O, m, l) to pair 0 through LDS and pair 0 merges and writes. Lane l of a wave
-// owns query row (l & 31); the logit accumulator of a 32-key block holds keys
-// 8 q + 4 (l >> 5) + j in register 4 q + j (the operand-swapped MFMA layout).
-// COMP: the logits take the compensated form Q_hi K_hi^T + Q_hi K_lo^T + Q_lo K_hi^T
-// (a.qkv_lo holds the remainders); otherwise Q K^T with the bf16 Q and K.
-template <int D, bool COMP>
-__global__ __launch_bounds__(256) void flash_fwd_kernel(FlashArgs a) {
-  constexpr int KS = D / 16, NB = D / 32, TILE = kFlashKeys * D, RING = kStages * 3 * TILE;
-  __shared__ __attribute__((aligned(1024))) bf16 smem[2 * RING];
+// Combination of a value with the one in lane l ^ 32 (v_permlane32_swap: no LDS round
+// trip). Both halves compute the same expression on the same operands.
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Work-group: 64 query rows of sequence b, head k, and 2 NG waves; wave w works on rows
+// q0 + 32 (w & 1) and key group w >> 1. The row block's visible key blocks (32 keys) are
+// split into NG contiguous runs, one per group, so the longest chain of dependent key
+// steps (the deepest row block walks every key of the sequence) is 1 / NG of the
+// sequence. Each group streams its run through its own two-stage LDS ring. At the end
+// groups 1..NG-1 park their running (O, m, l) in LDS and group 0 merges them in group
+// order and writes. Lane l of a wave owns query row (l & 31); the logit accumulator of a
+// 32-key block holds keys 8 q + 4 (l >> 5) + j in register 4 q + j (the operand-swapped
+// MFMA layout). COMP: the logits take the compensated form Q_hi K_hi^T + Q_hi K_lo^T +
+// Q_lo K_hi^T (a.qkv_lo holds the remainders); otherwise Q K^T with the bf16 Q and K.
+template <int D, bool COMP, int NG>
+__global__ __launch_bounds__(128 * NG) void flash_fwd_kernel(FlashArgs a) {
+  constexpr int KB = 32, NSTG = 2;
+  constexpr int KS = D / 16, NB = D / 32, TILE = KB * D, NT = COMP ? 3 : 2, RING = NSTG * NT * TILE;
+  constexpr int NV = NB * 16 + 2;  // parked floats per lane
+  static_assert((NG - 1) * NV * 128 * 4 <= NG * RING * 2, "parked partials fit the rings");
+  __shared__ __attribute__((aligned(1024))) bf16 smem[NG * RING];
   dma_lds_escape(smem);
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int pair = wave >> 1, wv = wave & 1;  // key half, and the 32-row half of the block
+  const int grp = wave >> 1, wv = wave & 1;
   const int h = lane >> 5, r32 = lane & 31;
   const int nqb = (a.seq + kFlashRows - 1) / kFlashRows;
   int z, qbi;
   xcd_block(nqb, z, qbi);
-  const int qb = nqb - 1 - qbi;  // deepest row blocks first
+  const int qb = nqb - 1 - qbi;
   const int b = z / a.heads, hd = z % a.heads;
-  const int row = qb * kFlashRows + wv * 32 + r32;  // this lane's query row
+  const int row = qb * kFlashRows + wv * 32 + r32;
   const bool row_ok = row < a.seq;
 
   const bf16* qkv = static_cast<const bf16*>(a.qkv) + (int64_t)b * a.seq * a.ldq;
   const bf16* qlo = static_cast<const bf16*>(a.qkv_lo) + (int64_t)b * a.seq * a.ldq;
   const int cq = hd * D, ck = a.hs + hd * D, cv = 2 * a.hs + hd * D;
 
-  // Q_hi, Q_lo fragments of this lane's row for the whole head dim (A operand).
   bf16x8 qh[KS], ql[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
@@ -135,31 +143,28 @@ __global__ __launch_bounds__(256) void flash_fwd_kernel(FlashArgs a) {
   const __amdgpu_buffer_rsrc_t rk = seq_rsrc(qkv + ck, a.ldq, a.seq);
   const __amdgpu_buffer_rsrc_t rkl = seq_rsrc(COMP ? qlo + ck : qkv + ck, a.ldq, a.seq);
   const __amdgpu_buffer_rsrc_t rv = seq_rsrc(qkv + cv, a.ldq, a.seq);
-  const int kend = min(a.seq, (qb + 1) * kFlashRows);  // keys this row block can see
-  const int nsteps = (kend + kFlashKeys - 1) / kFlashKeys;
-  const int half = (nsteps + 1) / 2;                    // pair 0: blocks [0, half)
-  const int tb = pair ? half : 0, cnt = pair ? nsteps - half : half;
-  bf16* ring = smem + pair * RING;
+  const int kend = min(a.seq, (qb + 1) * kFlashRows);
+  const int nsteps = (kend + KB - 1) / KB;
+  const int per = (nsteps + NG - 1) / NG;                 // steps of every group (barrier count)
+  const int tb = min(grp * per, nsteps), cnt = min(per, nsteps - tb);
+  bf16* ring = smem + grp * RING;
   TileOffsets<D, false, 2> ok;
   TileOffsets<D, true, 2> ov;
   ok.init(a.ldq, wv, lane);
   ov.init(a.ldq, wv, lane);
-  auto issue = [&](int j) {  // key block tb + j into stage j % kStages of this pair's ring
-    bf16* st = ring + (j % kStages) * 3 * TILE;
-    const uint32_t rb = (uint32_t)((tb + j) * kFlashKeys) * (uint32_t)a.ldq * 2u;
+  auto issue = [&](int j) {
+    bf16* st = ring + (j % NSTG) * NT * TILE;
+    const uint32_t rb = (uint32_t)((tb + j) * KB) * (uint32_t)a.ldq * 2u;
 #pragma unroll
-    for (int i = 0; i < TileOffsets<D, false, 2>::PER; ++i) {  // K_hi, K_lo and V tiles of key block tb + j
+    for (int i = 0; i < TileOffsets<D, false, 2>::PER; ++i) {
       const int q = (wv + i * 2) * 512;
       lds_dma16(rk, st + q, ok.off[i] + rb);
-      if (COMP) lds_dma16(rkl, st + TILE + q, ok.off[i] + rb);
-      lds_dma16(rv, st + 2 * TILE + q, ov.off[i] + rb);
+      if (COMP) lds_dma16(rkl, st + 2 * TILE + q, ok.off[i] + rb);
+      lds_dma16(rv, st + TILE + q, ov.off[i] + rb);
     }
   };
 
-  // Per-lane LDS offsets. K fragment (B operand of S): key row r32, chunk 2 ks + h.
-  // V fragment (B operand of O, transposing read): 16-lane group g reads key rows
-  // K0 + ((l & 15) >> 2), columns 32 nb + 16 (g & 1) + 4 (l & 3).
-  const float scale2 = a.scale * kLog2e;  // logits in log2 units
+  const float scale2 = a.scale * kLog2e;
   f32x16 o[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
@@ -167,57 +172,51 @@ __global__ __launch_bounds__(256) void flash_fwd_kernel(FlashArgs a) {
     for (int r = 0; r < 16; ++r) o[nb][r] = 0.f;
   float m = -__builtin_inff(), l = 0.f;
 
-  // Per wave: 3 tiles (2 without the K remainders) of 32 D / 512 DMA instructions, over
-  // the pair's 2 waves. Both pairs pass the same number of work-group barriers (half
-  // iterations; pair 1 has at most one block fewer and idles through the last).
-  constexpr int LOADS = (COMP ? 3 : 2) * (32 * D / 512) / 2;
   if (cnt > 0) issue(0);
-  if (cnt > 1) issue(1);
-  for (int j = 0; j < half; ++j) {
-    // this wave's loads of block j are done when at most those of block j + 1 are pending
-    if (j + 1 < cnt) wait_vmcnt<LOADS>();
-    else wait_vmcnt<0>();
+  for (int j = 0; j < per; ++j) {
+    wait_vmcnt<0>();  // this wave's loads of block j
     dma_barrier();
-    if (j + 2 < cnt) issue(j + 2);  // into the stage read in step j - 1
-    const bf16* sK = ring + (j % kStages) * 3 * TILE;
-    const bf16* sKl = sK + TILE;
-    const bf16* sV = sK + 2 * TILE;
-
-    // Keys of this block vs this wave's rows r0..r0 + 31 (block and row starts are
-    // multiples of 32): all visible, the diagonal block, or none (nothing to do).
-    const int kb = (tb + j) * kFlashKeys, r0 = qb * kFlashRows + wv * 32;
+    if (j + 1 < cnt) issue(j + 1);  // into the stage read in step j - 1
+    const bf16* sK = ring + (j % NSTG) * NT * TILE;
+    const bf16* sV = sK + TILE;
+    const bf16* sKl = sK + 2 * TILE;
+    const int kb = (tb + j) * KB, r0 = qb * kFlashRows + wv * 32;
     if (j >= cnt || kb > r0) continue;
     const bool diag = kb == r0;
 
-    // S block: 32 keys x this wave's 32 rows (three segments when compensated).
-    f32x16 s;
+    // two accumulation chains over the head dim (even and odd 16-wide steps)
+    f32x16 sa, sb;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+    for (int r = 0; r < 16; ++r) sa[r] = sb[r] = 0.f;
+    // all K fragments of the block first, then the MFMAs
+    bf16x8 kf[KS], klf[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int off = r32 * D + (kswz<D>(r32, 2 * ks + h) << 3);
-      const bf16x8 kh = *reinterpret_cast<const bf16x8*>(sK + off);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qh[ks], s, 0, 0, 0);
+      kf[ks] = *reinterpret_cast<const bf16x8*>(sK + off);
+      if constexpr (COMP) klf[ks] = *reinterpret_cast<const bf16x8*>(sKl + off);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      f32x16& s = (ks & 1) ? sb : sa;
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qh[ks], s, 0, 0, 0);
       if constexpr (COMP) {
-        const bf16x8 kl = *reinterpret_cast<const bf16x8*>(sKl + off);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, qh[ks], s, 0, 0, 0);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, ql[ks], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(klf[ks], qh[ks], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], ql[ks], s, 0, 0, 0);
       }
     }
-
-    // Online softmax (row shared by lanes l and l ^ 32), in log2 units of the scaled
-    // logits. m is the maximum the exponentials are taken against; it is raised (and O,
-    // l rescaled) only when the block maximum exceeds it by more than 8, so the
-    // exponentials stay <= 2^8 and most blocks need no rescaling.
+    f32x16 sv;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sv[r] = sa[r] + sb[r];
     if (diag) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (kb + 8 * (r >> 2) + 4 * h + (r & 3) > row) s[r] = -__builtin_inff();
+        if (kb + 8 * (r >> 2) + 4 * h + (r & 3) > row) sv[r] = -__builtin_inff();
     }
-    float mloc = s[0];
+    float mloc = sv[0];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, s[r]);
-    const float mblk = fmaxf(mloc, __shfl_xor(mloc, 32)) * scale2;
+    for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, sv[r]);
+    const float mblk = xor32_max(mloc) * scale2;
     if (__any(mblk > m + 8.f)) {
       const float mnew = fmaxf(m, mblk);
       const float alpha = __builtin_amdgcn_exp2f(m - mnew);
@@ -231,17 +230,16 @@ __global__ __launch_bounds__(256) void flash_fwd_kernel(FlashArgs a) {
     float lsum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], scale2, -m));
-      lsum += s[r];
+      sv[r] = __builtin_amdgcn_exp2f(fmaf(sv[r], scale2, -m));
+      lsum += sv[r];
     }
-    l += lsum + __shfl_xor(lsum, 32);
+    l += xor32_sum(lsum);
 
-    // O += P V over the block's two 16-key slices.
 #pragma unroll
     for (int sl = 0; sl < 2; ++sl) {
       bf16x8 p;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) p[e] = (bf16)s[8 * sl + e];
+      for (int e = 0; e < 8; ++e) p[e] = (bf16)sv[8 * sl + e];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const int col = 32 * nb + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
@@ -258,32 +256,44 @@ __global__ __launch_bounds__(256) void flash_fwd_kernel(FlashArgs a) {
     }
   }
 
-  // Merge the pairs: pair 1 parks (O, m, l) in LDS as [value][wave-in-pair, lane] floats
-  // (consecutive lanes on consecutive words); pair 0 combines them with its own:
-  // M = max(m0, m1), O = O0 2^(m0 - M) + O1 2^(m1 - M), l likewise (a pair that saw no
-  // key of a row has m = -inf, l = 0, O = 0 and contributes nothing).
-  constexpr int NV = NB * 16 + 2;
+  // Merge: groups 1..NG-1 park (O, m, l) as [group - 1][value][wave-in-group, lane] floats;
+  // group 0 combines all groups in order: M = max m_g, O = sum O_g 2^(m_g - M), l likewise
+  // (a group that saw no key of a row has m = -inf, l = 0, O = 0 and adds nothing).
   float* park = reinterpret_cast<float*>(smem);
   const int slot = wv * 64 + lane;
-  dma_barrier();  // both rings are done with
-  if (pair == 1) {
+  dma_barrier();  // every ring is done with
+  if (grp > 0) {
+    float* pg = park + (grp - 1) * NV * 128;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) park[(nb * 16 + r) * 128 + slot] = o[nb][r];
-    park[(NV - 2) * 128 + slot] = m;
-    park[(NV - 1) * 128 + slot] = l;
+      for (int r = 0; r < 16; ++r) pg[(nb * 16 + r) * 128 + slot] = o[nb][r];
+    pg[(NV - 2) * 128 + slot] = m;
+    pg[(NV - 1) * 128 + slot] = l;
   }
   dma_barrier();
-  if (pair == 1) return;
-  const float m1 = park[(NV - 2) * 128 + slot], l1 = park[(NV - 1) * 128 + slot];
-  const float mm = fmaxf(m, m1);
-  const float w0 = __builtin_amdgcn_exp2f(m - mm), w1 = __builtin_amdgcn_exp2f(m1 - mm);
-  l = l * w0 + l1 * w1;
+  if (grp > 0) {
+    return;
+  }
+  float mm = m;
+#pragma unroll
+  for (int g = 1; g < NG; ++g) mm = fmaxf(mm, park[((g - 1) * NV + NV - 2) * 128 + slot]);
+  const float w0 = __builtin_amdgcn_exp2f(m - mm);
+  l *= w0;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o[nb][r] = o[nb][r] * w0 + park[(nb * 16 + r) * 128 + slot] * w1;
+    for (int r = 0; r < 16; ++r) o[nb][r] *= w0;
+#pragma unroll
+  for (int g = 1; g < NG; ++g) {
+    const float* pg = park + (g - 1) * NV * 128;
+    const float wg = __builtin_amdgcn_exp2f(pg[(NV - 2) * 128 + slot] - mm);
+    l += pg[(NV - 1) * 128 + slot] * wg;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[nb][r] += pg[(nb * 16 + r) * 128 + slot] * wg;
+  }
 
   if (row_ok) {
     const float inv = 1.f / l;
@@ -371,25 +381,36 @@ __device__ __forceinline__ void store_rows(bf16* out, const f32x16* acc, float s
     }
 }
 
-// dK and dV. Work-group: 64 keys (wave w: keys 64 kb + 32 w ..) of sequence b, head k;
-// streams the query blocks (32 queries) that see them. Lane l owns key (l & 31); the
-// accumulators of S^T and dP^T hold queries 8 q + 4 (l >> 5) + j in register 4 q + j.
+// Stage layouts of the backward rings (elements): NT tiles of [32][D] (Q or K first, then
+// dO or V, then the Q or K remainders when compensated), and for the key part 1 KB for L
+// and 1 KB for D of the stage's 32 queries (one DMA instruction each; the first 128 bytes
+// carry the values).
+template <int D, bool COMP>
+constexpr int kv_stage() { return (COMP ? 3 : 2) * 32 * D + 1024; }
+template <int D, bool COMP>
+constexpr int q_stage() { return (COMP ? 3 : 2) * 32 * D; }
+// Ring depth per group: two stages (loads one block ahead) with several groups, three
+// (two blocks ahead) for a single group.
+template <int NG>
+constexpr int bwd_stages() { return NG == 1 ? 3 : 2; }
+
+// dK and dV. Work-group: 64 keys of sequence b, head k, and NG groups of two waves (wave
+// w: keys 64 kb + 32 (w & 1) .., group w >> 1). The query blocks (32 queries) that see the
+// keys are split into NG consecutive runs; each group streams its run through its own
+// two-stage LDS ring and accumulates partial dK, dV, which groups 1..NG-1 park in LDS at
+// the end for group 0 to add in group order. Lane l owns key (l & 31); the accumulators
+// of S^T and dP^T hold queries 8 q + 4 (l >> 5) + j in register 4 q + j.
 //   P^T = exp(S^T / sqrt(d) - L[q]) (0 above the diagonal), dV += P^T dO,
 //   dS^T = P^T * (dP^T - D[q]) with dP^T = V dO^T, dK += dS^T Q / sqrt(d).
-// Per stage: Q_hi, Q_lo, dO tiles, then 1 KB for L and 1 KB for D of the 32 queries (one
-// DMA instruction each, wave 0 and wave 1; the first 128 bytes carry the values).
-template <int D>
-constexpr int kv_stage() { return 3 * 32 * D + 1024; }
-template <int D>
-constexpr int q_stage() { return 3 * 32 * D; }
-
-template <int D, bool COMP>
+template <int D, bool COMP, int NG>
 __device__ __forceinline__ void flash_bwd_kv(const FlashArgs& a, int kblk, int z, bf16* smem) {
-  constexpr int KS = D / 16, NB = D / 32, TILE = 32 * D, STAGE = kv_stage<D>();
+  constexpr int KS = D / 16, NB = D / 32, TILE = 32 * D, NT = COMP ? 3 : 2, STAGE = kv_stage<D, COMP>();
+  constexpr int NSTG = bwd_stages<NG>();
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = wave >> 1, wv = wave & 1;
   const int h = lane >> 5, r32 = lane & 31;
   const int b = z / a.heads, hd = z % a.heads;
-  const int key = kblk * 64 + wave * 32 + r32;
+  const int key = kblk * 64 + wv * 32 + r32;
   const bool key_ok = key < a.seq;
 
   const bf16* qkv = static_cast<const bf16*>(a.qkv) + (int64_t)b * a.seq * a.ldq;
@@ -420,24 +441,27 @@ __device__ __forceinline__ void flash_bwd_kv(const FlashArgs& a, int kblk, int z
       __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.D) + (int64_t)z * a.seq, (short)0, a.seq * 4, 0x00020000);
   const int qb0 = (kblk * 64) / 32, nqb = (a.seq + 31) / 32;
   const int nsteps = nqb - qb0;
+  const int per = (nsteps + NG - 1) / NG;
+  const int tb = min(grp * per, nsteps), cnt = min(per, nsteps - tb);
+  bf16* ring = smem + grp * NSTG * STAGE;
   DualOffsets<D> oq, oo;
-  oq.init(a.ldq, wave, lane);
-  oo.init(a.ldc, wave, lane);
+  oq.init(a.ldq, wv, lane);
+  oo.init(a.ldc, wv, lane);
   // lanes 0..7 of one instruction fetch the 32 floats; the others read past the range
   // (2^31 plus a row offset below 2^20 stays past it)
   const uint32_t lane_ld = lane < 8 ? 16u * lane : 0x80000000u;
-  auto issue = [&](int t) {
-    bf16* st = smem + (t % kStages) * STAGE;
-    const uint32_t r0 = (uint32_t)((qb0 + t) * 32);
+  auto issue = [&](int j) {
+    bf16* st = ring + (j % NSTG) * STAGE;
+    const uint32_t r0 = (uint32_t)((qb0 + tb + j) * 32);
     const uint32_t rbq = r0 * (uint32_t)a.ldq * 2u, rbo = r0 * (uint32_t)a.ldc * 2u;
 #pragma unroll
-    for (int i = 0; i < DualOffsets<D>::PER; ++i) {  // Q_hi, Q_lo and dO tiles of query block qb0 + t
-      const int q = (wave + i * 2) * 512;
+    for (int i = 0; i < DualOffsets<D>::PER; ++i) {  // Q_hi, dO (and Q_lo) tiles of the block
+      const int q = (wv + i * 2) * 512;
       lds_dma16(rq, st + q, oq.off[i] + rbq);
-      if (COMP) lds_dma16(rql, st + TILE + q, oq.off[i] + rbq);
-      lds_dma16(rdo, st + 2 * TILE + q, oo.off[i] + rbo);
+      lds_dma16(rdo, st + TILE + q, oo.off[i] + rbo);
+      if (COMP) lds_dma16(rql, st + 2 * TILE + q, oq.off[i] + rbq);
     }
-    lds_dma16(wave == 0 ? rl : rd, st + 3 * TILE + wave * 512, lane_ld + r0 * 4u);
+    lds_dma16(wv == 0 ? rl : rd, st + NT * TILE + wv * 512, lane_ld + r0 * 4u);
   };
 
   const float scale2 = a.scale * kLog2e;
@@ -447,34 +471,37 @@ __device__ __forceinline__ void flash_bwd_kv(const FlashArgs& a, int kblk, int z
 #pragma unroll
     for (int r = 0; r < 16; ++r) dv[nb][r] = dk[nb][r] = 0.f;
 
-  // Per wave: 3 tiles of 32 D / 512 DMA instructions over 2 waves, plus one for L or D.
-  constexpr int LOADS = (COMP ? 3 : 2) * DualOffsets<D>::PER + 1;
-  if (nsteps > 0) issue(0);
-  if (nsteps > 1) issue(1);
-  for (int t = 0; t < nsteps; ++t) {
-    if (t + 1 < nsteps) wait_vmcnt<LOADS>();
+  // per wave and block: NT tiles of DualOffsets::PER instructions, and one for L or D
+  constexpr int LOADS = NT * DualOffsets<D>::PER + 1;
+  for (int j = 0; j < NSTG - 1; ++j)
+    if (j < cnt) issue(j);
+  for (int j = 0; j < per; ++j) {
+    // this wave's loads of block j are done when at most those of the NSTG - 2 blocks
+    // after it are pending
+    if (NSTG == 3 && j + 1 < cnt) wait_vmcnt<(NSTG - 2) * LOADS>();
     else wait_vmcnt<0>();
     dma_barrier();
-    if (t + 2 < nsteps) issue(t + 2);
-    const bf16* sQ = smem + (t % kStages) * STAGE;
-    const bf16* sQl = sQ + TILE;
-    const bf16* sO = sQ + 2 * TILE;
-    const int q0 = (qb0 + t) * 32, k0 = kblk * 64 + wave * 32;
+    if (j + NSTG - 1 < cnt) issue(j + NSTG - 1);  // into the stage read in step j - 1
+    if (j >= cnt) continue;
+    const bf16* sQ = ring + (j % NSTG) * STAGE;
+    const bf16* sO = sQ + TILE;
+    const bf16* sQl = sQ + 2 * TILE;
+    const int q0 = (qb0 + tb + j) * 32, k0 = kblk * 64 + wv * 32;
     // Queries of this block vs this wave's keys (starts are multiples of 32): all see
     // them, the diagonal block, or none.
     const bool masked = q0 == k0 || q0 + 32 > a.seq;
     if (q0 < k0) continue;
     // L and D of this lane's 16 query columns (4 runs of 4 consecutive queries).
-    const float* sL = reinterpret_cast<const float*>(sQ + 3 * TILE);
+    const float* sL = reinterpret_cast<const float*>(sQ + NT * TILE);
     float l2[16], dq[16];
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
       const f32x4 lv = *reinterpret_cast<const f32x4*>(sL + 8 * qq + 4 * h);
       const f32x4 dv4 = *reinterpret_cast<const f32x4*>(sL + 256 + 8 * qq + 4 * h);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        l2[4 * qq + j] = lv[j] * kLog2e;
-        dq[4 * qq + j] = dv4[j];
+      for (int jj = 0; jj < 4; ++jj) {
+        l2[4 * qq + jj] = lv[jj] * kLog2e;
+        dq[4 * qq + jj] = dv4[jj];
       }
     }
     f32x16 st, dpt;
@@ -513,23 +540,54 @@ __device__ __forceinline__ void flash_bwd_kv(const FlashArgs& a, int kblk, int z
       }
     }
   }
-  if (key_ok) {
+  // Merge dK, then dV: groups 1..NG-1 park [group - 1][value][wave-in-group, lane] floats,
+  // group 0 adds them in group order.
+  float* park = reinterpret_cast<float*>(smem);
+  const int slot = wv * 64 + lane;
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    f32x16* acc = which ? dv : dk;
+    dma_barrier();  // the rings (or the previous round) are done with
+    if (grp > 0) {
+      float* pg = park + (grp - 1) * NB * 16 * 128;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pg[(nb * 16 + r) * 128 + slot] = acc[nb][r];
+    }
+    dma_barrier();
+    if (grp == 0) {
+#pragma unroll
+      for (int g = 1; g < NG; ++g) {
+        const float* pg = park + (g - 1) * NB * 16 * 128;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[nb][r] += pg[(nb * 16 + r) * 128 + slot];
+      }
+    }
+  }
+  if (grp == 0 && key_ok) {
     bf16* out = static_cast<bf16*>(a.dqkv) + ((int64_t)b * a.seq + key) * a.ldq;
     store_rows<D>(out + ck, dk, a.scale, h);
     store_rows<D>(out + cv, dv, 1.f, h);
   }
 }
 
-// dQ. Work-group: 64 query rows of sequence b, head k; streams the key blocks (32 keys)
-// they see. Lane l owns query row (l & 31).
+// dQ. Work-group: 64 query rows of sequence b, head k, and NG groups of two waves (wave w:
+// rows 64 qb + 32 (w & 1) .., group w >> 1); the key blocks (32 keys) the rows see are
+// split into NG consecutive runs, one per group, and group 0 adds the parked partial dQ
+// of the others in group order. Lane l owns query row (l & 31).
 //   P = exp(S / sqrt(d) - L), dS = P * (dO V^T - D), dQ += dS K / sqrt(d).
-template <int D, bool COMP>
+template <int D, bool COMP, int NG>
 __device__ __forceinline__ void flash_bwd_q(const FlashArgs& a, int qb, int z, bf16* smem) {
-  constexpr int KS = D / 16, NB = D / 32, TILE = 32 * D;
+  constexpr int KS = D / 16, NB = D / 32, TILE = 32 * D, STAGE = q_stage<D, COMP>();
+  constexpr int NSTG = bwd_stages<NG>();
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = wave >> 1, wv = wave & 1;
   const int h = lane >> 5, r32 = lane & 31;
   const int b = z / a.heads, hd = z % a.heads;
-  const int row = qb * kFlashRows + wave * 32 + r32;
+  const int row = qb * kFlashRows + wv * 32 + r32;
   const bool row_ok = row < a.seq;
 
   const bf16* qkv = static_cast<const bf16*>(a.qkv) + (int64_t)b * a.seq * a.ldq;
@@ -558,18 +616,21 @@ __device__ __forceinline__ void flash_bwd_q(const FlashArgs& a, int qb, int z, b
   const __amdgpu_buffer_rsrc_t rv = seq_rsrc(qkv + cv, a.ldq, a.seq);
   const int kend = min(a.seq, (qb + 1) * kFlashRows);
   const int nsteps = (kend + 31) / 32;
+  const int per = (nsteps + NG - 1) / NG;
+  const int tb = min(grp * per, nsteps), cnt = min(per, nsteps - tb);
+  bf16* ring = smem + grp * NSTG * STAGE;
   DualOffsets<D> koff;
-  koff.init(a.ldq, wave, lane);
-  auto issue = [&](int t) {
-    bf16* st = smem + (t % kStages) * 3 * TILE;
-    const uint32_t rb = (uint32_t)(t * 32) * (uint32_t)a.ldq * 2u;
+  koff.init(a.ldq, wv, lane);
+  auto issue = [&](int j) {
+    bf16* st = ring + (j % NSTG) * STAGE;
+    const uint32_t rb = (uint32_t)((tb + j) * 32) * (uint32_t)a.ldq * 2u;
 #pragma unroll
-    for (int i = 0; i < DualOffsets<D>::PER; ++i) {  // K_hi, K_lo and V tiles of key block t
-      const int q = (wave + i * 2) * 512;
+    for (int i = 0; i < DualOffsets<D>::PER; ++i) {  // K_hi, V (and K_lo) tiles of the key block
+      const int q = (wv + i * 2) * 512;
       const uint32_t off = koff.off[i] + rb;
       lds_dma16(rk, st + q, off);
-      if (COMP) lds_dma16(rkl, st + TILE + q, off);
-      lds_dma16(rv, st + 2 * TILE + q, off);
+      lds_dma16(rv, st + TILE + q, off);
+      if (COMP) lds_dma16(rkl, st + 2 * TILE + q, off);
     }
   };
 
@@ -580,20 +641,21 @@ __device__ __forceinline__ void flash_bwd_q(const FlashArgs& a, int qb, int z, b
 #pragma unroll
     for (int r = 0; r < 16; ++r) dq[nb][r] = 0.f;
 
-  constexpr int LOADS = (COMP ? 3 : 2) * DualOffsets<D>::PER;  // per wave: 3 tiles (2), over 2 waves
-  issue(0);
-  if (nsteps > 1) issue(1);
-  for (int t = 0; t < nsteps; ++t) {
-    if (t + 1 < nsteps) wait_vmcnt<LOADS>();
+  constexpr int LOADS = (COMP ? 3 : 2) * DualOffsets<D>::PER;  // per wave and block
+  for (int j = 0; j < NSTG - 1; ++j)
+    if (j < cnt) issue(j);
+  for (int j = 0; j < per; ++j) {
+    if (NSTG == 3 && j + 1 < cnt) wait_vmcnt<(NSTG - 2) * LOADS>();
     else wait_vmcnt<0>();
     dma_barrier();
-    if (t + 2 < nsteps) issue(t + 2);
-    const bf16* sK = smem + (t % kStages) * 3 * TILE;
-    const bf16* sKl = sK + TILE;
-    const bf16* sV = sK + 2 * TILE;
+    if (j + NSTG - 1 < cnt) issue(j + NSTG - 1);  // into the stage read in step j - 1
+    if (j >= cnt) continue;
+    const bf16* sK = ring + (j % NSTG) * STAGE;
+    const bf16* sV = sK + TILE;
+    const bf16* sKl = sK + 2 * TILE;
     // Keys of this block vs this wave's rows (starts are multiples of 32): all visible,
     // the diagonal block, or none.
-    const int kb = t * 32, r0 = qb * kFlashRows + wave * 32;
+    const int kb = (tb + j) * 32, r0 = qb * kFlashRows + wv * 32;
     if (kb > r0) continue;
     f32x16 s, dp;
 #pragma unroll
@@ -627,24 +689,46 @@ __device__ __forceinline__ void flash_bwd_q(const FlashArgs& a, int qb, int z, b
         dq[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(sK, sl, nb, lane), dd, dq[nb], 0, 0, 0);
     }
   }
+  float* park = reinterpret_cast<float*>(smem);
+  const int slot = wv * 64 + lane;
+  dma_barrier();  // the rings are done with
+  if (grp > 0) {
+    float* pg = park + (grp - 1) * NB * 16 * 128;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pg[(nb * 16 + r) * 128 + slot] = dq[nb][r];
+  }
+  dma_barrier();
+  if (grp > 0) return;
+#pragma unroll
+  for (int g = 1; g < NG; ++g) {
+    const float* pg = park + (g - 1) * NB * 16 * 128;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dq[nb][r] += pg[(nb * 16 + r) * 128 + slot];
+  }
   if (row_ok) store_rows<D>(static_cast<bf16*>(a.dqkv) + ((int64_t)b * a.seq + row) * a.ldq + cq, dq, a.scale, h);
 }
 
 // Both backward parts in one grid, each walking its deepest blocks first: blockIdx.x
 // interleaves them (even: key block x / 2 of dK, dV; odd: row block of dQ, deepest
 // first), so the grid's critical path is the longer of the two chains, not their sum.
-template <int D, bool COMP>
-__global__ __launch_bounds__(128) void flash_bwd_kernel(FlashArgs a) {
-  constexpr int SMEM = kStages * (kv_stage<D>() > q_stage<D>() ? kv_stage<D>() : q_stage<D>());
+template <int D, bool COMP, int NG>
+__global__ __launch_bounds__(128 * NG) void flash_bwd_kernel(FlashArgs a) {
+  constexpr int KVS = kv_stage<D, COMP>(), QS = q_stage<D, COMP>();
+  constexpr int SMEM = NG * bwd_stages<NG>() * (KVS > QS ? KVS : QS);
+  static_assert((NG - 1) * (D / 32) * 16 * 128 * 4 <= SMEM * 2, "parked partials fit the rings");
   __shared__ __attribute__((aligned(1024))) bf16 smem[SMEM];
   dma_lds_escape(smem);
   int z, x;
   xcd_block((int)gridDim.x, z, x);
   const int nqb = (a.seq + kFlashRows - 1) / kFlashRows, nkb = (a.seq + 63) / 64;
   if ((x & 1) == 0) {
-    if (x / 2 < nkb) flash_bwd_kv<D, COMP>(a, x / 2, z, smem);
+    if (x / 2 < nkb) flash_bwd_kv<D, COMP, NG>(a, x / 2, z, smem);
   } else {
-    if (x / 2 < nqb) flash_bwd_q<D, COMP>(a, nqb - 1 - x / 2, z, smem);
+    if (x / 2 < nqb) flash_bwd_q<D, COMP, NG>(a, nqb - 1 - x / 2, z, smem);
   }
 }
 
@@ -665,10 +749,14 @@ hipError_t launch_flash_bwd(const FlashArgs& a, int d, hipStream_t s) {
   const int n = 2 * (nqb > nkb ? nqb : nkb);
   const dim3 grid(n, a.batch * a.heads);
   const bool comp = a.qkv_lo != nullptr;
-  if (d == 128 && comp) hipLaunchKernelGGL((flash_bwd_kernel<128, true>), grid, dim3(128), 0, s, a);
-  else if (d == 128) hipLaunchKernelGGL((flash_bwd_kernel<128, false>), grid, dim3(128), 0, s, a);
-  else if (d == 64 && comp) hipLaunchKernelGGL((flash_bwd_kernel<64, true>), grid, dim3(128), 0, s, a);
-  else if (d == 64) hipLaunchKernelGGL((flash_bwd_kernel<64, false>), grid, dim3(128), 0, s, a);
+  // Two groups of two waves per work-group; one group (three-stage ring) for the plain
+  // head dim 128, where a work-group per CU leaves three rounds of work-groups either
+  // way and the split only adds the merge (more groups spill registers at head dim 128
+  // and ran slower at 64).
+  if (d == 128 && comp) hipLaunchKernelGGL((flash_bwd_kernel<128, true, 2>), grid, dim3(256), 0, s, a);
+  else if (d == 128) hipLaunchKernelGGL((flash_bwd_kernel<128, false, 1>), grid, dim3(128), 0, s, a);
+  else if (d == 64 && comp) hipLaunchKernelGGL((flash_bwd_kernel<64, true, 2>), grid, dim3(256), 0, s, a);
+  else if (d == 64) hipLaunchKernelGGL((flash_bwd_kernel<64, false, 2>), grid, dim3(256), 0, s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
@@ -678,10 +766,12 @@ hipError_t launch_flash_fwd(const FlashArgs& a, int d, hipStream_t s) {
   if (!flash_extents_ok(a)) return hipErrorInvalidValue;
   const dim3 grid((a.seq + kFlashRows - 1) / kFlashRows, a.batch * a.heads);
   const bool comp = a.qkv_lo != nullptr;
-  if (d == 128 && comp) hipLaunchKernelGGL((flash_fwd_kernel<128, true>), grid, dim3(256), 0, s, a);
-  else if (d == 128) hipLaunchKernelGGL((flash_fwd_kernel<128, false>), grid, dim3(256), 0, s, a);
-  else if (d == 64 && comp) hipLaunchKernelGGL((flash_fwd_kernel<64, true>), grid, dim3(256), 0, s, a);
-  else if (d == 64) hipLaunchKernelGGL((flash_fwd_kernel<64, false>), grid, dim3(256), 0, s, a);
+  // four key groups (8 waves) where their rings fit the LDS; two for the compensated
+  // head dim 128 (three tiles per stage)
+  if (d == 128 && comp) hipLaunchKernelGGL((flash_fwd_kernel<128, true, 2>), grid, dim3(256), 0, s, a);
+  else if (d == 128) hipLaunchKernelGGL((flash_fwd_kernel<128, false, 4>), grid, dim3(512), 0, s, a);
+  else if (d == 64 && comp) hipLaunchKernelGGL((flash_fwd_kernel<64, true, 4>), grid, dim3(512), 0, s, a);
+  else if (d == 64) hipLaunchKernelGGL((flash_fwd_kernel<64, false, 4>), grid, dim3(512), 0, s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

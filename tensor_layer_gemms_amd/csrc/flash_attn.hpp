@@ -1,12 +1,13 @@
 // Fused causal attention of the layer shard's heads (bf16 path, head dim 64 or 128).
 //
-// Forward: a work-group owns 64 query rows of one (sequence, head); two pairs of waves
-// stream the two halves of the visible keys in blocks of 32 through their own LDS rings
-// (DMA loads, three stages) and merge their partial results at the end. Per block the
-// logits S = Q K^T / sqrt(d) — with qkv_lo given, in the compensated form
-// (Q_hi K_hi^T + Q_hi K_lo^T + Q_lo K_hi^T) / sqrt(d) — are formed on the matrix cores, the causal mask is applied, the running row maximum and exponential sum are
-// updated (online softmax) and O += P V is accumulated with P taken straight from the
-// logit accumulators (rounded to bf16 as the matrix-core operand). S and P never reach
+// Forward: a work-group owns 64 query rows of one (sequence, head); four (two) groups of
+// two waves stream consecutive runs of the visible keys in blocks of 32 through their own
+// LDS rings (DMA loads, two stages) and merge their partial results at the end. Per block
+// the logits S = Q K^T / sqrt(d) — with qkv_lo given, in the compensated form
+// (Q_hi K_hi^T + Q_hi K_lo^T + Q_lo K_hi^T) / sqrt(d) — are formed on the matrix cores,
+// the causal mask is applied, the running row maximum and exponential sum are updated
+// (online softmax) and O += P V is accumulated with P taken straight from the logit
+// accumulators (rounded to bf16 as the matrix-core operand). S and P never reach
 // HBM. The forward writes ctx = O / l and the row log-sum-exp L = m + ln(l), from which
 // the backward recomputes P = exp(S - L).
 //
