@@ -6,23 +6,27 @@ The bar of a bf16 output tensor T has two parts:
     2e-2 unless the rounding model (oracle/rounding.py: the oracle's formulas with bf16
     rounding at the bf16 path's storage points) predicts a larger max|err| / RMS for T
     on the same inputs:
-        c_T = max(2e-2, 1.5 * m_T * max(1, e_T / r_T)),
+        c_T = max(2e-2, f_T * m_T * max(1, e_T / r_T)),
     m_T and r_T the model's max|err| / RMS and RMS(err) / RMS, e_T the GPU's RMS(err) /
-    RMS. The model predicts each tensor's error without bias: over the 655 bf16 tensors
-    of the GPU tests the measured max / predicted max (after the RMS scaling) has median
-    1.00, 90th percentile 1.08 and 99th percentile 1.29, and its largest value is 1.43 (a
-    LayerNorm-gain gradient: the largest of a few thousand heavy-tailed column sums is a
-    noisy statistic, one realisation on each side). The factor 1.5 covers that spread.
-    The max prediction is scaled by the measured normwise error where that is larger
-    (fp32 accumulation order and the fused softmax's running maximum put the kernels'
-    error scale a few percent above the model's in places); the normwise part caps that
-    at 2e-2.
+    RMS, f_T = 1.5 for matrices and 2.0 for one-dimensional tensors (LayerNorm gains and
+    biases, bias gradients: column sums over all tokens). The model predicts each
+    tensor's error without bias, and its RMS prediction is tight; its max prediction is
+    one realisation of the largest of many errors. Measured max / predicted max (after
+    the RMS scaling) over the bf16 tensors of the GPU tests, in two builds whose
+    attention kernels accumulate in different orders (two realisations of the same
+    errors): matrices median 1.00, 99th percentile 1.15-1.16, largest 1.27-1.28;
+    one-dimensional tensors median 1.00, 99th percentile 1.24-1.34, largest 1.43 and
+    1.52 (the largest of a few thousand heavy-tailed column sums is the noisier
+    statistic). The factors cover those spreads. The max prediction is scaled by the
+    measured normwise error where that is larger (fp32 accumulation order and the fused
+    softmax's running maximum put the kernels' error scale a few percent above the
+    model's in places); the normwise part caps that at 2e-2.
 A correct bf16 path cannot meet 2e-2 x RMS elementwise where the model, which has no
 GPU arithmetic in it, already exceeds it (near-tied logits flipping under the rounding
 of U, Q and K; heavy-tailed weight gradients). A regression confined to a few rows or
 tiles raises the largest error and hardly the RMS error: it fails unless its errors stay
 below the ceiling (2e-2 x RMS for most tensors, at most 0.18 x RMS for a single layer's
-tensors, 0.37 x RMS for the dX of the 4-layer stage).
+tensors, 0.32 x RMS for the 4-layer stage's gradients and 0.37 x RMS for its dX).
 
 Small cases are predicted here at test time; the full-size cases come from
 tests/golden/precision_ceilings.json (written by tests/golden/make_precision_ceilings.py).
@@ -38,7 +42,8 @@ import numpy as np
 import seeded_inputs as si
 from oracle import rounding
 
-CEILING_FACTOR = 1.5
+CEILING_FACTOR = 1.5      # matrices
+CEILING_FACTOR_1D = 2.0   # one-dimensional tensors (column sums)
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "precision_ceilings.json")
 
 
@@ -49,14 +54,14 @@ def mode_of(shape: si.LayerShape) -> str:
 Pred = Tuple[float, float]  # the model's (max|err| / RMS, RMS(err) / RMS) of a tensor
 
 
-def ceiling(pred: Optional[Pred], tol: float = 2e-2, rms_gpu: float = 0.0) -> float:
+def ceiling(pred: Optional[Pred], tol: float = 2e-2, rms_gpu: float = 0.0, one_d: bool = False) -> float:
     """max|err| / RMS allowed for a tensor whose model prediction is `pred`, given the
-    GPU's own RMS(err) / RMS."""
+    GPU's own RMS(err) / RMS; one_d for one-dimensional tensors."""
     if pred is None:
         return tol
     m, r = pred
     scale = rms_gpu / r if r > 0 and rms_gpu > r else 1.0
-    return max(tol, CEILING_FACTOR * m * scale)
+    return max(tol, (CEILING_FACTOR_1D if one_d else CEILING_FACTOR) * m * scale)
 
 
 def stored(key: str) -> Dict[str, Pred]:

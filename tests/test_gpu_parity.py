@@ -3,7 +3,8 @@
 Every output of the layer is compared: Out, dX and all twelve parameter gradients,
 to the bar stated in gpu_support (fp32: max-abs <= 1e-4 RMS; bf16: RMS error <= 2e-2
 RMS and max error <= c_T RMS, c_T the literal 2e-2 unless the bf16 rounding model
-predicts more for that tensor, then 1.5 x the prediction: tests/ceilings.py).
+predicts more for that tensor, then 1.5 x the prediction, 2 x for one-dimensional
+tensors: tests/ceilings.py).
 Shapes go from the tiny fp32 layer through multi-tile shapes with ragged tails and
 odd head dims to the workloads' full sizes, in both bf16 modes wherever bench.py can
 report the workload in that mode.
