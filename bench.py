@@ -224,7 +224,7 @@ def recompute_report(shape, ms_per_step: float, saved_bytes: int):
     pairs, as the model FLOPs are: forward n logit segments + P V; backward, key-block
     part n logit segments + dP + dV + dK, row-block part n logit segments + dP + dQ,
     with n = 3 (MT_BF16_QK) or 1."""
-    if shape.dtype != "bf16" or shape.head_dim not in (64, 128):
+    if shape.dtype != "bf16" or shape.head_dim not in (64, 128, 160):
         return None
     B, s, at, d = shape.micro_batch, shape.seq, shape.heads_per_shard, shape.head_dim
     M, h, t = shape.tokens, shape.h, shape.tp

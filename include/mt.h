@@ -48,7 +48,7 @@
  *     pairs, and the logits are Q_hi K_hi^T + Q_hi K_lo^T + Q_lo K_hi^T (Q and K to
  *     about 16 bits). Cost: one more GEMM over the Q and K columns, two more logit
  *     products, and the remainders in the saved store and workspace.
- *   - Attention of the bf16 paths with head dim 64 or 128 is fused: the logits and
+ *   - Attention of the bf16 paths with head dim 64, 128 or 160 is fused: the logits and
  *     probabilities stay on chip, the saved store keeps each row's log-sum-exp (fp32)
  *     (and under MT_BF16_QK the Q, K remainders) instead of P, and the backward
  *     recomputes P. Other head dims, and the fp32 path, store P and the gradients of

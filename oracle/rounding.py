@@ -17,7 +17,7 @@ QKV product and Q, K into the logits as hi + lo bf16 pairs ("u_pair", "qk_pair":
 bf16(x), lo = bf16(x - hi), about 16 significant bits; the V columns take the bf16 U,
 and the logits are Q_hi K_hi + Q_hi K_lo + Q_lo K_hi, without Q_lo K_lo).
 
-Attention with head dim 64 or 128 is fused on the bf16 path: the forward rounds the
+Attention with head dim 64, 128 or 160 is fused on the bf16 path: the forward rounds the
 unnormalised exponentials exp(S - max) to bf16 as the P V operand and divides by their
 fp32 sum afterwards, and the backward recomputes P in fp32, rounds it to bf16 as the dV
 operand and forms dS from the fp32 P. Other head dims store the normalised P in bf16 and
@@ -88,7 +88,7 @@ def _f64(p: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
 # --------------------------------------------------------------------------- blocks
 def fused_attention(d: int, r: _R) -> bool:
     """Whether the bf16 path runs this head dim's attention fused (see the module docstring)."""
-    return "p" in r and d in (64, 128)
+    return "p" in r and d in (64, 128, 160)
 
 
 def attn_fwd(u: np.ndarray, u_exact: np.ndarray, p, B: int, s: int, d: int, r: _R):

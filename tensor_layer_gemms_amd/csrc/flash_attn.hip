@@ -11,20 +11,41 @@ constexpr int kFlashRows = 64;  // query rows per work-group (waves of 32 rows)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Head dim 160: rows of 20 chunks (320 bytes) take no XOR swizzle; rotating row r's
+// chunks by (r >> 2) & 3 keeps 16 consecutive rows at one chunk, and 4 consecutive rows
+// at 4 consecutive chunks, on distinct bank groups (every fragment read of the kernels
+// below is conflict-free).
+__device__ __forceinline__ int rot20(int row, int chunk) {
+  const int c = chunk + ((row >> 2) & 3);
+  return c >= 20 ? c - 20 : c;
+}
+__device__ __forceinline__ int unrot20(int row, int p) {
+  const int c = p - ((row >> 2) & 3);
+  return c < 0 ? c + 20 : c;
+}
+
 // LDS placement of 16-byte chunks in a [32 keys][D] tile.
 // K (read with ds_read_b128, 16 lanes on 16 consecutive keys at one chunk): spread the 16
 // rows over the 64 banks.
 template <int D>
 __device__ __forceinline__ int kswz(int row, int chunk) {
-  if constexpr (D == 128) return chunk ^ (row & 15);
+  if constexpr (D == 160) return rot20(row, chunk);
+  else if constexpr (D == 128) return chunk ^ (row & 15);
   else return chunk ^ ((row >> 1) & 7);
 }
 // V (read with ds_read_b64_tr_b16, a half-wave on 4 consecutive keys x 32 columns): put
 // the 4 rows in 4 different 64-byte bank groups.
 template <int D>
 __device__ __forceinline__ int vswz(int row, int chunk) {
-  if constexpr (D == 128) return chunk ^ ((row & 3) << 2);
+  if constexpr (D == 160) return rot20(row, chunk);
+  else if constexpr (D == 128) return chunk ^ ((row & 3) << 2);
   else return chunk ^ (((row >> 1) & 1) << 2);
+}
+// Logical chunk held by stored chunk p of a row (the XOR swizzles are their own inverse).
+template <int D, bool VTILE>
+__device__ __forceinline__ int tile_unswz(int row, int p) {
+  if constexpr (D == 160) return unrot20(row, p);
+  else return VTILE ? vswz<D>(row, p) : kswz<D>(row, p);
 }
 
 // DMA of one [32][D] tile whose rows are key rows kb.. of a head's column slice. `rsrc`
@@ -37,15 +58,14 @@ __device__ __forceinline__ int vswz(int row, int chunk) {
 // kernels issue the loads themselves).
 template <int D, bool VTILE, int NW>
 struct TileOffsets {
-  static constexpr int CPR = D / 8, RPI = 64 / CPR, INSTR = 32 * D / 512, PER = INSTR / NW;
+  static constexpr int CPR = D / 8, INSTR = 32 * D / 512, PER = INSTR / NW;
   static_assert(INSTR % NW == 0, "tile instructions split over the waves");
   uint32_t off[PER];
   __device__ __forceinline__ void init(int64_t ld, int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int q = wave + i * NW;
-      const int r = q * RPI + lane / CPR, p = lane % CPR;
-      const int c = VTILE ? vswz<D>(r, p) : kswz<D>(r, p);
+      const int pos = (wave + i * NW) * 64 + lane;  // stored chunk of the tile
+      const int r = pos / CPR, c = tile_unswz<D, VTILE>(r, pos % CPR);
       off[i] = (uint32_t)(((int64_t)r * ld + c * 8) * 2);
     }
   }
@@ -310,17 +330,24 @@ __global__ __launch_bounds__(128 * NG) void flash_fwd_kernel(FlashArgs a) {
 }
 
 // ---------------------------------------------------------------------------- backward
-// Head dim D = 64 or 128. Tiles [32 rows][D] that serve both row reads (ds_read_b128, 16
-// lanes on 16 consecutive rows at one chunk) and transposing reads (a half-wave on 4
-// consecutive rows x 4 chunks) XOR the chunk index so that 16 consecutive rows land on 16
-// different 16-byte bank positions and 4 consecutive rows in 4 different 64-byte bank
-// groups: D = 128 (256-byte rows) chunk ^ (4 (r & 3) | ((r >> 2) & 3)); D = 64 (128-byte
-// rows, two per bank window) chunk ^ (4 ((r >> 1) & 1) | ((r >> 2) & 3)).
+// Head dim D = 64, 128 or 160. Tiles [32 rows][D] that serve both row reads
+// (ds_read_b128, 16 lanes on 16 consecutive rows at one chunk) and transposing reads (a
+// half-wave on 4 consecutive rows x 4 chunks) permute the chunks of each row so that 16
+// consecutive rows land on 16 different 16-byte bank positions and 4 consecutive rows in 4
+// different 64-byte bank groups: D = 128 (256-byte rows) chunk ^ (4 (r & 3) | ((r >> 2) &
+// 3)); D = 64 (128-byte rows, two per bank window) chunk ^ (4 ((r >> 1) & 1) | ((r >> 2) &
+// 3)); D = 160 (320-byte rows) the rotation rot20.
 template <int D>
 __device__ __forceinline__ int dswz(int row, int chunk) {
-  static_assert(D == 64 || D == 128, "backward head dims");
-  if constexpr (D == 128) return chunk ^ (((row & 3) << 2) | ((row >> 2) & 3));
+  static_assert(D == 64 || D == 128 || D == 160, "backward head dims");
+  if constexpr (D == 160) return rot20(row, chunk);
+  else if constexpr (D == 128) return chunk ^ (((row & 3) << 2) | ((row >> 2) & 3));
   else return chunk ^ ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+}
+template <int D>
+__device__ __forceinline__ int dunswz(int row, int p) {
+  if constexpr (D == 160) return unrot20(row, p);
+  else return dswz<D>(row, p);
 }
 
 // Per-lane byte offsets of the DMA loads of a [32][D] tile (dual swizzle) relative to the
@@ -328,13 +355,13 @@ __device__ __forceinline__ int dswz(int row, int chunk) {
 // rows past the sequence read zeros through the resource's range (as for dma_tile).
 template <int D>
 struct DualOffsets {
-  static constexpr int CPR = D / 8, RPI = 64 / CPR, PER = 32 * D / 512 / 2;  // per wave, 2 waves
+  static constexpr int CPR = D / 8, PER = 32 * D / 512 / 2;  // per wave, 2 waves
   uint32_t off[PER];
   __device__ __forceinline__ void init(int64_t ld, int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int q = wave + i * 2;
-      const int r = q * RPI + lane / CPR, c = dswz<D>(r, lane % CPR);
+      const int pos = (wave + i * 2) * 64 + lane;  // stored chunk of the tile
+      const int r = pos / CPR, c = dunswz<D>(r, pos % CPR);
       off[i] = (uint32_t)(((int64_t)r * ld + c * 8) * 2);
     }
   }
@@ -753,7 +780,9 @@ hipError_t launch_flash_bwd(const FlashArgs& a, int d, hipStream_t s) {
   // head dim 128, where a work-group per CU leaves three rounds of work-groups either
   // way and the split only adds the merge (more groups spill registers at head dim 128
   // and ran slower at 64).
-  if (d == 128 && comp) hipLaunchKernelGGL((flash_bwd_kernel<128, true, 2>), grid, dim3(256), 0, s, a);
+  if (d == 160 && comp) hipLaunchKernelGGL((flash_bwd_kernel<160, true, 2>), grid, dim3(256), 0, s, a);
+  else if (d == 160) hipLaunchKernelGGL((flash_bwd_kernel<160, false, 1>), grid, dim3(128), 0, s, a);
+  else if (d == 128 && comp) hipLaunchKernelGGL((flash_bwd_kernel<128, true, 2>), grid, dim3(256), 0, s, a);
   else if (d == 128) hipLaunchKernelGGL((flash_bwd_kernel<128, false, 1>), grid, dim3(128), 0, s, a);
   else if (d == 64 && comp) hipLaunchKernelGGL((flash_bwd_kernel<64, true, 2>), grid, dim3(256), 0, s, a);
   else if (d == 64) hipLaunchKernelGGL((flash_bwd_kernel<64, false, 2>), grid, dim3(256), 0, s, a);
@@ -767,8 +796,10 @@ hipError_t launch_flash_fwd(const FlashArgs& a, int d, hipStream_t s) {
   const dim3 grid((a.seq + kFlashRows - 1) / kFlashRows, a.batch * a.heads);
   const bool comp = a.qkv_lo != nullptr;
   // four key groups (8 waves) where their rings fit the LDS; two for the compensated
-  // head dim 128 (three tiles per stage)
-  if (d == 128 && comp) hipLaunchKernelGGL((flash_fwd_kernel<128, true, 2>), grid, dim3(256), 0, s, a);
+  // head dim 128 (three tiles per stage) and for head dim 160
+  if (d == 160 && comp) hipLaunchKernelGGL((flash_fwd_kernel<160, true, 2>), grid, dim3(256), 0, s, a);
+  else if (d == 160) hipLaunchKernelGGL((flash_fwd_kernel<160, false, 2>), grid, dim3(256), 0, s, a);
+  else if (d == 128 && comp) hipLaunchKernelGGL((flash_fwd_kernel<128, true, 2>), grid, dim3(256), 0, s, a);
   else if (d == 128) hipLaunchKernelGGL((flash_fwd_kernel<128, false, 4>), grid, dim3(512), 0, s, a);
   else if (d == 64 && comp) hipLaunchKernelGGL((flash_fwd_kernel<64, true, 4>), grid, dim3(512), 0, s, a);
   else if (d == 64) hipLaunchKernelGGL((flash_fwd_kernel<64, false, 4>), grid, dim3(512), 0, s, a);

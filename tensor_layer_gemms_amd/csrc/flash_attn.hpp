@@ -1,4 +1,4 @@
-// Fused causal attention of the layer shard's heads (bf16 path, head dim 64 or 128).
+// Fused causal attention of the layer shard's heads (bf16 path, head dim 64, 128 or 160).
 //
 // Forward: a work-group owns 64 query rows of one (sequence, head); four (two) groups of
 // two waves stream consecutive runs of the visible keys in blocks of 32 through their own
@@ -35,11 +35,11 @@ struct FlashArgs {
 };
 
 // Head dims the fused kernels handle (forward and backward).
-inline bool flash_supported(int d) { return d == 64 || d == 128; }
+inline bool flash_supported(int d) { return d == 64 || d == 128 || d == 160; }
 
-// Forward: ctx and lse from qkv, qkv_lo (d = 64 or 128).
+// Forward: ctx and lse from qkv, qkv_lo (d = 64, 128 or 160).
 hipError_t launch_flash_fwd(const FlashArgs& a, int d, hipStream_t s);
-// Backward: dQ, dK, dV into dqkv from qkv, qkv_lo, dctx, lse and D (d = 64 or 128).
+// Backward: dQ, dK, dV into dqkv from qkv, qkv_lo, dctx, lse and D (d = 64, 128 or 160).
 hipError_t launch_flash_bwd(const FlashArgs& a, int d, hipStream_t s);
 
 }  // namespace mt

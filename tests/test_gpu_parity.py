@@ -115,7 +115,8 @@ def _run_attn_gpu(shape, u, d_o, p):
     ("fp32", 2, 64, 4, 32, 2),       # unfused attention, literal 1e-4 bar
     ("bf16", 2, 512, 4, 136, 2),     # head dim 128: fused attention
     ("bf16", 4, 512, 8, 72, 3),      # head dim 64, three sequences
-    ("bf16", 2, 640, 4, 104, 1),     # head dim 160: materialised attention
+    ("bf16", 2, 640, 4, 104, 1),     # head dim 160: fused attention, ragged blocks
+    ("bf16", 2, 384, 4, 104, 1),     # head dim 96: materialised attention
 ])
 def test_attn_shards_sum_to_unsharded_block(dtype, tp, h, heads, seq, mb):
     """The pages' head-parallel split on the GPU: every shard of the attention block
@@ -146,7 +147,9 @@ def test_attn_shards_sum_to_unsharded_block(dtype, tp, h, heads, seq, mb):
 
 @pytest.mark.parametrize("h,heads,seq,mb,tp,shard", [
     (320, 5, 136, 3, 1, 0),    # several tiles, ragged token and feature tails
-    (640, 4, 264, 1, 2, 1),    # head dim 160, shard 1 of 2, ragged seq
+    (640, 4, 264, 1, 2, 1),    # head dim 160 (fused attention), shard 1 of 2, ragged seq
+    (1280, 8, 200, 2, 2, 0),   # head dim 160, 4 heads per shard, ragged query and key blocks
+    (384, 4, 136, 2, 2, 1),    # head dim 96: materialised attention
     (512, 8, 520, 2, 2, 0),    # seq spanning three causal chunks
     (512, 4, 200, 2, 2, 1),    # head dim 128 (fused attention): ragged query and key blocks
     (1024, 8, 72, 3, 1, 0),    # head dim 128, short sequences, 3 sequences per micro-batch
