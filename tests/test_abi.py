@@ -60,13 +60,18 @@ def test_buffer_queries_consistent(lib):
     assert need_q <= mt.layer_saved_bytes(sq) <= need_q + 64 * 256
     assert mt.layer_workspace_bytes(sq) >= 4 * M * (3 * h + 2 * h) + 2 * M * h
     assert mt.layer_workspace_bytes(s) <= mt.layer_workspace_bytes(sq)
-    # head dim 160 keeps the materialised attention: P (bf16) in the saved store, fp32
-    # scores in the workspace
+    # head dim 160 is fused too (row log-sum-exp, no P)
     s160 = _shape(h=640, heads=4, seq=256, micro_batch=2)
-    M1, h1, f1, a1, q1 = 512, 640, 2560, 4, 256
-    need160 = 2 * (M1 * h1 * 2 + M1 * 3 * h1 + 2 * a1 * q1 * q1 + M1 * h1 + 2 * M1 * f1) + 4 * M1 * h1 + 16 * M1
+    M1, h1, f1, a1, q1, B1 = 512, 640, 2560, 4, 256, 2
+    need160 = 2 * (M1 * h1 + M1 * 3 * h1 + M1 * h1 + M1 * h1 + 2 * M1 * f1) + 4 * M1 * h1 + 16 * M1 + 4 * B1 * a1 * q1
     assert need160 <= mt.layer_saved_bytes(s160) <= need160 + 64 * 256
-    assert mt.layer_workspace_bytes(s160) >= 4 * 2 * a1 * q1 * q1
+    # head dim 96 keeps the materialised attention: P (bf16) in the saved store, fp32
+    # scores in the workspace
+    s96 = _shape(h=384, heads=4, seq=256, micro_batch=2)
+    M2, h2, f2, a2, q2 = 512, 384, 1536, 4, 256
+    need96 = 2 * (M2 * h2 * 2 + M2 * 3 * h2 + 2 * a2 * q2 * q2 + M2 * h2 + 2 * M2 * f2) + 4 * M2 * h2 + 16 * M2
+    assert need96 <= mt.layer_saved_bytes(s96) <= need96 + 64 * 256
+    assert mt.layer_workspace_bytes(s96) >= 4 * 2 * a2 * q2 * q2
     assert mt.mlp_saved_bytes(s) == 2 * 2 * M * f
     s8 = _shape(h=12288, heads=96, seq=2048, micro_batch=1, tp=8)
     s8b = _shape(h=12288, heads=96, seq=2048, micro_batch=1, tp=8, shard=7)
