@@ -28,21 +28,27 @@ __global__ __launch_bounds__(kLnThreads) void ln_fwd_kernel(const T* __restrict_
   __shared__ float red[NW];
   const int64_t row = blockIdx.x;
   const int nch = h / 8;
-  float v[CPT][8];
+  float v[CPT][8], ov[CPT][8], bv[CPT][8];
   float s = 0.f;
+  // every load first (clamped chunk indices keep idle chunks' loads in bounds)
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int chc = min((int)threadIdx.x + c * kLnThreads, nch - 1);
+    const int64_t off = row * h + (int64_t)chc * 8;
+    load8(x + off, v[c]);
+    if constexpr (ADD) {
+      load8(o + off, ov[c]);
+      load8(bias + chc * 8, bv[c]);
+    }
+  }
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     const int ch = threadIdx.x + c * kLnThreads;
     if (ch < nch) {
-      const int64_t off = row * h + (int64_t)ch * 8;
-      load8(x + off, v[c]);
       if constexpr (ADD) {
-        float ov[8], bv[8];
-        load8(o + off, ov);
-        load8(bias + ch * 8, bv);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[c][e] += ov[e] + bv[e];
-        store8(x2 + off, v[c]);
+        for (int e = 0; e < 8; ++e) v[c][e] += ov[c][e] + bv[c][e];
+        store8(x2 + row * h + (int64_t)ch * 8, v[c]);
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) s += v[c][e];
@@ -102,20 +108,27 @@ __global__ __launch_bounds__(kLnThreads) void ln_bwd_kernel(const T* __restrict_
   const int64_t row = blockIdx.x;
   const int nch = h / 8;
   const float mu = mean[row], rs = rstd[row];
-  float g[CPT][8], xh[CPT][8];
+  // Every load first (clamped chunk indices keep idle chunks' loads in bounds); above 4
+  // chunks per thread the residual is loaded after the reduction, to stay in registers.
+  constexpr bool kResidFirst = CPT <= 4;
+  float g[CPT][8], xh[CPT][8], gv[CPT][8], rv[CPT][8];
   float s[2] = {0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int chc = min((int)threadIdx.x + c * kLnThreads, nch - 1);
+    const int64_t off = row * h + (int64_t)chc * 8;
+    load8(dy + off, g[c]);
+    load8(x + off, xh[c]);
+    load8(gamma + chc * 8, gv[c]);
+    if constexpr (kResidFirst) load8(resid + off, rv[c]);
+  }
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     const int ch = threadIdx.x + c * kLnThreads;
     if (ch < nch) {
-      const int64_t off = row * h + (int64_t)ch * 8;
-      float gv[8];
-      load8(dy + off, g[c]);
-      load8(x + off, xh[c]);
-      load8(gamma + ch * 8, gv);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        g[c][e] *= gv[e];
+        g[c][e] *= gv[c][e];
         xh[c][e] = (xh[c][e] - mu) * rs;
         s[0] += g[c][e];
         s[1] += g[c][e] * xh[c][e];
@@ -124,15 +137,19 @@ __global__ __launch_bounds__(kLnThreads) void ln_bwd_kernel(const T* __restrict_
   }
   block_sum<2, NW>(s, red);
   const float mg = s[0] / (float)h, mgx = s[1] / (float)h;
+  if constexpr (!kResidFirst) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c)
+      load8(resid + row * h + (int64_t)min((int)threadIdx.x + c * kLnThreads, nch - 1) * 8, rv[c]);
+  }
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     const int ch = threadIdx.x + c * kLnThreads;
     if (ch < nch) {
       const int64_t off = row * h + (int64_t)ch * 8;
-      float rv[8], out[8];
-      load8(resid + off, rv);
+      float out[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) out[e] = rv[e] + rs * (g[c][e] - mg - xh[c][e] * mgx);
+      for (int e = 0; e < 8; ++e) out[e] = rv[c][e] + rs * (g[c][e] - mg - xh[c][e] * mgx);
       store8(dx + off, out);
       if (dxf) store8(dxf + off, out);
     }
@@ -167,27 +184,40 @@ __global__ __launch_bounds__(kLnThreads) void ln_bwd_sums_kernel(const T* __rest
     for (int c = 0; c < CPT; ++c)
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[k][c][e] = 0.f;
+  // Every load of a row is issued before any of its arithmetic (clamped chunk indices
+  // keep the loads of idle chunks in bounds); gamma is loaded once per block where the
+  // registers allow (up to 3 chunks per thread), else with each row.
+  constexpr bool kGammaOnce = CPT <= 3;
+  static_assert(CPT <= 3 || !RSUM, "the residual's column sum rides along up to 3 chunks per thread");
+  float gv[CPT][8];
+  if constexpr (kGammaOnce) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) load8(gamma + min((int)threadIdx.x + c * kLnThreads, nch - 1) * 8, gv[c]);
+  }
   for (int row = r0; row < r1; ++row) {
     const float mu = mean[row], rs = rstd[row];
     float g[CPT][8], xh[CPT][8], rv[CPT][8];
     float s[2] = {0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
+      const int chc = min((int)threadIdx.x + c * kLnThreads, nch - 1);
+      const int64_t off = (int64_t)row * h + (int64_t)chc * 8;
+      load8(dy + off, g[c]);
+      load8(x + off, xh[c]);
+      if constexpr (kGammaOnce) load8(resid + off, rv[c]);  // else after the reduction
+      else load8(gamma + chc * 8, gv[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
       const int ch = threadIdx.x + c * kLnThreads;
       if (ch < nch) {
-        const int64_t off = (int64_t)row * h + (int64_t)ch * 8;
-        float gv[8];
-        load8(dy + off, g[c]);
-        load8(x + off, xh[c]);
-        load8(resid + off, rv[c]);
-        load8(gamma + ch * 8, gv);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           xh[c][e] = (xh[c][e] - mu) * rs;
           acc[0][c][e] += g[c][e] * xh[c][e];
           acc[1][c][e] += g[c][e];
           if constexpr (RSUM) acc[NS - 1][c][e] += rv[c][e];
-          g[c][e] *= gv[e];
+          g[c][e] *= gv[c][e];
           s[0] += g[c][e];
           s[1] += g[c][e] * xh[c][e];
         }
@@ -195,6 +225,11 @@ __global__ __launch_bounds__(kLnThreads) void ln_bwd_sums_kernel(const T* __rest
     }
     block_sum<2, NW>(s, red);
     const float mg = s[0] / (float)h, mgx = s[1] / (float)h;
+    if constexpr (!kGammaOnce) {
+#pragma unroll
+      for (int c = 0; c < CPT; ++c)
+        load8(resid + (int64_t)row * h + (int64_t)min((int)threadIdx.x + c * kLnThreads, nch - 1) * 8, rv[c]);
+    }
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int ch = threadIdx.x + c * kLnThreads;
