@@ -62,9 +62,17 @@ struct GemmArgs {
   // batch z = blockIdx.y; offsets (z / zdiv) * so + (z % zdiv) * si, in elements
   int64_t a_so, a_si, b_so, b_si, c_so, c_si;
   int64_t vec_bs;   // row-vector batch stride (EPI_DSOFTMAX)
+  // EPI_DGELU, unbatched, bf16 launchers: if set, also the column sums of the stored
+  // (bf16) C over each 128-row block of the M rows, fp32 [ceil(M / 128)][N] (the bias
+  // gradient of the layer whose pre-activation gradient C is, before its final sum).
+  float* colsum;
   int M, N, K, zdiv, causal;
   float alpha;
 };
+constexpr int kColsumRows = 128;  // rows per partial column-sum row of GemmArgs::colsum
+inline size_t gemm_colsum_floats(int rows, int cols) {
+  return (size_t)((rows + kColsumRows - 1) / kColsumRows) * (size_t)cols;
+}
 
 // Host launchers (gemm_*.hip). a_kcontig / b_kcontig: whether A(m, k) / B(n, k) is
 // contiguous along k. Return the launch status.

@@ -125,10 +125,30 @@ bool dma_ok(const GemmArgs& g, bool a_k, bool b_k) {
   return a_span < lim && b_span < lim;
 }
 
+// Column sums of C over each 128-row block (the register-staged kernel's epilogue does
+// not form them): thread = one column, rows in order, fp32.
+__global__ __launch_bounds__(256) void colsum_rows_kernel(const bf16* __restrict__ c, int64_t ldc, int M, int N,
+                                                          float* __restrict__ out) {
+  const int n = blockIdx.x * 256 + threadIdx.x, rb = blockIdx.y;
+  if (n >= N) return;
+  const int r1 = min(M, (rb + 1) * kColsumRows);
+  float sum = 0.f;
+  for (int r = rb * kColsumRows; r < r1; ++r) sum += (float)c[(int64_t)r * ldc + n];
+  out[(int64_t)rb * N + n] = sum;
+}
+
 template <bool AK, bool BK, int KIND>
 hipError_t dispatch(const GemmArgs& g, int batch, hipStream_t s) {
   if (dma_ok(g, AK, BK)) return run_dma_tile<AK, BK, KIND>(g, batch, s);
-  return run_tile<AK, BK, KIND>(g, batch, s);
+  const hipError_t e = run_tile<AK, BK, KIND>(g, batch, s);
+  if constexpr (KIND == EPI_DGELU) {
+    if (e == hipSuccess && g.colsum) {
+      hipLaunchKernelGGL(colsum_rows_kernel, dim3((unsigned)((g.N + 255) / 256), (unsigned)((g.M + kColsumRows - 1) / kColsumRows)),
+                         dim3(256), 0, s, static_cast<const bf16*>(g.C), g.ldc, g.M, g.N, g.colsum);
+      return hipGetLastError();
+    }
+  }
+  return e;
 }
 
 // Paired launch with tile config (BM, BN, WM, WN) for both problems.
@@ -247,11 +267,13 @@ hipError_t launch_gemm_bf16_pair(const GemmArgs& g0, bool a_k0, bool b_k0, int k
   }
   if (!(a_k0 && !b_k0 && !a_k1 && !b_k1 && kind1 == EPI_STORE_F32)) return hipErrorNotSupported;
   if (kind0 != EPI_STORE && kind0 != EPI_DGELU) return hipErrorNotSupported;
+  if ((g0.colsum && kind0 != EPI_DGELU) || g1.colsum) return hipErrorInvalidValue;
   return kind0 == EPI_DGELU ? pair_dispatch<EPI_DGELU>(g0, g1, s) : pair_dispatch<EPI_STORE>(g0, g1, s);
 }
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, bool a_k, bool b_k, int kind, int batch, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0 || batch <= 0) return hipSuccess;
+  if (g.colsum && (kind != EPI_DGELU || batch != 1)) return hipErrorInvalidValue;
   if (g.nseg < 1 || g.nseg > kMaxSeg || (g.nseg > 1 && g.causal != CAUSAL_NONE && g.causal != CAUSAL_SKIP_UPPER))
     return hipErrorInvalidValue;
   if (a_k && b_k) {  // forward products (X W^T, Q K^T, dctx V^T)

@@ -221,6 +221,17 @@ __device__ __forceinline__ void epi_staged(const GemmArgs& g, f32x16 (&acc)[TM][
   auto put = [&](bf16* region, int rho, int c, const float* v) {  // 4 values, staged row rho, columns c..c+3
     store4_bf16(region + rho * BN + (epi_swz<BN>(rho, c >> 3) << 3) + (c & 7), v);
   };
+  // EPI_DGELU with g.colsum: each thread drains one 8-column chunk (NT is a multiple of
+  // CPR) of several rows and adds the stored bf16 values per 128-row half of the tile.
+  constexpr bool CSUM = KIND == EPI_DGELU;
+  constexpr int HALVES = BM / kColsumRows;
+  static_assert(!CSUM || (NT % CPR == 0 && BM % kColsumRows == 0 && ROUNDS == 1), "column-sum drain layout");
+  const bool csum = CSUM && g.colsum != nullptr;
+  float cs[CSUM ? HALVES : 1][8];
+#pragma unroll
+  for (int hh = 0; hh < (CSUM ? HALVES : 1); ++hh)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) cs[hh][e] = 0.f;
   auto drain = [&](const bf16* region, void* dst, int round, int ncols) {
 #pragma unroll 2
     for (int it = 0; it < RROWS * CPR / NT; ++it) {
@@ -228,7 +239,20 @@ __device__ __forceinline__ void epi_staged(const GemmArgs& g, f32x16 (&acc)[TM][
       const int r = (rho / (32 * TR)) * (BM / WM) + round * TR * 32 + rho % (32 * TR);
       const int m = m0 + r, n = n0 + 8 * c;
       const u32x4 w = *reinterpret_cast<const u32x4*>(region + rho * BN + (epi_swz<BN>(rho, c) << 3));
-      if (m < g.M && n < ncols) *reinterpret_cast<u32x4*>(static_cast<bf16*>(dst) + coff + (int64_t)m * g.ldc + n) = w;
+      if (m < g.M && n < ncols) {
+        *reinterpret_cast<u32x4*>(static_cast<bf16*>(dst) + coff + (int64_t)m * g.ldc + n) = w;
+        if constexpr (CSUM) {
+          if (csum) {
+            const bf16x8 v = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+            for (int hh = 0; hh < HALVES; ++hh)
+              if (r / kColsumRows == hh) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) cs[hh][e] += (float)v[e];
+              }
+          }
+        }
+      }
     }
   };
 
@@ -294,6 +318,28 @@ __device__ __forceinline__ void epi_staged(const GemmArgs& g, f32x16 (&acc)[TM][
     dma_barrier();
     drain(s0, g.C, round, g.N);
     if constexpr (TWO) drain(s1, g.C2, round, KIND == EPI_BIAS_SPLIT ? min(g.N, g.seg_n) : g.N);
+  }
+  if constexpr (CSUM) {
+    if (csum) {  // wave-uniform: the threads of a chunk column add their rows in slot order
+      constexpr int TPC = NT / CPR;
+      float* red = reinterpret_cast<float*>(smem);  // [TPC][HALVES][BN]
+      const int c = tid % CPR, slot = tid / CPR;
+      dma_barrier();  // the drain's reads of the staged tile are done
+#pragma unroll
+      for (int hh = 0; hh < HALVES; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red[(slot * HALVES + hh) * BN + c * 8 + e] = cs[hh][e];
+      dma_barrier();
+      for (int t = tid; t < HALVES * BN; t += NT) {
+        const int hh = t / BN, col = t % BN, n = n0 + col, mrow = m0 + hh * kColsumRows;
+        if (n < g.N && mrow < g.M) {
+          float sum = 0.f;
+#pragma unroll
+          for (int sl = 0; sl < TPC; ++sl) sum += red[(sl * HALVES + hh) * BN + col];
+          g.colsum[(int64_t)(mrow / kColsumRows) * g.N + n] = sum;
+        }
+      }
+    }
   }
 }
 

@@ -14,6 +14,7 @@ hipError_t run(const GemmArgs& g, int batch, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm_f32(const GemmArgs& g, bool a_k, bool b_k, int kind, int batch, hipStream_t s) {
+  if (g.colsum) return hipErrorInvalidValue;  // the fused column sums are a bf16-launcher feature
   if (g.M <= 0 || g.N <= 0 || batch <= 0) return hipSuccess;
   if (a_k && b_k) {
     switch (kind) {

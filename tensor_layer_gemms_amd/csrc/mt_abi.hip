@@ -149,6 +149,7 @@ int64_t dgrad_split_floats(const Dims& d) {
 size_t colsum_floats(const Dims& d) {
   size_t n = colsum_partial_floats((int)d.M, (int)d.h, 1);
   n = std::max(n, colsum_partial_floats((int)d.M, (int)d.ft, 0));
+  n = std::max(n, gemm_colsum_floats((int)d.M, (int)d.ft));
   n = std::max(n, colsum_partial_floats((int)d.M, (int)d.qkv, 0));
   if (ln_bwd_sums_supported((int)d.h)) n = std::max(n, ln_bwd_sums_partial_floats((int)d.M, (int)d.h, 4));
   return n;
@@ -186,7 +187,7 @@ struct MlpWs {
 size_t carve_mlp_ws(const Dims& d, void* base, MlpWs* w) {
   Carver c(base);
   w->da = c.take(d.M * d.ft * d.es);
-  w->part = c.take<float>(colsum_partial_floats((int)d.M, (int)d.ft, 0) * 4);
+  w->part = c.take<float>(std::max(colsum_partial_floats((int)d.M, (int)d.ft, 0), gemm_colsum_floats((int)d.M, (int)d.ft)) * 4);
   return c.off;
 }
 
@@ -604,14 +605,17 @@ int layer_bwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, cons
       return launch_colsum(bf, 0, dout, false, nullptr, false, nullptr, nullptr, gr.b_fc2, nullptr, ws.part, M,
                            (int)d.h, stream);
     });
+  // (bf16: the dgrad epilogue also forms db_fc1's column sums of dA per 128 rows)
   q.run("fc2_dgrad_wgrad", 2 * gflop(d.M, d.ft, d.h), 0, [&] {
     GemmArgs dg = plain(dout, d.h, w.w_fc2, d.ft, ws.da, d.ft, d.M, d.ft, d.h);
     dg.aux = sv.a;
+    if (bf) dg.colsum = ws.part;
     const GemmArgs wg = plain(dout, d.h, sv.z, d.ft, gr.w_fc2, d.ft, d.h, d.ft, d.M);
     return gemm_dgrad_wgrad(d, dg, EPI_DGELU, wg, stream);
   });
   // B2 FC1: db_fc1, dW1 = dA^T V2, dV2 = dA W1 (partial)
-  q.run("db_fc1", 0, d.M * d.ft * es, [&] {
+  q.run("db_fc1", 0, bf ? 4.0 * gemm_colsum_floats(M, (int)d.ft) : d.M * d.ft * es, [&] {
+    if (bf) return launch_colsum_final(ws.part, gr.b_fc1, (M + kColsumRows - 1) / kColsumRows, (int)d.ft, stream);
     return launch_colsum(bf, 0, ws.da, false, nullptr, false, nullptr, nullptr, gr.b_fc1, nullptr, ws.part, M,
                          (int)d.ft, stream);
   });
@@ -687,10 +691,13 @@ int mlp_bwd_impl(const Dims& d, const void* x, const void* w1, const void* w2, c
   q.run("fc2_dgrad_wgrad", 2 * gflop(d.M, d.ft, d.h), 0, [&] {
     GemmArgs dg = plain(dy, d.h, w2, d.ft, ws.da, d.ft, d.M, d.ft, d.h);
     dg.aux = sv.a;
+    if (d.bf16) dg.colsum = ws.part;  // db_fc1's column sums of dA per 128 rows
     const GemmArgs wg = plain(dy, d.h, sv.z, d.ft, dw2, d.ft, d.h, d.ft, d.M);
     return gemm_dgrad_wgrad(d, dg, EPI_DGELU, wg, stream);
   });
-  q.run("db_fc1", 0, (double)d.M * d.ft * d.es, [&] {
+  q.run("db_fc1", 0, d.bf16 ? 4.0 * gemm_colsum_floats((int)d.M, (int)d.ft) : (double)d.M * d.ft * d.es, [&] {
+    if (d.bf16)
+      return launch_colsum_final(ws.part, db1, ((int)d.M + kColsumRows - 1) / kColsumRows, (int)d.ft, stream);
     return launch_colsum(d.bf16, 0, ws.da, false, nullptr, false, nullptr, nullptr, db1, nullptr, ws.part, (int)d.M,
                          (int)d.ft, stream);
   });

@@ -719,6 +719,14 @@ size_t colsum_partial_floats(int rows, int cols, int mode) {
   return (size_t)nrb * cols * (mode == 1 ? 2 : 1);
 }
 
+hipError_t launch_colsum_final(const float* part, float* out, int nrb, int cols, hipStream_t s) {
+  if (nrb <= 0 || cols <= 0) return hipSuccess;
+  if (cols % 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(colsum_final_kernel, colsum_final_grid(cols, 1), dim3(64 * kFinalWaves), 0, s, part, out, nullptr,
+                     nullptr, nullptr, nrb, cols);
+  return hipGetLastError();
+}
+
 hipError_t launch_colsum(bool is_bf16, int mode, const void* a, bool a_f32, const void* x, bool x_f32,
                          const float* mean, const float* rstd, float* out0, float* out1, float* partial, int rows,
                          int cols, hipStream_t s) {

@@ -56,6 +56,9 @@ hipError_t launch_colsum(bool is_bf16, int mode, const void* a, bool a_f32, cons
                          const float* mean, const float* rstd, float* out0, float* out1, float* partial, int rows,
                          int cols, hipStream_t s);
 
+// out[c] = sum over the nrb partial rows part[r, c] (fp32 [nrb][cols]), in row order.
+hipError_t launch_colsum_final(const float* part, float* out, int nrb, int cols, hipStream_t s);
+
 // out = x2 + y + bias (x2 fp32, bias broadcast over rows).
 hipError_t launch_add_bias_residual(bool is_bf16, const float* x2, const void* y, const void* bias, void* out,
                                     int rows, int h, hipStream_t s);
