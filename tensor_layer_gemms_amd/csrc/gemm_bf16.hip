@@ -61,7 +61,7 @@ hipError_t run(const GemmArgs& g, int batch, hipStream_t s) {
 template <bool AK, bool BK, int BM, int BN, int KT, int WM, int WN, int KIND>
 hipError_t run_dma(const GemmArgs& g, int batch, hipStream_t s) {
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_dma_kernel<AK, BK, BM, BN, KT, 2, WM, WN, KIND>), dim3(tiles, batch), dim3(64 * WM * WN),
+  hipLaunchKernelGGL((gemm_dma_kernel<bf16, AK, BK, BM, BN, KT, 2, WM, WN, KIND>), dim3(tiles, batch), dim3(64 * WM * WN),
                      0, s, g);
   return hipGetLastError();
 }
@@ -109,21 +109,7 @@ hipError_t run_dma_tile(const GemmArgs& g, int batch, hipStream_t s) {
 }
 
 // Whether the DMA kernel can address the problem (see the file comment).
-bool dma_ok(const GemmArgs& g, bool a_k, bool b_k) {
-  auto a16 = [](const void* p) { return ((uintptr_t)p & 15u) == 0; };
-  if (g.M % 8 || g.N % 8 || g.K % 8 || g.lda % 8 || g.ldb % 8) return false;
-  if (g.a_so % 8 || g.a_si % 8 || g.b_so % 8 || g.b_si % 8) return false;
-  // the staged epilogue writes 16-byte row chunks of C and C2
-  if (g.ldc % 8 || g.c_so % 8 || g.c_si % 8 || g.seg_n % 8 || !a16(g.C) || !a16(g.C2)) return false;
-  for (int s = 0; s < g.nseg; ++s)
-    if (!a16(g.seg_a[s]) || !a16(g.seg_b[s])) return false;
-  const uint64_t lim = 0xFFFFFFF0ull;
-  // largest byte offset from a tile's base: k-contiguous 256 rows of ld, m-contiguous
-  // K rows of ld
-  const uint64_t a_span = (uint64_t)(a_k ? 256 : g.K) * (uint64_t)g.lda * 2u;
-  const uint64_t b_span = (uint64_t)(b_k ? 256 : g.K) * (uint64_t)g.ldb * 2u;
-  return a_span < lim && b_span < lim;
-}
+bool dma_ok(const GemmArgs& g, bool a_k, bool b_k) { return dma_addressable(g, a_k, b_k, 2); }
 
 // Column sums of C over each 128-row block (the register-staged kernel's epilogue does
 // not form them): thread = one column, rows in order, fp32.

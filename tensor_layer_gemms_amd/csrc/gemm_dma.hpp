@@ -1,14 +1,19 @@
-// MFMA GEMM fed by LDS-DMA loads, for every operand layout of the layer.
+// MFMA GEMM fed by LDS-DMA loads, for every operand layout of the layer, in bf16
+// (v_mfma_f32_32x32x16_bf16, k-step 64) or fp32 (v_mfma_f32_32x32x2_f32, k-step 32).
 //
 // Each lane's 16-byte global load is written by the memory system straight into LDS
 // (buffer_load ... lds): no staging registers, no LDS store instructions, no register
 // transposes. A k-contiguous operand tile is kept in LDS as rows of k ([rows][BK]) and
 // read with ds_read_b128; an m-contiguous operand tile (token-strided wgrad operands,
 // the weight of a dgrad, V in P V) is kept as it lies in memory ([BK][rows]) and read
-// with the transposing ds_read_b64_tr_b16, which hands each lane 4 consecutive k of one
-// m. Out-of-range rows and the k tail read zeros through the buffer resource's range
-// check. Two LDS stages alternate: one is multiplied while the loads of the next fill the
-// other.
+// with the transposing ds_read_b64_tr_b16 (bf16), which hands each lane 4 consecutive k
+// of one m, or with one ds_read_b32 per k (fp32). Out-of-range rows and the k tail read
+// zeros through the buffer resource's range check. Two LDS stages alternate: one is
+// multiplied while the loads of the next fill the other. Both element types use the same
+// LDS geometry in 16-byte chunks (a k-contiguous row is 128 bytes: 64 bf16 or 32 fp32),
+// the same loaders, schedule and accumulator layout; they differ in the fragment reads,
+// the MFMA instruction and the epilogue (bf16 outputs are staged through LDS, fp32
+// outputs stored by each lane).
 #pragma once
 
 #include "gemm_kernels.hpp"
@@ -48,12 +53,13 @@ __device__ __forceinline__ void dma_barrier() {
 }
 
 // LDS placement of 16-byte chunks.
-// k-contiguous tile [rows][BK] (BK = 32 or 64): chunk c of row r sits at c ^ f(r); f
-// spreads the 16 rows one ds_read_b128 quarter-wave touches (same chunk) over the 64
-// banks.
-template <int BK>
+// k-contiguous tile [rows][BK] (KCH = 8 or 4 chunks per row): chunk c of row r sits at
+// c ^ f(r); f spreads the 16 rows one ds_read_b128 quarter-wave touches (same chunk) over
+// the 64 banks.
+template <int KCH>
 __device__ __forceinline__ int kc_swz(int row, int chunk) {
-  if constexpr (BK == 64) return chunk ^ ((row >> 1) & 7);
+  static_assert(KCH == 8 || KCH == 4, "k-contiguous rows of 128 or 64 bytes");
+  if constexpr (KCH == 8) return chunk ^ ((row >> 1) & 7);
   else return chunk ^ ((row >> 2) & 3);
 }
 // m-contiguous tile [BK][rows] (rows a power of two >= 128): chunk c of k-row r sits at
@@ -62,22 +68,25 @@ __device__ __forceinline__ int kc_swz(int row, int chunk) {
 // bank groups.
 __device__ __forceinline__ int mc_swz(int krow, int chunk) { return chunk ^ ((krow & 3) << 2); }
 
-// DMA loads of one ROWS x BK operand tile (ROWS along m or n). The tile is 2 ROWS BK
-// bytes = ROWS BK / 512 wave instructions of 1 KB. Lane L of instruction q fills LDS
-// bytes [q 1024 + 16 L, +16): LDS row q RPI + L / CPR, stored chunk L % CPR, which holds
-// the logical chunk the swizzle maps there.
+// DMA loads of one ROWS x BK operand tile (ROWS along m or n) of element type T. The
+// tile is ROWS BK sizeof(T) bytes = INSTR wave instructions of 1 KB. Lane L of
+// instruction q fills LDS bytes [q 1024 + 16 L, +16): LDS row q RPI + L / CPR, stored
+// chunk L % CPR, which holds the logical chunk the swizzle maps there.
 // Loader waves: with 8 waves (two per SIMD) only waves 0-3, one per SIMD, issue the
 // loads (wave w instructions w, w + 4, ...), so the other wave of every SIMD never waits
 // for loads of its own and runs its MFMAs while its partner issues and waits; measured on
 // the layer's shapes: forward GEMMs 4-15% faster, input and weight gradients 3-6%, than
 // with every wave issuing an equal share at the same point of the step. With 4 waves
 // every wave issues (instructions w, w + 4, ...).
-template <int ROWS, int BK, int NW, bool KC>
+template <typename T, int ROWS, int BK, int NW, bool KC>
 struct DmaLoader {
-  static constexpr int ROW_ELEMS = KC ? BK : ROWS;  // elements per LDS row
-  static constexpr int CPR = ROW_ELEMS / 8;          // 16-byte chunks per LDS row
-  static constexpr int RPI = 64 / CPR;               // LDS rows per wave instruction
-  static constexpr int INSTR = ROWS * BK / 512;      // instructions per tile
+  static constexpr int ES = sizeof(T), EPC = 16 / ES;  // bytes per element, elements per chunk
+  static constexpr int ROW_ELEMS = KC ? BK : ROWS;     // elements per LDS row
+  static constexpr int CPR = ROW_ELEMS / EPC;          // 16-byte chunks per LDS row
+  static constexpr int KCH = BK / EPC;                 // chunks per k-contiguous row
+  static constexpr int RPI = 64 / CPR;                 // LDS rows per wave instruction
+  static constexpr int INSTR = ROWS * BK * ES / 1024;  // instructions per tile
+  static constexpr int IEL = 1024 / ES;                // elements per instruction
   static constexpr int LW = NW == 8 ? 4 : NW;        // loader waves
   static constexpr int PER_WAVE = INSTR / LW;        // instructions per loader wave
   static_assert(INSTR % LW == 0, "tile must split evenly over the loader waves");
@@ -90,14 +99,14 @@ struct DmaLoader {
   // KC: base = element (row0, 0), rows_valid rows left; the range ends after them.
   // !KC: base = element (k = 0, row0); the range is the K x ld block; rows past
   // rows_valid are masked per lane.
-  __device__ __forceinline__ void init(const bf16* base, int64_t ld_, int rows_valid_, int kdim) {
+  __device__ __forceinline__ void init(const T* base, int64_t ld_, int rows_valid_, int kdim) {
     ld = ld_;
     rows_valid = rows_valid_;
     uint64_t bytes;
-    if constexpr (KC) bytes = rows_valid_ > 0 ? (uint64_t)rows_valid_ * (uint64_t)ld_ * 2u : 0u;
-    else bytes = (uint64_t)kdim * (uint64_t)ld_ * 2u;
+    if constexpr (KC) bytes = rows_valid_ > 0 ? (uint64_t)rows_valid_ * (uint64_t)ld_ * ES : 0u;
+    else bytes = (uint64_t)kdim * (uint64_t)ld_ * ES;
     invalid = bytes < 0xFFFFFFF0ull ? (uint32_t)bytes : 0xFFFFFFF0u;
-    rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base), (short)0, (int)invalid, 0x00020000);
+    rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base), (short)0, (int)invalid, 0x00020000);
   }
 
   // Fast path of a full k-step (k0 + BK <= kend, every lane's k in range): the lane's byte
@@ -115,26 +124,26 @@ struct DmaLoader {
       const int r = q * RPI + lane / CPR;
       const int p = lane % CPR;
       if constexpr (KC) {
-        vo[i] = (uint32_t)(r * ld + kc_swz<BK>(r, p) * 8) * 2u;
+        vo[i] = (uint32_t)(r * ld + kc_swz<KCH>(r, p) * EPC) * ES;
       } else {
-        const int m = mc_swz(r, p) * 8;
-        vo[i] = m < rows_valid ? (uint32_t)(r * ld + m) * 2u : invalid;
+        const int m = mc_swz(r, p) * EPC;
+        vo[i] = m < rows_valid ? (uint32_t)(r * ld + m) * ES : invalid;
       }
     }
   }
-  __device__ __forceinline__ void issue_full(bf16* lds_stage, int k0, const uint32_t* vo, int wave) const {
+  __device__ __forceinline__ void issue_full(T* lds_stage, int k0, const uint32_t* vo, int wave) const {
     if (wave >= LW) return;  // wave-uniform
-    const uint32_t soff = KC ? (uint32_t)k0 * 2u : (uint32_t)k0 * (uint32_t)ld * 2u;
+    const uint32_t soff = KC ? (uint32_t)k0 * ES : (uint32_t)k0 * (uint32_t)ld * ES;
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int q = wave + i * LW;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(lds_stage + q * 512), 16, vo[i], soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(lds_stage + q * IEL), 16, vo[i], soff, 0, 0);
     }
   }
 
   // General path (tail steps, causal k ranges, segmented m-contiguous operands): every
   // lane checks its k against kend (and its m against rows_valid) each step.
-  __device__ __forceinline__ void issue(bf16* lds_stage, int k0, int kend, int wave, int lane) const {
+  __device__ __forceinline__ void issue(T* lds_stage, int k0, int kend, int wave, int lane) const {
     if (wave >= LW) return;  // wave-uniform
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
@@ -143,21 +152,30 @@ struct DmaLoader {
       const int p = lane % CPR;
       uint32_t off;
       if constexpr (KC) {
-        const int k = k0 + kc_swz<BK>(r, p) * 8;
-        off = k < kend ? (uint32_t)(r * ld + k) * 2u : invalid;
+        const int k = k0 + kc_swz<KCH>(r, p) * EPC;
+        off = k < kend ? (uint32_t)(r * ld + k) * ES : invalid;
       } else {
-        const int k = k0 + r, m = mc_swz(r, p) * 8;
-        off = (k < kend && m < rows_valid) ? (uint32_t)(k * ld + m) * 2u : invalid;
+        const int k = k0 + r, m = mc_swz(r, p) * EPC;
+        off = (k < kend && m < rows_valid) ? (uint32_t)(k * ld + m) * ES : invalid;
       }
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(lds_stage + q * 512), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(lds_stage + q * IEL), 16, off, 0, 0, 0);
     }
   }
 };
 
-// Operand fragment reads for the 32x32x16 MFMA: lane l gets rows (l & 31) of the
-// 32-row block and k = 8 (l >> 5) + 0..7 of the 16-k step.
+// Operand fragment reads, one slice (16 k of bf16, 8 k of fp32) per call.
+// bf16, for the 32x32x16 MFMA: lane l gets row (l & 31) of the 32-row block and
+// k = 8 (l >> 5) + 0..7 of the slice.
+// fp32, for four 32x32x2 MFMAs: lane l gets row (l & 31) and k = 4 (l >> 5) + 0..3 of
+// the slice; MFMA e takes value e, i.e. contracts the slice's k = e and k = 4 + e (the
+// two lane halves), the same pairing for both operands, so the four cover the slice.
+template <typename T, int ROWS, int BK, bool KC>
+struct FragReader;
+
 template <int ROWS, int BK, bool KC>
-struct FragReader {
+struct FragReader<bf16, ROWS, BK, KC> {
+  using Frag = bf16x8;
+  static constexpr int READS = KC ? 1 : 2;  // LDS read instructions per call
   int off;  // per-lane element offset of the block at k-step 0
   int row;  // KC: this lane's tile row
   __device__ __forceinline__ void init(int row0, int lane) {
@@ -175,7 +193,7 @@ struct FragReader {
   }
   __device__ __forceinline__ bf16x8 read(const bf16* tile, int ks, int lane) const {
     if constexpr (KC) {
-      return *reinterpret_cast<const bf16x8*>(tile + off + (kc_swz<BK>(row, 2 * ks + (lane >> 5)) << 3));
+      return *reinterpret_cast<const bf16x8*>(tile + off + (kc_swz<BK / 8>(row, 2 * ks + (lane >> 5)) << 3));
     } else {
       const bf16* p = tile + off + ks * 16 * ROWS;
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(p));
@@ -185,6 +203,49 @@ struct FragReader {
     }
   }
 };
+
+template <int ROWS, int BK, bool KC>
+struct FragReader<float, ROWS, BK, KC> {
+  using Frag = f32x4;
+  static constexpr int READS = KC ? 1 : 4;
+  int off[KC ? 1 : 4];  // per-lane element offsets at k-step 0 (m-contiguous: one per k-row)
+  int row;
+  __device__ __forceinline__ void init(int row0, int lane) {
+    if constexpr (KC) {
+      row = row0 + (lane & 31);
+      off[0] = row * BK;
+    } else {
+      // k-row 4 (l >> 5) + e of the slice, column m = row0 + (l & 31); chunk m / 4 of
+      // k-row r sits at mc_swz(r, m / 4), and r & 3 = e for every slice.
+      const int m = row0 + (lane & 31), kr = 4 * (lane >> 5);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) off[e] = (kr + e) * ROWS + (mc_swz(kr + e, m >> 2) << 2) + (m & 3);
+    }
+  }
+  __device__ __forceinline__ f32x4 read(const float* tile, int ks, int lane) const {
+    if constexpr (KC) {
+      return *reinterpret_cast<const f32x4*>(tile + off[0] + (kc_swz<BK / 4>(row, 2 * ks + (lane >> 5)) << 2));
+    } else {
+      const float* p = tile + ks * 8 * ROWS;
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = p[off[e]];
+      return v;
+    }
+  }
+};
+
+// acc += the slice's product: bf16 one 32x32x16 MFMA, fp32 four 32x32x2 MFMAs. The B
+// fragment goes first, so lane l holds accumulator row (l & 31) of the A side.
+__device__ __forceinline__ void mfma_frag(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mfma_frag(f32x16& acc, const f32x4& a, const f32x4& b) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(b[e], a[e], acc, 0, 0, 0);
+}
+template <typename T>
+constexpr int kMfmaPerFrag = sizeof(T) == 2 ? 1 : 4;
 
 // LDS placement of the 16-byte chunks of a staged bf16 output tile [BM][BN]: chunk c of
 // row r sits at c ^ f(r), so the 16 consecutive rows that one accumulator write covers
@@ -344,16 +405,20 @@ __device__ __forceinline__ void epi_staged(const GemmArgs& g, f32x16 (&acc)[TM][
 }
 
 // One output tile: bid = tile index of the problem, z = batch index, smem = the
-// launch's LDS ring (at least NS (BM + BN) BK elements).
-template <bool A_K, bool B_K, int BM, int BN, int BK, int NS, int WM, int WN, int KIND>
-__device__ __forceinline__ void gemm_dma_tile(const GemmArgs& g, int bid, int z, bf16* smem) {
+// launch's LDS ring (at least NS (BM + BN) BK elements). T = bf16 or float: the type of
+// the operands and of the outputs the epilogue writes (fp32 weight gradients aside).
+template <typename T, bool A_K, bool B_K, int BM, int BN, int BK, int NS, int WM, int WN, int KIND>
+__device__ __forceinline__ void gemm_dma_tile(const GemmArgs& g, int bid, int z, T* smem) {
+  constexpr bool F32 = sizeof(T) == 4;
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
-  constexpr int STAGE = (BM + BN) * BK;  // bf16 elements per stage
+  constexpr int STAGE = (BM + BN) * BK;  // elements per stage
+  static_assert(BK * sizeof(T) == 128, "k-contiguous LDS rows of 128 bytes");
   static_assert(TM >= 1 && TN >= 1 && BM % (WM * 32) == 0 && BN % (WN * 32) == 0, "wave tile of 32x32 blocks");
-  static_assert(KIND == EPI_STORE_F32 ||
+  static_assert(F32 || KIND == EPI_STORE_F32 ||
                     ((KIND == EPI_BIAS_GELU || KIND == EPI_BIAS_SPLIT) ? 2 * (BM / TM) * BN : BM * BN) <= NS * STAGE,
                 "the staged epilogue fits the LDS ring");
+  static_assert(!F32 || KIND != EPI_BIAS_SPLIT, "the hi/lo split is a bf16 epilogue");
 
   dma_lds_escape(smem);
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -370,17 +435,21 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs& g, int bid, int z,
   const int64_t boff = zo * g.b_so + zi * g.b_si + (B_K ? (int64_t)n0 * g.ldb : (int64_t)n0);
   const int nseg = n0 < g.seg_n ? g.nseg : 1;
 
-  DmaLoader<BM, BK, NW, A_K> la[kMaxSeg];
-  DmaLoader<BN, BK, NW, B_K> lb[kMaxSeg];
+  using LA = DmaLoader<T, BM, BK, NW, A_K>;
+  using LB = DmaLoader<T, BN, BK, NW, B_K>;
+  LA la[kMaxSeg];
+  LB lb[kMaxSeg];
 #pragma unroll
   for (int s = 0; s < kMaxSeg; ++s) {
     if (s < nseg) {
-      la[s].init(static_cast<const bf16*>(g.seg_a[s]) + aoff, g.lda, g.M - m0, g.K);
-      lb[s].init(static_cast<const bf16*>(g.seg_b[s]) + boff, g.ldb, (s ? min(g.N, g.seg_n) : g.N) - n0, g.K);
+      la[s].init(static_cast<const T*>(g.seg_a[s]) + aoff, g.lda, g.M - m0, g.K);
+      lb[s].init(static_cast<const T*>(g.seg_b[s]) + boff, g.ldb, (s ? min(g.N, g.seg_n) : g.N) - n0, g.K);
     }
   }
-  FragReader<BM, BK, A_K> ra[TM];
-  FragReader<BN, BK, B_K> rb[TN];
+  using RA = FragReader<T, BM, BK, A_K>;
+  using RB = FragReader<T, BN, BK, B_K>;
+  RA ra[TM];
+  RB rb[TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i) ra[i].init(wm0 + i * 32, lane);
 #pragma unroll
@@ -399,8 +468,6 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs& g, int bid, int z,
   // per-lane offsets of the full-step loads (shared by the segments, whose operands have
   // the same strides; an m-contiguous operand masks per lane, so with several segments,
   // whose ranges differ, it stays on the general path)
-  using LA = DmaLoader<BM, BK, NW, A_K>;
-  using LB = DmaLoader<BN, BK, NW, B_K>;
   uint32_t va[LA::PER_WAVE], vb[LB::PER_WAVE];
   la[0].offsets(wave, lane, va);
   lb[0].offsets(wave, lane, vb);
@@ -411,7 +478,7 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs& g, int bid, int z,
   auto issue = [&](int t) {  // loads of step t into stage t % NS
     const int sg = (t >= nk1) + (t >= 2 * nk1);
     const int k0 = kbeg + (t - sg * nk1) * BK;
-    bf16* st = smem + (t % NS) * STAGE;
+    T* st = smem + (t % NS) * STAGE;
     if (full_ok && k0 + BK <= kend) {
       if (sg == 0) {
         la[0].issue_full(st, k0, va, wave);
@@ -451,12 +518,13 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs& g, int bid, int z,
   //   the last slice's MFMAs run under them, so the barrier's latency is covered by
   //   matrix work (5-7% on the paired backward launches; 2-3% slower on the forward ones).
   static_assert(NS == 2, "two-stage ring");
-  constexpr int KS = BK / 16;
+  constexpr int KS = BK * sizeof(T) / 32;  // slices per step (16 k of bf16, 8 k of fp32)
   static_assert(KS % 2 == 0, "slice buffers alternate; every step starts in buffer 0");
-  constexpr int NM = TM * TN;                                  // MFMAs per slice
-  constexpr int NR = TM * (A_K ? 1 : 2) + TN * (B_K ? 1 : 2);  // LDS read instructions per slice
-  bf16x8 af[2][TM], bfr[2][TN];
-  auto read_slice = [&](const bf16* sA, int ks, int b) {
+  constexpr int NM = TM * TN * kMfmaPerFrag<T>;            // MFMAs per slice
+  constexpr int NR = TM * RA::READS + TN * RB::READS;      // LDS read instructions per slice
+  typename RA::Frag af[2][TM];
+  typename RB::Frag bfr[2][TN];
+  auto read_slice = [&](const T* sA, int ks, int b) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) af[b][i] = ra[i].read(sA, ks, lane);
 #pragma unroll
@@ -466,8 +534,7 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs& g, int bid, int z,
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[b][j], af[b][i], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < TN; ++j) mfma_frag(acc[i][j], af[b][i], bfr[b][j]);
   };
   auto interleave = [&]() {  // instruction order: next slice's reads between the first MFMAs
     constexpr int q = NR / NM, r = NR % NM;
@@ -478,7 +545,7 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs& g, int bid, int z,
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
   };
-  auto inner_slices = [&](const bf16* sA) {  // slices 0 .. KS - 2, each reading the next
+  auto inner_slices = [&](const T* sA) {  // slices 0 .. KS - 2, each reading the next
 #pragma unroll
     for (int ks = 0; ks + 1 < KS; ++ks) {
       read_slice(sA, ks + 1, (ks + 1) & 1);
@@ -492,7 +559,7 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs& g, int bid, int z,
       for (int t = 0; t < nk; ++t) {
         wait_vmcnt<0>();
         dma_barrier();
-        const bf16* sA = smem + (t & 1) * STAGE;
+        const T* sA = smem + (t & 1) * STAGE;
         read_slice(sA, 0, 0);
         if (t + 1 < nk) issue(t + 1);  // after the first reads, which fly under the issue
         inner_slices(sA);
@@ -517,8 +584,9 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs& g, int bid, int z,
 
   const int64_t coff = zo * g.c_so + zi * g.c_si;
   const int64_t voff = (int64_t)z * g.vec_bs;
-  if constexpr (KIND == EPI_STORE_F32) {
-    // fp32 tiles do not fit the LDS ring; each lane stores its 16-byte row pieces.
+  if constexpr (KIND == EPI_STORE_F32 || F32) {
+    // fp32 tiles do not fit the LDS ring; each lane stores its 16-byte row pieces (fp32
+    // outputs of the other epilogues value by value; N is a multiple of 4 here).
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int m = m0 + wm0 + i * 32 + (lane & 31);
@@ -528,7 +596,14 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs& g, int bid, int z,
         for (int q = 0; q < 4; ++q) {
           const int n = n0 + wn0 + j * 32 + q * 8 + (lane >> 5) * 4;
           float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          if (m < g.M && n < g.N) epi_store4<KIND>(g, coff, voff, m, n, v);
+          if (m < g.M && n < g.N) {
+            if constexpr (KIND == EPI_STORE_F32) {
+              epi_store4<KIND>(g, coff, voff, m, n, v);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) epi_store<float, KIND>(g, coff, voff, m, n + e, v[e]);
+            }
+          }
         }
       }
     }
@@ -537,10 +612,29 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs& g, int bid, int z,
   }
 }
 
-template <bool A_K, bool B_K, int BM, int BN, int BK, int NS, int WM, int WN, int KIND>
+template <typename T, bool A_K, bool B_K, int BM, int BN, int BK, int NS, int WM, int WN, int KIND>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(1024))) bf16 smem[NS * (BM + BN) * BK];
-  gemm_dma_tile<A_K, B_K, BM, BN, BK, NS, WM, WN, KIND>(g, blockIdx.x, blockIdx.y, smem);
+  __shared__ __attribute__((aligned(1024))) T smem[NS * (BM + BN) * BK];
+  gemm_dma_tile<T, A_K, B_K, BM, BN, BK, NS, WM, WN, KIND>(g, blockIdx.x, blockIdx.y, smem);
+}
+
+// Whether the DMA kernel can address the problem with elements of es bytes (2 or 4):
+// every contiguous dimension, stride and batch offset a whole number of 16-byte chunks,
+// 16-byte aligned bases (the bf16 epilogue writes 16-byte row chunks of C and C2, the
+// fp32 one 16-byte pieces), and every byte offset from a tile's base below 4 GiB (the
+// buffer resource's 32-bit range): k-contiguous 256 rows of ld, m-contiguous K rows.
+inline bool dma_addressable(const GemmArgs& g, bool a_k, bool b_k, int es) {
+  const int64_t epc = 16 / es;
+  auto a16 = [](const void* p) { return ((uintptr_t)p & 15u) == 0; };
+  if (g.M % epc || g.N % epc || g.K % epc || g.lda % epc || g.ldb % epc) return false;
+  if (g.a_so % epc || g.a_si % epc || g.b_so % epc || g.b_si % epc) return false;
+  if (g.ldc % epc || g.c_so % epc || g.c_si % epc || g.seg_n % epc || !a16(g.C) || !a16(g.C2)) return false;
+  for (int s = 0; s < g.nseg; ++s)
+    if (!a16(g.seg_a[s]) || !a16(g.seg_b[s])) return false;
+  const uint64_t lim = 0xFFFFFFF0ull;
+  const uint64_t a_span = (uint64_t)(a_k ? 256 : g.K) * (uint64_t)g.lda * (uint64_t)es;
+  const uint64_t b_span = (uint64_t)(b_k ? 256 : g.K) * (uint64_t)g.ldb * (uint64_t)es;
+  return a_span < lim && b_span < lim;
 }
 
 // Compile-time description of one problem of a paired launch.
@@ -548,7 +642,7 @@ template <bool A_K, bool B_K, int BM, int BN, int BK, int WM, int WN, int KIND>
 struct DmaProblem {
   static constexpr int kBM = BM, kBN = BN, kThreads = 64 * WM * WN, kSmem = 2 * (BM + BN) * BK;
   static __device__ __forceinline__ void tile(const GemmArgs& g, int bid, int z, bf16* smem) {
-    gemm_dma_tile<A_K, B_K, BM, BN, BK, 2, WM, WN, KIND>(g, bid, z, smem);
+    gemm_dma_tile<bf16, A_K, B_K, BM, BN, BK, 2, WM, WN, KIND>(g, bid, z, smem);
   }
 };
 

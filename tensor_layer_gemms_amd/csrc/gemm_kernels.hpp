@@ -7,7 +7,7 @@
 namespace mt {
 
 // ---------------------------------------------------------------------------- epilogue
-// Per-element epilogue (fp32 SIMT path).
+// Per-element epilogue (fp32 outputs: the fp32 DMA MFMA path and the SIMT fallback).
 template <typename T, int KIND>
 __device__ __forceinline__ void epi_store(const GemmArgs& g, int64_t coff, int64_t voff, int m, int n, float v) {
   const int64_t idx = coff + (int64_t)m * g.ldc + n;
@@ -355,8 +355,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
   }
 }
 
-// ---------------------------------------------------------------------------- fp32 SIMT
-// fp32 path: 64x64 tiles, 16-deep k steps through LDS, 4x4 outputs per thread, fp32
+// ---------------------------------------------------------------------------- fp32 SIMT (fallback)
+// fp32 problems the DMA kernel cannot address: 64x64 tiles, 16-deep k steps through LDS, 4x4 outputs per thread, fp32
 // fused multiply-add. Same operand layouts, causal modes and epilogues as the MFMA path.
 template <bool A_K, bool B_K, int KIND>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
