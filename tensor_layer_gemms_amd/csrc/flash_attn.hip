@@ -408,6 +408,54 @@ __device__ __forceinline__ void store_rows(bf16* out, const f32x16* acc, float s
     }
 }
 
+// Column sums of one wave's 32 rows of a stored gradient (acc * scale rounded to bf16 as
+// store_rows rounds it; rows past the sequence 0) into out[0 .. D). The wave puts its rows
+// in its own LDS region t (32 rows of D + 4 floats); lane l then adds 4 consecutive
+// columns over a run of rows (RS runs of 32 / RS rows per column group, as many as the
+// 64 lanes allow) and the runs' sums are added across lanes, run 0 first. LDS operations
+// of one wave complete in order, so the exchange needs no barrier.
+template <int D>
+__device__ __forceinline__ void wave_colsum(float* out, const f32x16* acc, float scale, bool ok, float* t, int lane) {
+  constexpr int LD = D + 4, G = D / 4;  // row pitch, column groups
+  constexpr int RS = G <= 16 ? 4 : G <= 32 ? 2 : 1, RPL = 32 / RS;
+  float* rowp = t + (lane & 31) * LD + 4 * (lane >> 5);
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = ok ? (float)(bf16)(acc[nb][4 * q + e] * scale) : 0.f;
+      *reinterpret_cast<f32x4*>(rowp + 32 * nb + 8 * q) = v;
+    }
+  const int g = lane % G, run = lane / G;
+  f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+  if (run < RS) {
+    const float* p = t + run * RPL * LD + 4 * g;
+#pragma unroll 8
+    for (int r = 0; r < RPL; ++r) sum += *reinterpret_cast<const f32x4*>(p + r * LD);
+  }
+  if constexpr (RS == 4) {  // G = 16: runs in lanes g, g + 16, g + 32, g + 48
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a = sum[e] + __shfl_xor(sum[e], 16);  // run 0 + run 1 (run 2 + run 3)
+      sum[e] = a + __shfl_xor(a, 32);
+    }
+  } else if constexpr (RS == 2) {  // G = 32: runs in lanes g, g + 32
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sum[e] += __shfl_xor(sum[e], 32);
+  }
+  if (lane < G) *reinterpret_cast<f32x4*>(out + 4 * g) = sum;
+}
+// LDS floats of the parked partials of groups 1 .. NG - 1 (placed first in the rings), and
+// the column-sum region of wave wv of group 0 after them.
+template <int D, int NG>
+constexpr int park_floats() { return (NG - 1) * (D / 32) * 16 * 128; }
+template <int D, int NG>
+__device__ __forceinline__ float* colsum_region(bf16* smem, int wv) {
+  return reinterpret_cast<float*>(smem) + park_floats<D, NG>() + wv * 32 * (D + 4);
+}
+
 // Stage layouts of the backward rings (elements): NT tiles of [32][D] (Q or K first, then
 // dO or V, then the Q or K remainders when compensated), and for the key part 1 KB for L
 // and 1 KB for D of the stage's 32 queries (one DMA instruction each; the first 128 bytes
@@ -599,6 +647,12 @@ __device__ __forceinline__ void flash_bwd_kv(const FlashArgs& a, int kblk, int z
     store_rows<D>(out + ck, dk, a.scale, h);
     store_rows<D>(out + cv, dv, 1.f, h);
   }
+  if (grp == 0 && a.dbias_part) {  // the rings and the parked partials are done with
+    float* prow = a.dbias_part + (flash_dbias_rows(b, a.seq) + 2 * kblk + wv) * (3 * (int64_t)a.hs);
+    float* t = colsum_region<D, NG>(smem, wv);
+    wave_colsum<D>(prow + ck, dk, a.scale, key_ok, t, lane);
+    wave_colsum<D>(prow + cv, dv, 1.f, key_ok, t, lane);
+  }
 }
 
 // dQ. Work-group: 64 query rows of sequence b, head k, and NG groups of two waves (wave w:
@@ -737,6 +791,10 @@ __device__ __forceinline__ void flash_bwd_q(const FlashArgs& a, int qb, int z, b
       for (int r = 0; r < 16; ++r) dq[nb][r] += pg[(nb * 16 + r) * 128 + slot];
   }
   if (row_ok) store_rows<D>(static_cast<bf16*>(a.dqkv) + ((int64_t)b * a.seq + row) * a.ldq + cq, dq, a.scale, h);
+  if (a.dbias_part) {
+    float* prow = a.dbias_part + (flash_dbias_rows(b, a.seq) + 2 * qb + wv) * (3 * (int64_t)a.hs);
+    wave_colsum<D>(prow + cq, dq, a.scale, row_ok, colsum_region<D, NG>(smem, wv), lane);
+  }
 }
 
 // Both backward parts in one grid, each walking its deepest blocks first: blockIdx.x
@@ -747,6 +805,7 @@ __global__ __launch_bounds__(128 * NG) void flash_bwd_kernel(FlashArgs a) {
   constexpr int KVS = kv_stage<D, COMP>(), QS = q_stage<D, COMP>();
   constexpr int SMEM = NG * bwd_stages<NG>() * (KVS > QS ? KVS : QS);
   static_assert((NG - 1) * (D / 32) * 16 * 128 * 4 <= SMEM * 2, "parked partials fit the rings");
+  static_assert((park_floats<D, NG>() + 64 * (D + 4)) * 4 <= SMEM * 2, "the column-sum regions fit the rings");
   __shared__ __attribute__((aligned(1024))) bf16 smem[SMEM];
   dma_lds_escape(smem);
   int z, x;

@@ -29,6 +29,11 @@ struct FlashArgs {
   const void* dctx;    // backward: dL/dctx, layout of ctx
   const float* D;      // backward: rowsum(dctx * ctx) [B, heads, seq]
   void* dqkv;          // backward: layout of qkv (dQ, dK, dV of every head)
+  // backward, optional: column sums of the stored (bf16) dQ, dK, dV over each block of
+  // 32 rows of a sequence, fp32 [flash_dbias_rows(batch, seq)][3 hs] (row
+  // b flash_dbias_rows(1, seq) + j: rows 32 j .. of sequence b, zeros past its end), for
+  // the QKV bias gradient's fixed-order final sum
+  float* dbias_part;
   int64_t ldq, ldc;
   int batch, heads, seq, hs;
   float scale;         // 1 / sqrt(d)
@@ -39,7 +44,10 @@ inline bool flash_supported(int d) { return d == 64 || d == 128 || d == 160; }
 
 // Forward: ctx and lse from qkv, qkv_lo (d = 64, 128 or 160).
 hipError_t launch_flash_fwd(const FlashArgs& a, int d, hipStream_t s);
-// Backward: dQ, dK, dV into dqkv from qkv, qkv_lo, dctx, lse and D (d = 64, 128 or 160).
+// Backward: dQ, dK, dV into dqkv from qkv, qkv_lo, dctx, lse and D (d = 64, 128 or 160),
+// and, if dbias_part is set, their per-32-row column sums.
 hipError_t launch_flash_bwd(const FlashArgs& a, int d, hipStream_t s);
+// Rows of dbias_part: two per 64-row block of every sequence.
+__host__ __device__ inline int64_t flash_dbias_rows(int batch, int seq) { return (int64_t)batch * 2 * ((seq + 63) / 64); }
 
 }  // namespace mt

@@ -151,6 +151,7 @@ size_t colsum_floats(const Dims& d) {
   n = std::max(n, colsum_partial_floats((int)d.M, (int)d.ft, 0));
   n = std::max(n, gemm_colsum_floats((int)d.M, (int)d.ft));
   n = std::max(n, colsum_partial_floats((int)d.M, (int)d.qkv, 0));
+  if (d.flash) n = std::max(n, (size_t)(flash_dbias_rows((int)d.B, (int)d.seq) * d.qkv));
   if (ln_bwd_sums_supported((int)d.h)) n = std::max(n, ln_bwd_sums_partial_floats((int)d.M, (int)d.h, 4));
   return n;
 }
@@ -519,12 +520,14 @@ void attn_bwd_part(Seq& q, const Dims& d, const void* u, const void* w_qkv, cons
   });
   if (d.flash) {
     // B5/B6 fused: P recomputed from Q, K and the saved log-sum-exp; dK, dV per key block
-    // and dQ per query block, each summed in one work-group (no atomics).
+    // and dQ per query block, each summed in one work-group (no atomics), with the column
+    // sums of each 64-row block of dQKV for db_qkv.
     q.run("attn_bwd", 4 * at.flops(), 0, [&] {
       FlashArgs fa = flash_args(d, sv.qkv, sv.qkv_lo_saved, nullptr, sv.lse, scale);
       fa.dctx = ws.dctx;
       fa.D = ws.D;
       fa.dqkv = ws.dqkv;
+      fa.dbias_part = ws.part;
       return launch_flash_bwd(fa, (int)d.d, stream);
     });
   } else {
@@ -577,10 +580,15 @@ void attn_bwd_part(Seq& q, const Dims& d, const void* u, const void* w_qkv, cons
     });
   }
   // B7 QKV: db_qkv, dW_qkv = dQKV^T U, dU = dQKV W_qkv (partial)
-  q.run("db_qkv", 0, d.M * d.qkv * es, [&] {
-    return launch_colsum(bf, 0, ws.dqkv, false, nullptr, false, nullptr, nullptr, db_qkv, nullptr, ws.part, M,
-                         (int)d.qkv, stream);
-  });
+  if (d.flash) {  // fixed-order sum of the attention backward's per-block column sums
+    const int64_t nrb = flash_dbias_rows((int)d.B, (int)d.seq);
+    q.run("db_qkv", 0, nrb * d.qkv * 4.0, [&] { return launch_colsum_final(ws.part, db_qkv, (int)nrb, (int)d.qkv, stream); });
+  } else {
+    q.run("db_qkv", 0, d.M * d.qkv * es, [&] {
+      return launch_colsum(bf, 0, ws.dqkv, false, nullptr, false, nullptr, nullptr, db_qkv, nullptr, ws.part, M,
+                           (int)d.qkv, stream);
+    });
+  }
   q.run("qkv_dgrad_wgrad", 2 * gflop(d.M, d.h, d.qkv), 0, [&] {
     const GemmArgs dg = plain(ws.dqkv, d.qkv, w_qkv, d.h, du, d.h, d.M, d.h, d.qkv);
     const GemmArgs wg = plain(ws.dqkv, d.qkv, u, d.h, dw_qkv, d.h, d.qkv, d.h, d.M);
@@ -732,7 +740,9 @@ size_t carve_attn_bwd_ws(const Dims& d, void* base, AttnBwdWs* w) {
   w->ds = d.flash ? nullptr : c.take(d.B * d.at * d.seq * d.seq * d.es);
   w->dqkv = c.take(d.M * d.qkv * d.es);
   w->D = c.take<float>(d.B * d.at * d.seq * 4);
-  w->part = c.take<float>(colsum_partial_floats((int)d.M, (int)d.qkv, 0) * 4);
+  size_t np = colsum_partial_floats((int)d.M, (int)d.qkv, 0);
+  if (d.flash) np = std::max(np, (size_t)(flash_dbias_rows((int)d.B, (int)d.seq) * d.qkv));
+  w->part = c.take<float>(np * 4);
   const int64_t sp = dgrad_split_floats(d);
   w->spart = sp ? c.take<float>(sp * 4) : nullptr;
   return c.off;
