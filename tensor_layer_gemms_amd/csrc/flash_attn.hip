@@ -408,26 +408,46 @@ __device__ __forceinline__ void store_rows(bf16* out, const f32x16* acc, float s
     }
 }
 
-// Column sums of one wave's 32 rows of a stored gradient (acc * scale rounded to bf16 as
-// store_rows rounds it; rows past the sequence 0) into out[0 .. D). The wave puts its rows
-// in its own LDS region t (32 rows of D + 4 floats); lane l then adds 4 consecutive
-// columns over a run of rows (RS runs of 32 / RS rows per column group, as many as the
-// 64 lanes allow) and the runs' sums are added across lanes, run 0 first. LDS operations
-// of one wave complete in order, so the exchange needs no barrier.
+// Stores a wave's 32 rows of a gradient (acc * scale, rounded to bf16) where `store`
+// holds, and, if t is set, puts the rounded values (0 for rows past the sequence, given
+// by ok) as fp32 in the wave's own LDS region t (32 rows of D + 4 floats) for
+// wave_colsum. One conversion serves both.
 template <int D>
-__device__ __forceinline__ void wave_colsum(float* out, const f32x16* acc, float scale, bool ok, float* t, int lane) {
-  constexpr int LD = D + 4, G = D / 4;  // row pitch, column groups
-  constexpr int RS = G <= 16 ? 4 : G <= 32 ? 2 : 1, RPL = 32 / RS;
-  float* rowp = t + (lane & 31) * LD + 4 * (lane >> 5);
+__device__ __forceinline__ void store_stage_rows(bf16* out, bool store, const f32x16* acc, float scale, int h,
+                                                 float* t, bool ok, int lane) {
+  float* rowp = t ? t + (lane & 31) * (D + 4) + 4 * h : nullptr;
 #pragma unroll
   for (int nb = 0; nb < D / 32; ++nb)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      f32x4 v;
+      float v[4] = {acc[nb][4 * q] * scale, acc[nb][4 * q + 1] * scale, acc[nb][4 * q + 2] * scale,
+                    acc[nb][4 * q + 3] * scale};
+      u32x2 r;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = ok ? (float)(bf16)(acc[nb][4 * q + e] * scale) : 0.f;
-      *reinterpret_cast<f32x4*>(rowp + 32 * nb + 8 * q) = v;
+      for (int e = 0; e < 2; ++e) {
+        const bf16 lo = (bf16)v[2 * e], hi = (bf16)v[2 * e + 1];
+        r[e] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+      }
+      if (store) *reinterpret_cast<u32x2*>(out + 32 * nb + 8 * q + 4 * h) = r;
+      if (rowp) {
+        f32x4 w;
+        w[0] = ok ? __uint_as_float(r[0] << 16) : 0.f;
+        w[1] = ok ? __uint_as_float(r[0] & 0xffff0000u) : 0.f;
+        w[2] = ok ? __uint_as_float(r[1] << 16) : 0.f;
+        w[3] = ok ? __uint_as_float(r[1] & 0xffff0000u) : 0.f;
+        *reinterpret_cast<f32x4*>(rowp + 32 * nb + 8 * q) = w;
+      }
     }
+}
+
+// Column sums of the 32 rows a wave staged in t (store_stage_rows) into out[0 .. D): lane
+// l adds 4 consecutive columns over a run of rows (RS runs of 32 / RS rows per column
+// group, as many as the 64 lanes allow) and the runs' sums are added across lanes, run 0
+// first. LDS operations of one wave complete in order, so the exchange needs no barrier.
+template <int D>
+__device__ __forceinline__ void wave_colsum(float* out, const float* t, int lane) {
+  constexpr int LD = D + 4, G = D / 4;  // row pitch, column groups
+  constexpr int RS = G <= 16 ? 4 : G <= 32 ? 2 : 1, RPL = 32 / RS;
   const int g = lane % G, run = lane / G;
   f32x4 sum = {0.f, 0.f, 0.f, 0.f};
   if (run < RS) {
@@ -438,8 +458,8 @@ __device__ __forceinline__ void wave_colsum(float* out, const f32x16* acc, float
   if constexpr (RS == 4) {  // G = 16: runs in lanes g, g + 16, g + 32, g + 48
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float a = sum[e] + __shfl_xor(sum[e], 16);  // run 0 + run 1 (run 2 + run 3)
-      sum[e] = a + __shfl_xor(a, 32);
+      const float x = sum[e] + __shfl_xor(sum[e], 16);  // run 0 + run 1 (run 2 + run 3)
+      sum[e] = x + __shfl_xor(x, 32);
     }
   } else if constexpr (RS == 2) {  // G = 32: runs in lanes g, g + 32
 #pragma unroll
@@ -642,16 +662,21 @@ __device__ __forceinline__ void flash_bwd_kv(const FlashArgs& a, int kblk, int z
       }
     }
   }
-  if (grp == 0 && key_ok) {
+  if (grp == 0) {
     bf16* out = static_cast<bf16*>(a.dqkv) + ((int64_t)b * a.seq + key) * a.ldq;
-    store_rows<D>(out + ck, dk, a.scale, h);
-    store_rows<D>(out + cv, dv, 1.f, h);
-  }
-  if (grp == 0 && a.dbias_part) {  // the rings and the parked partials are done with
-    float* prow = a.dbias_part + (flash_dbias_rows(b, a.seq) + 2 * kblk + wv) * (3 * (int64_t)a.hs);
-    float* t = colsum_region<D, NG>(smem, wv);
-    wave_colsum<D>(prow + ck, dk, a.scale, key_ok, t, lane);
-    wave_colsum<D>(prow + cv, dv, 1.f, key_ok, t, lane);
+    if (!a.dbias_part) {  // uniform
+      if (key_ok) {
+        store_rows<D>(out + ck, dk, a.scale, h);
+        store_rows<D>(out + cv, dv, 1.f, h);
+      }
+    } else {  // the rings and the parked partials are done with
+      float* prow = a.dbias_part + (flash_dbias_rows(b, a.seq) + 2 * kblk + wv) * (3 * (int64_t)a.hs);
+      float* t = colsum_region<D, NG>(smem, wv);
+      store_stage_rows<D>(out + ck, key_ok, dk, a.scale, h, t, key_ok, lane);
+      wave_colsum<D>(prow + ck, t, lane);
+      store_stage_rows<D>(out + cv, key_ok, dv, 1.f, h, t, key_ok, lane);
+      wave_colsum<D>(prow + cv, t, lane);
+    }
   }
 }
 
@@ -790,10 +815,13 @@ __device__ __forceinline__ void flash_bwd_q(const FlashArgs& a, int qb, int z, b
 #pragma unroll
       for (int r = 0; r < 16; ++r) dq[nb][r] += pg[(nb * 16 + r) * 128 + slot];
   }
-  if (row_ok) store_rows<D>(static_cast<bf16*>(a.dqkv) + ((int64_t)b * a.seq + row) * a.ldq + cq, dq, a.scale, h);
-  if (a.dbias_part) {
-    float* prow = a.dbias_part + (flash_dbias_rows(b, a.seq) + 2 * qb + wv) * (3 * (int64_t)a.hs);
-    wave_colsum<D>(prow + cq, dq, a.scale, row_ok, colsum_region<D, NG>(smem, wv), lane);
+  bf16* out = static_cast<bf16*>(a.dqkv) + ((int64_t)b * a.seq + row) * a.ldq + cq;
+  if (!a.dbias_part) {  // uniform
+    if (row_ok) store_rows<D>(out, dq, a.scale, h);
+  } else {
+    float* t = colsum_region<D, NG>(smem, wv);
+    store_stage_rows<D>(out, row_ok, dq, a.scale, h, t, row_ok, lane);
+    wave_colsum<D>(a.dbias_part + (flash_dbias_rows(b, a.seq) + 2 * qb + wv) * (3 * (int64_t)a.hs) + cq, t, lane);
   }
 }
 

@@ -20,8 +20,9 @@ M, H, FT = 2048, 12288, 6144
 ALGORITHMIC = {
     # read V2, W1, b1; write A and Z (bf16)
     "fc1_fwd": M * H * 2 + FT * H * 2 + FT * 2 + 2 * M * FT * 2,
-    # read dOut (dgrad and wgrad), W2, A, Z (bf16); write dA (bf16) and dW2 (fp32)
-    "fc2_dgrad_wgrad": 2 * M * H * 2 + H * FT * 2 + 2 * M * FT * 2 + M * FT * 2 + H * FT * 4,
+    # read dOut (dgrad and wgrad), W2, A, Z (bf16); write dA (bf16), dW2 (fp32) and the
+    # per-128-row column sums of dA (fp32, the FC1 bias gradient's partials)
+    "fc2_dgrad_wgrad": 2 * M * H * 2 + H * FT * 2 + 2 * M * FT * 2 + M * FT * 2 + H * FT * 4 + (M // 128) * FT * 4,
 }
 
 
