@@ -63,6 +63,9 @@ def test_traffic_summary_arithmetic(path):
         assert alg == ALGORITHMIC[label]
     assert abs(traffic / alg - _num(kv["traffic_over_algorithmic"])) < 1e-3
     assert traffic >= alg  # counters cannot read below the bytes the kernel must move
+    if "kernel_trace_avg_us_timed_pass" in kv:  # the trace and the bench's events time the same launches
+        tr, ev = _num(kv["kernel_trace_avg_us_timed_pass"]), _num(kv["event_avg_us_same_command"])
+        assert abs(tr - ev) <= 0.05 * ev
 
 
 @pytest.mark.parametrize("path", SUMMARIES, ids=[os.path.basename(p) for p in SUMMARIES])
