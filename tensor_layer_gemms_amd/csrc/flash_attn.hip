@@ -467,6 +467,7 @@ __device__ __forceinline__ void wave_colsum(float* out, const float* t, int lane
   }
   if (lane < G) *reinterpret_cast<f32x4*>(out + 4 * g) = sum;
 }
+
 // LDS floats of the parked partials of groups 1 .. NG - 1 (placed first in the rings), and
 // the column-sum region of wave wv of group 0 after them.
 template <int D, int NG>
