@@ -37,9 +37,11 @@
  *     launched and the status says why (mt_status_string).
  *   - Shape limits: h % heads == 0, heads % tp == 0, 0 <= shard < tp, head dim
  *     d = h / heads a multiple of 8, seq a multiple of 8 and <= 4096, h <= 32768.
- *   - Precision of the bf16 path: the residual stream X2 = X + O + b_o and its
- *     gradient dX2 are kept in fp32 inside the call; everything stored between kernels
- *     as a GEMM operand (U, QKV, P, ctx, V2, A, Z, dA, dctx, dS, dQKV, partials) is bf16.
+ *   - Precision of the bf16 path: the residual stream X2 = X + O + b_o is kept in fp32
+ *     inside the call; everything else stored between kernels (U, QKV, P, ctx, V2, A, Z,
+ *     dA, dX2, dctx, dS, dQKV, partials) is bf16, each formed in fp32 and rounded once.
+ *     db_o is summed from the unrounded dX2 where the LayerNorm-2 backward carries the
+ *     column sums (h <= 16384), else from the stored dX2.
  *   - MT_BF16_QK: the softmax's exponent magnifies errors of the logits Q K^T / sqrt(d)
  *     by their own size, and with bf16 Q and K (8 significant bits) a shard whose logits
  *     reach the tens can miss the 2e-2 normwise bar on the attention gradients. In this

@@ -6,10 +6,12 @@ and is never imported by the product.
 The layer is evaluated with the oracle's own formulas in float64, except that every
 tensor the bf16 path stores in bf16 between its kernels is rounded to bf16 at that
 point (float64 -> float32 -> bf16, each to nearest even). Which tensors those are is
-the documented storage precision of the C ABI (include/mt.h): GEMM operands and
-intermediates in bf16, accumulation, LayerNorm / softmax / GeLU math, the residual
-stream X2 and its gradient dX2 in fp32 (not rounded here). With no rounding point
-enabled the model is exactly the oracle (pinned in tests/test_rounding_model.py).
+the documented storage precision of the C ABI (include/mt.h): GEMM operands,
+intermediates and the residual gradient dX2 in bf16; accumulation, LayerNorm / softmax /
+GeLU math and the residual stream X2 in fp32 (not rounded here). The sequence-parallel
+share takes dX2 in fp32 from its caller, so its model leaves out the "dx2" point. With
+no rounding point enabled the model is exactly the oracle (pinned in
+tests/test_rounding_model.py).
 
 A rounding point is a name; ``BF16`` is the set of the default MT_BF16 mode and
 ``BF16_QK`` that of the MT_BF16_QK mode, which carries U into the Q and K columns of the
@@ -47,6 +49,7 @@ BF16_QK = frozenset({
     "ctx", "o",     # context, out-projection partial
     "v2", "a", "z", "y", "out",
     "da", "dv2", "dx2_operand", "dctx", "ds", "dqkv", "du", "dx",
+    "dx2",          # its gradient as the LayerNorm-1 backward's residual input
     "ar",           # a reduce-scatter's output (sequence-parallel share), rounded once after the sum
     "u_pair",       # U as hi + lo into the Q and K columns of the projection (bf16 U into the V columns)
     "qk_pair",      # Q, K as hi + lo pairs in the logits
@@ -224,8 +227,11 @@ def layer(x, dout, ranks: List[Dict[str, np.ndarray]], B: int, s: int, d: int, r
     du = ar([du_ for du_, _ in ba])
     xh1 = (x - mu1[:, None]) * rs1[:, None]
     dxl1, _, _ = layernorm_bwd(du, x, p0["ln1_g"], mu1, rs1)
-    dx = r("dx", dx2 + dxl1)
-    rows = {"ln1_g": du * xh1, "ln1_b": du, "b_o": dx2, "ln2_g": dv2 * xh2, "ln2_b": dv2, "b_fc2": dout}
+    dx = r("dx", r("dx2", dx2) + dxl1)
+    # db_o: summed from the unrounded dX2 where the LayerNorm-2 backward carries the column
+    # sums in its row pass (h <= 16384), else from the stored dX2
+    db_o_rows = dx2 if x.shape[1] <= 16384 else r("dx2", dx2)
+    rows = {"ln1_g": du * xh1, "ln1_b": du, "b_o": db_o_rows, "ln2_g": dv2 * xh2, "ln2_b": dv2, "b_fc2": dout}
     for g in grads:
         g.update({k: v.sum(0) for k, v in rows.items()})
     return out, dx, grads, rows

@@ -130,8 +130,8 @@ size_t carve_layer_fwd_ws(const Dims& d, void* base, LayerFwdWs* w) {
 
 struct LayerBwdWs {
   void *da, *dv2, *dx2, *dctx, *ds, *dqkv;
-  float *dx2f, *D, *part;  // dx2f: fp32 copy of dX2 for the residual path
-  float* spart;            // k-slice partials of a split input gradient (bf16 path)
+  float *D, *part;
+  float* spart;  // k-slice partials of a split input gradient (bf16 path)
 };
 
 // fp32 partials of the largest split input gradient of the layer (0 if none splits).
@@ -161,7 +161,6 @@ size_t carve_layer_bwd_ws(const Dims& d, void* base, LayerBwdWs* w) {
   w->da = c.take(d.M * d.ft * d.es);
   w->dv2 = c.take(d.M * d.h * d.es);  // dV2 partial, later dU partial
   w->dx2 = c.take(d.M * d.h * d.es);
-  w->dx2f = c.take<float>(d.M * d.h * 4);
   w->dctx = c.take(d.M * d.hs * d.es);
   w->ds = d.flash ? nullptr : c.take(d.B * d.at * d.seq * d.seq * d.es);
   w->dqkv = c.take(d.M * d.qkv * d.es);
@@ -632,25 +631,26 @@ int layer_bwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, cons
     const GemmArgs wg = plain(ws.da, d.ft, sv.v2, d.h, gr.w_fc1, d.h, d.ft, d.h, d.M);
     return gemm_dgrad_wgrad(d, dg, EPI_STORE, wg, stream, ws.spart);
   });
-  // B3 dX2 = dOut + LN2-backward(AR(dV2)) (written as the GEMM operand and as an fp32
-  // copy for the residual path); dgamma2, dbeta2; db_o = colsum(dX2); db_fc2 = colsum(dOut)
-  // — in one pass over the rows where the fused kernel covers h, else as separate column sums
+  // B3 dX2 = dOut + LN2-backward(AR(dV2)) (the out-projection GEMMs' operand and the
+  // residual input of the LayerNorm-1 backward); dgamma2, dbeta2; db_o = colsum(dX2);
+  // db_fc2 = colsum(dOut) — in one pass over the rows where the fused kernel covers h (db_o
+  // then summed from the unrounded values), else as separate column sums
   if (ln_sums) {
-    q.run("ln2_bwd", 0, Mh * (3 * es + 8), [&] {
-      return launch_ln_bwd_sums(bf, ws.dv2, sv.x2, true, w.ln2_g, sv.mean2, sv.rstd2, dout, false, ws.dx2, ws.dx2f,
+    q.run("ln2_bwd", 0, Mh * (3 * es + 4), [&] {
+      return launch_ln_bwd_sums(bf, ws.dv2, sv.x2, true, w.ln2_g, sv.mean2, sv.rstd2, dout, false, ws.dx2, nullptr,
                                 ws.part, gr.ln2_g, gr.ln2_b, gr.b_o, gr.b_fc2, M, (int)d.h, stream);
     });
   } else {
-    q.run("ln2_bwd", 0, Mh * (3 * es + 8), [&] {
-      return launch_ln_bwd(bf, ws.dv2, sv.x2, true, w.ln2_g, sv.mean2, sv.rstd2, dout, false, ws.dx2, ws.dx2f, M,
+    q.run("ln2_bwd", 0, Mh * (3 * es + 4), [&] {
+      return launch_ln_bwd(bf, ws.dv2, sv.x2, true, w.ln2_g, sv.mean2, sv.rstd2, dout, false, ws.dx2, nullptr, M,
                            (int)d.h, stream);
     });
     q.run("ln2_param_grads", 0, Mh * (es + 4), [&] {
       return launch_colsum(bf, 1, ws.dv2, false, sv.x2, true, sv.mean2, sv.rstd2, gr.ln2_g, gr.ln2_b, ws.part, M,
                            (int)d.h, stream);
     });
-    q.run("db_o", 0, Mh * 4, [&] {
-      return launch_colsum(bf, 0, ws.dx2f, true, nullptr, false, nullptr, nullptr, gr.b_o, nullptr, ws.part, M,
+    q.run("db_o", 0, Mh * es, [&] {
+      return launch_colsum(bf, 0, ws.dx2, !bf, nullptr, false, nullptr, nullptr, gr.b_o, nullptr, ws.part, M,
                            (int)d.h, stream);
     });
   }
@@ -658,13 +658,13 @@ int layer_bwd_impl(const Dims& d, const mt_layer_weights& w, const void* x, cons
                 AttnBwdWs{ws.dctx, ws.ds, ws.dqkv, ws.D, ws.part, ws.spart}, stream);
   // B8 dX = dX2 + LN1-backward(AR(dU)); dgamma1, dbeta1
   if (ln_sums) {
-    q.run("ln1_bwd", 0, Mh * (3 * es + 4), [&] {
-      return launch_ln_bwd_sums(bf, ws.dv2, x, false, w.ln1_g, sv.mean1, sv.rstd1, ws.dx2f, true, dx, nullptr,
+    q.run("ln1_bwd", 0, Mh * 4 * es, [&] {
+      return launch_ln_bwd_sums(bf, ws.dv2, x, false, w.ln1_g, sv.mean1, sv.rstd1, ws.dx2, !bf, dx, nullptr,
                                 ws.part, gr.ln1_g, gr.ln1_b, nullptr, nullptr, M, (int)d.h, stream);
     });
   } else {
-    q.run("ln1_bwd", 0, Mh * (3 * es + 4), [&] {
-      return launch_ln_bwd(bf, ws.dv2, x, false, w.ln1_g, sv.mean1, sv.rstd1, ws.dx2f, true, dx, nullptr, M,
+    q.run("ln1_bwd", 0, Mh * 4 * es, [&] {
+      return launch_ln_bwd(bf, ws.dv2, x, false, w.ln1_g, sv.mean1, sv.rstd1, ws.dx2, !bf, dx, nullptr, M,
                            (int)d.h, stream);
     });
     q.run("ln1_param_grads", 0, 2 * Mh * es, [&] {

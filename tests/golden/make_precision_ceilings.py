@@ -10,6 +10,7 @@ unrounded oracle. Calls only oracle/ and the seeded input generators.
 """
 from __future__ import annotations
 
+import fcntl
 import json
 import os
 import sys
@@ -48,16 +49,20 @@ def predict(key: str):
 
 
 def main(keys):
-    data = {}
-    if os.path.exists(OUT):
-        with open(OUT) as f:
-            data = json.load(f)
     for key in keys:
         t0 = time.time()
-        data[key] = predict(key)
+        pred = predict(key)
+        # read-modify-write under a lock, so that runs over disjoint keys can go in parallel
+        with open(OUT + ".lock", "w") as lk:
+            fcntl.flock(lk, fcntl.LOCK_EX)
+            data = {}
+            if os.path.exists(OUT):
+                with open(OUT) as f:
+                    data = json.load(f)
+            data[key] = pred
+            with open(OUT, "w") as f:
+                json.dump(data, f, indent=1, sort_keys=True)
         print(f"{key}: {time.time() - t0:.0f} s", flush=True)
-        with open(OUT, "w") as f:
-            json.dump(data, f, indent=1, sort_keys=True)
 
 
 if __name__ == "__main__":
