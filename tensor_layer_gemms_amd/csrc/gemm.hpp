@@ -94,11 +94,22 @@ hipError_t launch_gemm_bf16_pair(const GemmArgs& g0, bool a_k0, bool b_k0, int k
 // split into (1, 2 or 4; depends on N and K only, so every token is computed the same way
 // at any batch size).
 int gemm_dgrad_splits(int64_t N, int64_t K);
-// The same pairing as above for an EPI_STORE input gradient dg (A k-contiguous, B
-// n-contiguous, unbatched) and a weight gradient wg, with dg split into
-// gemm_dgrad_splits(dg.N, dg.K) k slices written as fp32 to part ([splits, M, N]) and
-// summed in slice order into dg.C by a second pass. Returns hipErrorNotSupported
-// (nothing launched) if dg is not split or the pair does not qualify.
-hipError_t launch_gemm_bf16_pair_split(const GemmArgs& dg, const GemmArgs& wg, float* part, hipStream_t stream);
+// k slices of a paired input gradient dg (epilogue dkind) and weight gradient wg: at most
+// one of them splits (*sd or *sw > 1). An EPI_STORE input gradient splits as
+// gemm_dgrad_splits says; otherwise an EPI_STORE pair's weight gradient splits its
+// token dimension where its tiles are the long pole of the pair and the estimated time
+// saved exceeds the slices' extra traffic (the small, deep weight gradients of narrow
+// layers). Depends on the shapes only.
+void gemm_pair_splits(const GemmArgs& dg, int dkind, const GemmArgs& wg, int* sd, int* sw);
+// fp32 floats of `part` that launch_gemm_bf16_pair_split needs for the pair (0: no split).
+int64_t gemm_pair_split_floats(const GemmArgs& dg, int dkind, const GemmArgs& wg);
+// The same pairing as above for an input gradient dg (A k-contiguous, B n-contiguous,
+// unbatched; epilogue dkind) and a weight gradient wg, with the problem that
+// gemm_pair_splits names split into k slices written as fp32 to part ([splits, M, N])
+// and summed in slice order into its C by a second pass (bf16 dg.C, fp32 wg.C).
+// Returns hipErrorNotSupported (nothing launched) if neither splits or the pair does not
+// qualify.
+hipError_t launch_gemm_bf16_pair_split(const GemmArgs& dg, int dkind, const GemmArgs& wg, float* part,
+                                       hipStream_t stream);
 
 }  // namespace mt

@@ -137,32 +137,37 @@ hipError_t dispatch(const GemmArgs& g, int batch, hipStream_t s) {
   return e;
 }
 
-// Paired launch with tile config (BM, BN, WM, WN) for both problems.
-// Paired launch; problem 0 may be batched (batch0 entries, e.g. k slices).
+// Paired launch; either problem may be batched (batch0 / batch1 entries, e.g. k slices).
 template <class P0, class P1>
-hipError_t run_pair(const GemmArgs& g0, const GemmArgs& g1, hipStream_t s, int batch0 = 1) {
+hipError_t run_pair(const GemmArgs& g0, const GemmArgs& g1, hipStream_t s, int batch0 = 1, int batch1 = 1) {
   const int z0 = ((g0.M + P0::kBM - 1) / P0::kBM) * ((g0.N + P0::kBN - 1) / P0::kBN);
   const int z1 = ((g1.M + P1::kBM - 1) / P1::kBM) * ((g1.N + P1::kBN - 1) / P1::kBN);
-  const int t0 = z0 * batch0, t1 = z1;
+  const int t0 = z0 * batch0, t1 = z1 * batch1;
   const int first = g1.K > g0.K ? 1 : 0;  // deeper contraction first
   hipLaunchKernelGGL((gemm_dma_pair_kernel<P0, P1>), dim3(t0 + t1), dim3(P0::kThreads), 0, s, g0, g1, first,
                      first ? t1 : t0, z0, z1);
   return hipGetLastError();
 }
 
-// Estimated time of a paired launch: the larger of the mean work per resident slot and
-// the deepest single tile, in tile-k-steps, times the CU's share of tile area over the
-// candidate's throughput.
-double pair_cost(const TileCfg& c, const GemmArgs& g0, const GemmArgs& g1) {
+// Estimated time of a paired launch (problem i batched b_i times): the larger of the mean
+// work per resident slot and the deepest single tile, in tile-k-steps, times the CU's
+// share of tile area over the candidate's throughput.
+double pair_cost(const TileCfg& c, const GemmArgs& g0, const GemmArgs& g1, int b0 = 1, int b1 = 1) {
   auto tiles = [&](const GemmArgs& g) { return (double)((g.M + c.bm - 1) / c.bm) * ((g.N + c.bn - 1) / c.bn); };
   const double s0 = (g0.K + 63) / 64, s1 = (g1.K + 63) / 64;
   const double slots = (double)kNumCUs * c.per_cu;
-  const double t = std::max((tiles(g0) * s0 + tiles(g1) * s1) / slots, std::max(s0, s1));
+  const double t = std::max((tiles(g0) * b0 * s0 + tiles(g1) * b1 * s1) / slots, std::max(s0, s1));
   return t * c.bm * c.bn * c.per_cu / c.eff;
 }
 
-// C = bf16(sum over `splits` fp32 slices of part, each [M, N] dense), C strided by ldc.
-__global__ __launch_bounds__(256) void split_sum_kernel(const float* __restrict__ part, bf16* __restrict__ C, int M,
+// pair_cost in microseconds: one k-step of a 256x256 tile on a CU takes ~2.1 us (the
+// backward pairs of the 175B shard).
+constexpr double kUsPerCostUnit = 2.1 / (256.0 * 256.0);
+
+// C = sum over `splits` fp32 slices of part (each [M, N] dense) in slice order, stored as
+// T (bf16 input gradient or fp32 weight gradient), C strided by ldc.
+template <typename T>
+__global__ __launch_bounds__(256) void split_sum_kernel(const float* __restrict__ part, T* __restrict__ C, int M,
                                                         int N, int splits, int64_t ldc, int64_t total) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= total) return;
@@ -209,13 +214,83 @@ int gemm_dgrad_splits(int64_t N, int64_t K) {
   return best;
 }
 
-hipError_t launch_gemm_bf16_pair_split(const GemmArgs& dg, const GemmArgs& wg, float* part, hipStream_t s) {
-  const int sp = gemm_dgrad_splits(dg.N, dg.K);
-  if (sp <= 1 || !part || dg.N % 8 || dg.causal != CAUSAL_NONE || dg.nseg != 1 || dg.zdiv != 1)
+void gemm_pair_splits(const GemmArgs& dg, int dkind, const GemmArgs& wg, int* sd, int* sw) {
+  *sd = dkind == EPI_STORE ? gemm_dgrad_splits(dg.N, dg.K) : 1;
+  *sw = 1;
+  if (*sd > 1 || dkind != EPI_STORE) return;
+  // Weight gradient in k slices (the token dimension) where its tiles are the long pole of
+  // the pair: estimated time with sw slices plus the slices' extra traffic (written and
+  // read back beyond the direct store, at ~4 TB/s) and the summing launch, taken when it
+  // saves at least a tenth.
+  auto best_us = [&](const GemmArgs& g1, int b1) {
+    return std::min(pair_cost(kDmaT[0], dg, g1, 1, b1), pair_cost(kDmaT[1], dg, g1, 1, b1)) * kUsPerCostUnit;
+  };
+  double t_best = best_us(wg, 1);
+  for (int sp = 2; sp <= 4; sp *= 2) {
+    if (wg.K % (64 * sp) != 0) break;
+    GemmArgs g1 = wg;
+    g1.K = wg.K / sp;
+    const double extra_us = (2.0 * sp - 1.0) * 4.0 * (double)wg.M * (double)wg.N / 4.0e6 + 3.0;
+    const double t = best_us(g1, sp) + extra_us;
+    if (t < 0.9 * t_best) {
+      t_best = t;
+      *sw = sp;
+    }
+  }
+}
+
+int64_t gemm_pair_split_floats(const GemmArgs& dg, int dkind, const GemmArgs& wg) {
+  int sd, sw;
+  gemm_pair_splits(dg, dkind, wg, &sd, &sw);
+  if (sd > 1) return (int64_t)sd * dg.M * dg.N;
+  if (sw > 1) return (int64_t)sw * wg.M * wg.N;
+  return 0;
+}
+
+namespace {
+
+// The weight gradient of an EPI_STORE pair as sw k slices into part, then summed into wg.C.
+hipError_t pair_wgrad_split(const GemmArgs& dg, const GemmArgs& wg, int sw, float* part, hipStream_t s) {
+  if (wg.N % 8 || wg.zdiv != 1 || dg.colsum || wg.colsum) return hipErrorNotSupported;
+  // slice z contracts the tokens k in [z K/sw, (z + 1) K/sw) into part[z]
+  GemmArgs g1 = wg;
+  const int64_t ks = wg.K / sw;
+  g1.K = (int)ks;
+  g1.a_so = ks * wg.lda;  // A(m, k) at k lda + m
+  g1.b_so = ks * wg.ldb;  // B(n, k) at k ldb + n
+  g1.C = part;
+  g1.ldc = wg.N;
+  g1.c_so = (int64_t)wg.M * wg.N;
+  g1.a_si = g1.b_si = g1.c_si = 0;
+  g1.alpha = 1.0f;
+  if (!dma_ok(g1, false, false)) return hipErrorNotSupported;
+  hipError_t e;
+  if (pair_cost(kDmaT[0], dg, g1, 1, sw) <= pair_cost(kDmaT[1], dg, g1, 1, sw))
+    e = run_pair<DmaProblem<true, false, 256, 256, 64, 2, 4, EPI_STORE>,
+                 DmaProblem<false, false, 256, 256, 64, 2, 4, EPI_STORE_F32>>(dg, g1, s, 1, sw);
+  else
+    e = run_pair<DmaProblem<true, false, 128, 128, 64, 2, 2, EPI_STORE>,
+                 DmaProblem<false, false, 128, 128, 64, 2, 2, EPI_STORE_F32>>(dg, g1, s, 1, sw);
+  if (e != hipSuccess) return e;
+  const int64_t total = (int64_t)wg.M * (wg.N / 8);
+  hipLaunchKernelGGL(split_sum_kernel<float>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part,
+                     static_cast<float*>(wg.C), wg.M, wg.N, sw, wg.ldc, total);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_bf16_pair_split(const GemmArgs& dg, int dkind, const GemmArgs& wg, float* part,
+                                       hipStream_t s) {
+  int sp, sw;
+  gemm_pair_splits(dg, dkind, wg, &sp, &sw);
+  if ((sp <= 1 && sw <= 1) || !part || dg.causal != CAUSAL_NONE || dg.nseg != 1 || dg.zdiv != 1)
     return hipErrorNotSupported;
   for (const GemmArgs* g : {&dg, &wg})
     if (g->causal != CAUSAL_NONE || g->nseg != 1 || g->M <= 0 || g->N <= 0) return hipErrorNotSupported;
   if (!dma_ok(dg, true, false) || !dma_ok(wg, false, false)) return hipErrorNotSupported;
+  if (sw > 1) return pair_wgrad_split(dg, wg, sw, part, s);
+  if (dg.N % 8) return hipErrorNotSupported;
   // dgrad as `sp` k slices: slice z contracts k in [z K/sp, (z + 1) K/sp) into part[z].
   GemmArgs g0 = dg;
   const int64_t ks = dg.K / sp;
@@ -237,7 +312,7 @@ hipError_t launch_gemm_bf16_pair_split(const GemmArgs& dg, const GemmArgs& wg, f
                  DmaProblem<false, false, 128, 128, 64, 2, 2, EPI_STORE_F32>>(g0, wg, s, sp);
   if (e != hipSuccess) return e;
   const int64_t total = (int64_t)dg.M * (dg.N / 8);
-  hipLaunchKernelGGL(split_sum_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part,
+  hipLaunchKernelGGL(split_sum_kernel<bf16>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part,
                      static_cast<bf16*>(dg.C), dg.M, dg.N, sp, dg.ldc, total);
   return hipGetLastError();
 }

@@ -131,17 +131,23 @@ size_t carve_layer_fwd_ws(const Dims& d, void* base, LayerFwdWs* w) {
 struct LayerBwdWs {
   void *da, *dv2, *dx2, *dctx, *ds, *dqkv;
   float *D, *part;
-  float* spart;  // k-slice partials of a split input gradient (bf16 path)
+  float* spart;  // k-slice partials of a split input or weight gradient (bf16 path)
 };
 
-// fp32 partials of the largest split input gradient of the layer (0 if none splits).
+GemmArgs plain(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, int64_t M, int64_t N,
+               int64_t K);
+
+// fp32 k-slice partials of the largest split GEMM of the layer's backward pairs that
+// take them (FC1, out-projection, QKV; 0 if none splits): input gradient dg [M, N] over
+// K, weight gradient [K, N] over the M tokens.
 int64_t dgrad_split_floats(const Dims& d) {
   if (!d.bf16) return 0;
-  const int64_t nk[4][2] = {{d.ft, d.h}, {d.h, d.ft}, {d.hs, d.h}, {d.h, d.qkv}};
+  const int64_t nk[3][2] = {{d.h, d.ft}, {d.hs, d.h}, {d.h, d.qkv}};
   int64_t n = 0;
   for (const auto& p : nk) {
-    const int sp = gemm_dgrad_splits(p[0], p[1]);
-    if (sp > 1) n = std::max<int64_t>(n, sp * d.M * p[0]);
+    const GemmArgs dg = plain(nullptr, p[1], nullptr, p[0], nullptr, p[0], d.M, p[0], p[1]);
+    const GemmArgs wg = plain(nullptr, p[1], nullptr, p[0], nullptr, p[0], p[1], p[0], d.M);
+    n = std::max<int64_t>(n, gemm_pair_split_floats(dg, EPI_STORE, wg));
   }
   return n;
 }
@@ -295,8 +301,8 @@ hipError_t gemm(const Dims& d, const GemmArgs& g, bool a_k, bool b_k, int kind, 
 // launch where the bf16 path supports it, else the two one after the other.
 hipError_t gemm_dgrad_wgrad(const Dims& d, const GemmArgs& dg, int dkind, const GemmArgs& wg, hipStream_t s,
                             float* spart = nullptr) {
-  if (d.bf16 && dkind == EPI_STORE && spart) {  // deep, narrow input gradient: k slices
-    const hipError_t e = launch_gemm_bf16_pair_split(dg, wg, spart, s);
+  if (d.bf16 && spart) {  // a deep input gradient or weight gradient in k slices
+    const hipError_t e = launch_gemm_bf16_pair_split(dg, dkind, wg, spart, s);
     if (e != hipErrorNotSupported) return e;
   }
   if (d.bf16) {

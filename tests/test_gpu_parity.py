@@ -117,6 +117,7 @@ def _run_attn_gpu(shape, u, d_o, p):
     ("bf16", 4, 512, 8, 72, 3),      # head dim 64, three sequences
     ("bf16", 2, 640, 4, 104, 1),     # head dim 160: fused attention, ragged blocks
     ("bf16", 2, 384, 4, 104, 1),     # head dim 96: materialised attention
+    ("bf16", 2, 512, 8, 512, 4),     # 2048 tokens: out-projection and QKV weight gradients in 4 token slices
 ])
 def test_attn_shards_sum_to_unsharded_block(dtype, tp, h, heads, seq, mb):
     """The pages' head-parallel split on the GPU: every shard of the attention block
@@ -153,6 +154,8 @@ def test_attn_shards_sum_to_unsharded_block(dtype, tp, h, heads, seq, mb):
     (512, 8, 520, 2, 2, 0),    # seq spanning three causal chunks
     (512, 4, 200, 2, 2, 1),    # head dim 128 (fused attention): ragged query and key blocks
     (1024, 8, 72, 3, 1, 0),    # head dim 128, short sequences, 3 sequences per micro-batch
+    (512, 8, 512, 4, 2, 1),    # 2048 tokens over a narrow shard: FC1, out-projection and QKV
+                               # weight gradients in token slices (2, 4, 4)
 ])
 @pytest.mark.parametrize("qk_pairs", [False, True], ids=["bf16", "bf16qk"])
 def test_layer_bf16_multi_tile(h, heads, seq, mb, tp, shard, qk_pairs):
